@@ -225,6 +225,18 @@ def moe_forward(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray, W: dict,
     return out
 
 
+def residual(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """Residual between stacked layers: x' = RN_bf16(x + y), returned as bf16 bits.
+
+    The layers are stacked 48 deep (byteiota "Edge0-145B: Run a 145B Open-Source
+    Model on Your Laptop", Not Compression - Architecture); the residual form is
+    a stated reading.  x (bf16) + y (float32 values) is exact in float64 for the
+    layer's value ranges, so one bf16 rounding of it is the definition.
+    """
+    v = rn_bf16(bf16_to_f64(x_bits) + np.asarray(y, dtype=np.float64))
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def layer_forward(x_bits, wr_bits, bias, W, experts_per_group, k, mode="contract", keep=False):
     """route() followed by moe_forward() on the routed experts."""
     rt = route(x_bits, wr_bits, bias, k)

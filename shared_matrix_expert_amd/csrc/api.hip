@@ -1,0 +1,351 @@
+// C-ABI entry points: validation, workspace layout and launch sequencing.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/edge_moe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_dims(const edge_moe_dims* p) {
+    if (!p) return EDGE_MOE_EINVAL;
+    const edge_moe_dims& d = *p;
+    if (d.T < 1 || d.d < 1 || d.h < 1 || d.n_experts < 1 || d.experts_per_group < 1 ||
+        d.top_k < 1 || d.delta_rank < 1 || d.lora_rank < 1 || d.quant_group < 1)
+        return EDGE_MOE_EINVAL;
+    if (d.n_experts % d.experts_per_group != 0) return EDGE_MOE_EINVAL;
+    if (d.top_k > d.n_experts) return EDGE_MOE_EINVAL;
+    if ((d.d & 1) || (d.h & 1) || (d.delta_rank & 1)) return EDGE_MOE_EINVAL;
+    const int Ks[3] = {d.d, d.h, d.delta_rank};
+    for (int K : Ks) {
+        const int g = d.quant_group < K ? d.quant_group : K;
+        if (K % g != 0) return EDGE_MOE_EINVAL;
+    }
+    // limits of the kernels
+    if (d.T > (1 << 20)) return EDGE_MOE_EUNSUPPORTED;
+    if (d.d % 128 || d.h % 128 || d.d > 32768 || d.h > 32768) return EDGE_MOE_EUNSUPPORTED;
+    if (d.n_experts > 1024 || d.n_experts / d.experts_per_group > 64) return EDGE_MOE_EUNSUPPORTED;
+    if (d.top_k > 32) return EDGE_MOE_EUNSUPPORTED;
+    if (d.delta_rank % 8 || d.delta_rank > 256) return EDGE_MOE_EUNSUPPORTED;
+    if (d.lora_rank % 2 || d.lora_rank > 32) return EDGE_MOE_EUNSUPPORTED;
+    if (!is_pow2(d.quant_group) || d.quant_group < 32 || d.quant_group > 4096) return EDGE_MOE_EUNSUPPORTED;
+    return EDGE_MOE_OK;
+}
+
+struct Layout {
+    size_t bm, pre, total, eoff, uoff, etile, gtile_u, gtile_r;
+    size_t row_tok, row_slot, row_exp, row_u, slot_row, ut_tok;
+    size_t z1, zl, hs, act, z2, zl2, o;
+    size_t logits;
+    size_t fwd_bytes, route_bytes;
+    int64_t R, Umax;
+    int W, G, rLp;
+};
+
+Layout make_layout(const edge_moe_dims& d) {
+    Layout L{};
+    const int64_t T = d.T, E = d.n_experts, k = d.top_k;
+    L.G = d.n_experts / d.experts_per_group;
+    L.W = (int)((T + 31) / 32);
+    L.R = T * k;
+    L.Umax = L.R < T * L.G ? L.R : T * L.G;
+    L.rLp = (d.lora_rank + 7) & ~7;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    const size_t nb = (size_t)(E + L.G) * L.W;
+    L.bm = take(nb * 4);
+    L.pre = take(nb * 4);
+    L.total = take((E + L.G) * 4);
+    L.eoff = take((E + 1) * 4);
+    L.uoff = take((L.G + 1) * 4);
+    L.etile = take((E + 1) * 4);
+    L.gtile_u = take((L.G + 1) * 4);
+    L.gtile_r = take((L.G + 1) * 4);
+    L.row_tok = take(L.R * 4);
+    L.row_slot = take(L.R * 4);
+    L.row_exp = take(L.R * 4);
+    L.row_u = take(L.R * 4);
+    L.slot_row = take(L.R * 4);
+    L.ut_tok = take(L.Umax * 4);
+    L.z1 = take((size_t)L.R * d.delta_rank * 2);
+    L.zl = take((size_t)L.Umax * L.rLp * 2);
+    L.hs = take((size_t)L.Umax * d.h * 4);
+    L.act = take((size_t)L.R * d.h * 2);
+    L.z2 = take((size_t)L.R * d.delta_rank * 2);
+    L.zl2 = take((size_t)L.R * L.rLp * 2);
+    L.o = take((size_t)L.R * d.d * 4);
+    L.fwd_bytes = off;
+    L.logits = 0;
+    L.route_bytes = align_up((size_t)T * E * 4);
+    return L;
+}
+
+bool aligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) == 0; }
+
+// gfx950 check, cached per device
+int check_device() {
+    static std::mutex mu;
+    static std::unordered_map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return EDGE_MOE_EHIP;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return EDGE_MOE_EHIP;
+    const std::string arch(prop.gcnArchName);
+    const int st = arch.rfind("gfx950", 0) == 0 ? EDGE_MOE_OK : EDGE_MOE_EUNSUPPORTED;
+    cache[dev] = st;
+    return st;
+}
+
+// ----------------------------------------------------------------- profiling ----
+struct ProfEntry { std::string name; hipEvent_t e0, e1; };
+struct ProfState {
+    bool on = false;
+    std::vector<ProfEntry> pending;
+    std::vector<hipEvent_t> pool;
+    hipEvent_t cur = nullptr;
+    std::vector<std::string> order;
+    std::unordered_map<std::string, std::pair<int64_t, double>> table;
+};
+ProfState& prof() { static ProfState s; return s; }
+
+hipEvent_t prof_event() {
+    ProfState& p = prof();
+    if (!p.pool.empty()) { hipEvent_t e = p.pool.back(); p.pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    hipEventCreate(&e);
+    return e;
+}
+
+void prof_drain() {
+    ProfState& p = prof();
+    for (auto& en : p.pending) {
+        hipEventSynchronize(en.e1);
+        float ms = 0.f;
+        hipEventElapsedTime(&ms, en.e0, en.e1);
+        auto it = p.table.find(en.name);
+        if (it == p.table.end()) { p.order.push_back(en.name); p.table[en.name] = {1, ms}; }
+        else { it->second.first += 1; it->second.second += ms; }
+        p.pool.push_back(en.e0);
+        p.pool.push_back(en.e1);
+    }
+    p.pending.clear();
+}
+
+}  // namespace
+
+namespace em {
+void prof_begin(hipStream_t s) {
+    ProfState& p = prof();
+    if (!p.on) return;
+    p.cur = prof_event();
+    hipEventRecord(p.cur, s);
+}
+void prof_end(hipStream_t s, const char* name) {
+    ProfState& p = prof();
+    if (!p.on || !p.cur) return;
+    hipEvent_t e1 = prof_event();
+    hipEventRecord(e1, s);
+    p.pending.push_back({name, p.cur, e1});
+    p.cur = nullptr;
+    if (p.pending.size() > 4096) prof_drain();
+}
+}  // namespace em
+
+extern "C" {
+
+size_t edge_moe_workspace_bytes(const edge_moe_dims* dims) {
+    if (check_dims(dims) != EDGE_MOE_OK) return 0;
+    const Layout L = make_layout(*dims);
+    return L.fwd_bytes > L.route_bytes ? L.fwd_bytes : L.route_bytes;
+}
+
+int edge_moe_route(const edge_moe_dims* dims, const uint16_t* x, const uint16_t* w_router,
+                   const float* router_bias, int32_t* topk_idx, float* topk_w,
+                   float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_dims(dims);
+    if (st != EDGE_MOE_OK) return st;
+    if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return EDGE_MOE_EINVAL;
+    if (router_bias && !aligned(router_bias, 4)) return EDGE_MOE_EINVAL;
+    if (logits_out && !aligned(logits_out, 4)) return EDGE_MOE_EINVAL;
+    const Layout L = make_layout(*dims);
+    float* logits = logits_out;
+    if (!logits) {
+        if (!ws || !aligned(ws, kAlign)) return ws ? EDGE_MOE_EINVAL : EDGE_MOE_EWORKSPACE;
+        if (ws_bytes < L.route_bytes) return EDGE_MOE_EWORKSPACE;
+        logits = reinterpret_cast<float*>(ws);
+    }
+    st = check_device();
+    if (st != EDGE_MOE_OK) return st;
+    const edge_moe_dims& d = *dims;
+    hipError_t err = em::launch_router(x, w_router, router_bias, logits, topk_idx, topk_w, d.T, d.d,
+                                       d.n_experts, d.top_k, (hipStream_t)stream);
+    return err == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
+}
+
+static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                        const float* topk_w, const edge_moe_weights* wt, float* y, void* ws,
+                        size_t ws_bytes, void* stream, const edge_moe_trace* trace) {
+    int st = check_dims(dims);
+    if (st != EDGE_MOE_OK) return st;
+    if (!wt) return EDGE_MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(y, 16))
+        return EDGE_MOE_EINVAL;
+    const void* wptrs[16] = {wt->s_up_q, wt->s_up_scale, wt->s_dn_q, wt->s_dn_scale,
+                             wt->a_up_q, wt->a_up_scale, wt->b_up_q, wt->b_up_scale,
+                             wt->a_dn_q, wt->a_dn_scale, wt->b_dn_q, wt->b_dn_scale,
+                             wt->lora_up_u, wt->lora_up_v, wt->lora_dn_u, wt->lora_dn_v};
+    for (const void* p : wptrs)
+        if (!aligned(p, 16)) return EDGE_MOE_EINVAL;
+    if (!ws) return EDGE_MOE_EWORKSPACE;
+    if (!aligned(ws, kAlign)) return EDGE_MOE_EINVAL;
+    const Layout L = make_layout(*dims);
+    if (ws_bytes < L.fwd_bytes) return EDGE_MOE_EWORKSPACE;
+    st = check_device();
+    if (st != EDGE_MOE_OK) return st;
+
+    const edge_moe_dims& d = *dims;
+    char* base = reinterpret_cast<char*>(ws);
+    em::LayerArgs a{};
+    a.T = d.T; a.d = d.d; a.h = d.h; a.E = d.n_experts; a.P = d.experts_per_group;
+    a.G = L.G; a.k = d.top_k; a.r = d.delta_rank; a.rL = d.lora_rank; a.gq = d.quant_group;
+    a.mt = 64;
+    a.x = x; a.topk_w = topk_w;
+    a.s_up = wt->s_up_q; a.s_up_s = wt->s_up_scale; a.s_dn = wt->s_dn_q; a.s_dn_s = wt->s_dn_scale;
+    a.a_up = wt->a_up_q; a.a_up_s = wt->a_up_scale; a.b_up = wt->b_up_q; a.b_up_s = wt->b_up_scale;
+    a.a_dn = wt->a_dn_q; a.a_dn_s = wt->a_dn_scale; a.b_dn = wt->b_dn_q; a.b_dn_s = wt->b_dn_scale;
+    a.lu_u = wt->lora_up_u; a.lu_v = wt->lora_up_v; a.ld_u = wt->lora_dn_u; a.ld_v = wt->lora_dn_v;
+    a.z1 = reinterpret_cast<uint16_t*>(base + L.z1);
+    a.zl = reinterpret_cast<uint16_t*>(base + L.zl);
+    a.hs = reinterpret_cast<float*>(base + L.hs);
+    a.act = reinterpret_cast<uint16_t*>(base + L.act);
+    a.z2 = reinterpret_cast<uint16_t*>(base + L.z2);
+    a.zl2 = reinterpret_cast<uint16_t*>(base + L.zl2);
+    a.o = reinterpret_cast<float*>(base + L.o);
+    a.y = y;
+    em::DispatchBufs& db = a.db;
+    db.bm = reinterpret_cast<uint32_t*>(base + L.bm);
+    db.pre = reinterpret_cast<uint32_t*>(base + L.pre);
+    db.total = reinterpret_cast<int32_t*>(base + L.total);
+    db.eoff = reinterpret_cast<int32_t*>(base + L.eoff);
+    db.uoff = reinterpret_cast<int32_t*>(base + L.uoff);
+    db.etile = reinterpret_cast<int32_t*>(base + L.etile);
+    db.gtile_u = reinterpret_cast<int32_t*>(base + L.gtile_u);
+    db.gtile_r = reinterpret_cast<int32_t*>(base + L.gtile_r);
+    db.row_tok = reinterpret_cast<int32_t*>(base + L.row_tok);
+    db.row_slot = reinterpret_cast<int32_t*>(base + L.row_slot);
+    db.row_exp = reinterpret_cast<int32_t*>(base + L.row_exp);
+    db.row_u = reinterpret_cast<int32_t*>(base + L.row_u);
+    db.slot_row = reinterpret_cast<int32_t*>(base + L.slot_row);
+    db.ut_tok = reinterpret_cast<int32_t*>(base + L.ut_tok);
+    const int64_t R = L.R;
+    const int64_t G = L.G;
+    const int64_t E = d.n_experts;
+    a.max_etiles = (int)((R + a.mt - 1) / a.mt + (E < R ? E : R));
+    a.max_gtiles_u = (int)((L.Umax + a.mt - 1) / a.mt + G);
+    a.max_gtiles_r = (int)((R + a.mt - 1) / a.mt + G);
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err = em::launch_dispatch(topk_idx, db, d.T, d.top_k, d.n_experts, d.experts_per_group,
+                                         a.mt, s);
+    if (err != hipSuccess) return EDGE_MOE_EHIP;
+    err = em::launch_expert_layer(a, s);
+    if (err != hipSuccess) return EDGE_MOE_EHIP;
+    if (trace) {
+        auto cp = [&](void* dst, const void* src, size_t bytes) {
+            if (dst && bytes) err = err != hipSuccess ? err : hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+        };
+        cp(trace->expert_offsets, db.eoff, (size_t)(E + 1) * 4);
+        cp(trace->row_token, db.row_tok, (size_t)R * 4);
+        cp(trace->row_slot, db.row_slot, (size_t)R * 4);
+        cp(trace->act, a.act, (size_t)R * d.h * 2);
+        cp(trace->expert_out, a.o, (size_t)R * d.d * 4);
+        if (err != hipSuccess) return EDGE_MOE_EHIP;
+    }
+    return EDGE_MOE_OK;
+}
+
+int edge_moe_forward(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                     const float* topk_w, const edge_moe_weights* weights, float* y, void* ws,
+                     size_t ws_bytes, void* stream) {
+    return forward_impl(dims, x, topk_idx, topk_w, weights, y, ws, ws_bytes, stream, nullptr);
+}
+
+int edge_moe_forward_traced(const edge_moe_dims* dims, const uint16_t* x,
+                            const int32_t* topk_idx, const float* topk_w,
+                            const edge_moe_weights* weights, float* y, void* ws,
+                            size_t ws_bytes, void* stream, const edge_moe_trace* trace) {
+    return forward_impl(dims, x, topk_idx, topk_w, weights, y, ws, ws_bytes, stream, trace);
+}
+
+int edge_moe_residual(int32_t T, int32_t d, const uint16_t* x, const float* y, uint16_t* x_out,
+                      void* stream) {
+    if (T < 1 || d < 8 || d % 8) return EDGE_MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(x_out, 16)) return EDGE_MOE_EINVAL;
+    const int st = check_device();
+    if (st != EDGE_MOE_OK) return st;
+    return em::launch_residual(T, d, x, y, x_out, (hipStream_t)stream) == hipSuccess ? EDGE_MOE_OK
+                                                                                     : EDGE_MOE_EHIP;
+}
+
+const char* edge_moe_status_string(int status) {
+    switch (status) {
+        case EDGE_MOE_OK: return "ok";
+        case EDGE_MOE_EINVAL: return "invalid argument (null or misaligned pointer, inconsistent dims)";
+        case EDGE_MOE_EUNSUPPORTED: return "unsupported shape or device (needs gfx950)";
+        case EDGE_MOE_EWORKSPACE: return "workspace missing or smaller than edge_moe_workspace_bytes()";
+        case EDGE_MOE_EHIP: return "HIP runtime or kernel launch error";
+        default: return "unknown status";
+    }
+}
+
+int edge_moe_abi_version(void) { return EDGE_MOE_ABI_VERSION; }
+
+int edge_moe_prof_enable(int on) {
+    ProfState& p = prof();
+    const int was = p.on ? 1 : 0;
+    p.on = on != 0;
+    return was;
+}
+
+int edge_moe_prof_read(char (*names)[64], int64_t* launches, double* total_ms, int cap) {
+    prof_drain();
+    ProfState& p = prof();
+    int i = 0;
+    for (const auto& n : p.order) {
+        if (i < cap) {
+            const auto& v = p.table[n];
+            if (names) {
+                size_t m = n.size() < 63 ? n.size() : 63;
+                for (size_t j = 0; j < m; ++j) names[i][j] = n[j];
+                names[i][m] = 0;
+            }
+            if (launches) launches[i] = v.first;
+            if (total_ms) total_ms[i] = v.second;
+        }
+        ++i;
+    }
+    return i;
+}
+
+void edge_moe_prof_reset(void) {
+    prof_drain();
+    ProfState& p = prof();
+    p.table.clear();
+    p.order.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,494 @@
+// Expert-layer products (steps a4-a11): int4 grouped GEMMs with the dequant
+// fused into the MFMA operand path, the low-rank and LoRA branches, the
+// activation epilogue and the weighted combine.
+//
+// Each group of 64 experts shares two large matrices and every expert keeps a
+// small set of its own parameters (launch post "Edge0-145B: Frontier AI
+// Capabilities on Your Own Computer", Under the Hood, Architecture paragraph);
+// the difference is taken as a rank-r additive delta and the base as int4 with
+// a parallel bf16 LoRA branch (byteiota "Edge0-145B: Run a 145B Open-Source
+// Model on Your Laptop", The Three Pillars, Recover-LoRA paragraph).  The
+// shared up product is computed once per (token, group) - over the group's
+// distinct tokens - and every weight byte is streamed once per task.
+//
+// Work decomposition: a task is (segment, up to 64 rows, 64 output columns);
+// each of the 4 waves of a workgroup owns 16 output columns and streams those
+// 16 weight rows over K in 128-element chunks: one 16-byte load per lane,
+// exact int4 -> bf16 conversion in registers, 4 MFMA 16x16x32 per 16-row
+// subtile, one fp16 group scale applied to the chunk's fp32 partial sum.
+#include "common.h"
+#include "kernels.h"
+
+namespace em {
+
+enum Mode { M_Z1 = 0, M_HS = 1, M_ACT = 2, M_Z2 = 3, M_OUT = 4 };
+
+constexpr int TASK_ROWS = 64;
+constexpr int NSUB = TASK_ROWS / 16;
+constexpr int KC = 128;
+
+EM_DEV int find_seg(const int32_t* __restrict__ pre, int n, int b) {
+    if (b >= pre[n]) return -1;
+    int lo = 0, hi = n;                       // pre[lo] <= b < pre[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= b) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// int4 weights: 32 elements [kk, kk+32) of one row (kk multiple of 32), as 4 dwords.
+EM_DEV uint4 load_b_i4(const uint8_t* __restrict__ row, int kk, int K) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (kk >= K) return v;
+    if ((K & 31) == 0) return *reinterpret_cast<const uint4*>(row + (kk >> 1));
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(row + (kk >> 1));
+    if (kk + 0 < K) v.x = p[0];
+    if (kk + 8 < K) v.y = p[1];
+    if (kk + 16 < K) v.z = p[2];
+    if (kk + 24 < K) v.w = p[3];
+    return v;
+}
+
+// bf16 weights: elements [kk, kk+8) of one row (K even), zero beyond K.
+EM_DEV uint4 load_b_bf16(const uint16_t* __restrict__ row, int kk, int K) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(row + kk);
+    if (kk + 0 < K) v.x = p[0];
+    if (kk + 2 < K) v.y = p[1];
+    if (kk + 4 < K) v.z = p[2];
+    if (kk + 6 < K) v.w = p[3];
+    return v;
+}
+
+// bf16 activations: elements [kk, kk+8) of a row whose storage is padded to a
+// multiple of 8 elements; elements >= K read as zero.
+EM_DEV uint4 load_a(const uint16_t* __restrict__ row, int kk, int K, bool valid) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (!valid || kk >= K) return v;
+    v = *reinterpret_cast<const uint4*>(row + kk);
+    const int n = K - kk;                     // valid elements, > 0
+    if (n < 8) {
+        uint32_t* u = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (2 * i >= n) u[i] = 0u;
+            else if (2 * i + 1 >= n) u[i] &= 0xFFFFu;
+        }
+    }
+    return v;
+}
+
+EM_DEV void dequant_b(uint4 raw, uint4 b[4]) {
+    uint32_t q[4][4];
+    dequant8(raw.x, q[0]);
+    dequant8(raw.y, q[1]);
+    dequant8(raw.z, q[2]);
+    dequant8(raw.w, q[3]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = make_uint4(q[s][0], q[s][1], q[s][2], q[s][3]);
+}
+
+// One 128-wide int4 chunk: acc[ms] += scale * (A[ms] . W) for each active
+// subtile.  K-slot mapping: lane group c holds chunk elements [32c, 32c+32),
+// MFMA s uses elements [32c + 8s, 32c + 8s + 8).  With quant groups narrower
+// than the chunk (32 or 64) each group gets its own pass in which the A lanes
+// of other groups are zero, so every partial sum carries a single scale.
+EM_DEV void mac_i4(floatx4 acc[NSUB], const uint4 af[NSUB][4], int nsub, uint4 raw,
+                   const uint16_t* __restrict__ srow, bool nvalid, int k0, int gq, int kvalid,
+                   int c) {
+    uint4 b[4];
+    dequant_b(raw, b);
+    if (gq >= kvalid) {
+        const float sc = nvalid ? 16.0f * fp16_bits_to_f32(srow[k0 / gq]) : 0.0f;
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms) {
+            if (ms < nsub) {
+                floatx4 t = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) t = mfma_bf16(af[ms][s], b[s], t);
+                acc[ms] = sc * t + acc[ms];
+            }
+        }
+    } else {
+        const int ng = kvalid / gq;
+        const int lanes_per = gq / 32;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        for (int gi = 0; gi < ng; ++gi) {
+            const bool mine = (c / lanes_per) == gi;
+            const float sc = nvalid ? 16.0f * fp16_bits_to_f32(srow[k0 / gq + gi]) : 0.0f;
+#pragma unroll
+            for (int ms = 0; ms < NSUB; ++ms) {
+                if (ms < nsub) {
+                    floatx4 t = zero4();
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) t = mfma_bf16(mine ? af[ms][s] : z, b[s], t);
+                    acc[ms] = sc * t + acc[ms];
+                }
+            }
+        }
+    }
+}
+
+struct Task {
+    int seg;        // expert or group
+    int rbeg, rend; // rows [rbeg, rend) of this task (row or unique-slot indices)
+};
+
+// Map blockIdx.x onto (segment, 64-row slice).  kind 0: experts' rows, kind 1:
+// groups' unique tokens, kind 2: groups' rows.
+EM_DEV bool get_task(const LayerArgs& a, int kind, Task& tk) {
+    const int b = blockIdx.x;
+    const int32_t* tiles = kind == 0 ? a.db.etile : (kind == 1 ? a.db.gtile_u : a.db.gtile_r);
+    const int nseg = kind == 0 ? a.E : a.G;
+    const int s = find_seg(tiles, nseg, b);
+    if (s < 0) return false;
+    int r0, r1;
+    if (kind == 0) { r0 = a.db.eoff[s]; r1 = a.db.eoff[s + 1]; }
+    else if (kind == 1) { r0 = a.db.uoff[s]; r1 = a.db.uoff[s + 1]; }
+    else { r0 = a.db.eoff[s * a.P]; r1 = a.db.eoff[(s + 1) * a.P]; }
+    const int m = b - tiles[s];
+    tk.seg = s;
+    tk.rbeg = r0 + m * TASK_ROWS;
+    tk.rend = min(r1, tk.rbeg + TASK_ROWS);
+    return tk.rbeg < tk.rend;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(256)
+expert_gemm(LayerArgs a) {
+    constexpr int kind = (MODE == M_Z1 || MODE == M_ACT || MODE == M_Z2) ? 0 : (MODE == M_HS ? 1 : 2);
+    Task tk;
+    if (!get_task(a, kind, tk)) return;
+    const int lane = lane_id();
+    const int c = lane >> 4;
+    const int li = lane & 15;
+    const int n0 = (blockIdx.y * 4 + wave_id()) * 16;
+
+    // ---- per-mode operands
+    int N, K, gq, lda;
+    const uint8_t* W;
+    const uint16_t* S;
+    const uint16_t* A;
+    if constexpr (MODE == M_Z1) {
+        N = a.r; K = a.d; gq = min(a.gq, K); lda = a.d; A = a.x;
+        W = a.a_up + (size_t)tk.seg * a.r * (a.d / 2);
+        S = a.a_up_s + (size_t)tk.seg * a.r * (K / gq);
+    } else if constexpr (MODE == M_HS) {
+        N = a.h; K = a.d; gq = min(a.gq, K); lda = a.d; A = a.x;
+        W = a.s_up + (size_t)tk.seg * a.h * (a.d / 2);
+        S = a.s_up_s + (size_t)tk.seg * a.h * (K / gq);
+    } else if constexpr (MODE == M_ACT) {
+        N = a.h; K = a.r; gq = min(a.gq, K); lda = a.r; A = a.z1;
+        W = a.b_up + (size_t)tk.seg * a.h * (a.r / 2);
+        S = a.b_up_s + (size_t)tk.seg * a.h * (K / gq);
+    } else if constexpr (MODE == M_Z2) {
+        N = a.r; K = a.h; gq = min(a.gq, K); lda = a.h; A = a.act;
+        W = a.a_dn + (size_t)tk.seg * a.r * (a.h / 2);
+        S = a.a_dn_s + (size_t)tk.seg * a.r * (K / gq);
+    } else {
+        N = a.d; K = a.h; gq = min(a.gq, K); lda = a.h; A = a.act;
+        W = a.s_dn + (size_t)tk.seg * a.d * (a.h / 2);
+        S = a.s_dn_s + (size_t)tk.seg * a.d * (K / gq);
+    }
+    if (n0 >= N) return;
+    const int ncol = n0 + li;
+    const bool nvalid = ncol < N;
+    const uint8_t* wrow = W + (size_t)(nvalid ? ncol : 0) * (K / 2);
+    const uint16_t* srow = S + (size_t)(nvalid ? ncol : 0) * (K / gq);
+
+    const int rows = tk.rend - tk.rbeg;
+    const int nsub = (rows + 15) >> 4;
+    const uint16_t* arow[NSUB];
+    bool avalid[NSUB];
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms) {
+        const int i = ms * 16 + li;
+        avalid[ms] = i < rows;
+        const int r = tk.rbeg + (avalid[ms] ? i : 0);
+        int src;
+        if constexpr (MODE == M_Z1) src = a.db.row_tok[r];
+        else if constexpr (MODE == M_HS) src = a.db.ut_tok[r];
+        else src = r;
+        arow[ms] = A + (size_t)src * lda;
+    }
+
+    floatx4 acc[NSUB];
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms) acc[ms] = zero4();
+
+    // ---- main K loop, one chunk of loads in flight ahead of the math
+    uint4 raw = nvalid ? load_b_i4(wrow, 32 * c, K) : make_uint4(0, 0, 0, 0);
+    uint4 af[NSUB][4];
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            af[ms][s] = (ms < nsub) ? load_a(arow[ms], 32 * c + 8 * s, K, avalid[ms]) : make_uint4(0, 0, 0, 0);
+    for (int k0 = 0; k0 < K; k0 += KC) {
+        const int kn = k0 + KC;
+        uint4 raw_n = make_uint4(0, 0, 0, 0);
+        uint4 af_n[NSUB][4];
+        if (kn < K) {
+            raw_n = nvalid ? load_b_i4(wrow, kn + 32 * c, K) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int ms = 0; ms < NSUB; ++ms)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    af_n[ms][s] = (ms < nsub) ? load_a(arow[ms], kn + 32 * c + 8 * s, K, avalid[ms])
+                                              : make_uint4(0, 0, 0, 0);
+        }
+        mac_i4(acc, af, nsub, raw, srow, nvalid, k0, gq, min(KC, K - k0), c);
+        raw = raw_n;
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[ms][s] = af_n[ms][s];
+    }
+
+    // ---- K extensions
+    if constexpr (MODE == M_HS || MODE == M_OUT) {
+        // LoRA branch: V[g] (bf16 [N][rL]) times the rounded LoRA input (bf16 [rows][rL])
+        const int rLp = (a.rL + 7) & ~7;
+        const uint16_t* Vrow = (MODE == M_HS ? a.lu_v + (size_t)tk.seg * a.h * a.rL
+                                             : a.ld_v + (size_t)tk.seg * a.d * a.rL) +
+                               (size_t)(nvalid ? ncol : 0) * a.rL;
+        const uint16_t* Z = MODE == M_HS ? a.zl : a.zl2;
+        for (int kb = 0; kb < a.rL; kb += 32) {
+            const uint4 bv = nvalid ? load_b_bf16(Vrow, kb + 8 * c, a.rL) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int ms = 0; ms < NSUB; ++ms) {
+                if (ms < nsub) {
+                    const int i = ms * 16 + li;
+                    const uint4 av = load_a(Z + (size_t)(tk.rbeg + (i < rows ? i : 0)) * rLp,
+                                            kb + 8 * c, a.rL, i < rows);
+                    acc[ms] = mfma_bf16(av, bv, acc[ms]);
+                }
+            }
+        }
+    }
+    if constexpr (MODE == M_OUT) {
+        // per-expert delta: B_dn[e] (int4 [d][r]) times R(A_dn[e] a) (bf16 [rows][r]),
+        // one pass per distinct expert among the task's rows (rows are expert-sorted)
+        const int gq_r = min(a.gq, a.r);
+        int my_e = -1, prev_e = -1;
+        if (lane < rows) my_e = a.db.row_exp[tk.rbeg + lane];
+        if (lane >= 1 && lane - 1 < rows) prev_e = a.db.row_exp[tk.rbeg + lane - 1];
+        uint64_t starts = __ballot(lane < rows && (lane == 0 || my_e != prev_e));
+        while (starts) {
+            const int p = __ffsll((long long)starts) - 1;
+            starts &= starts - 1;
+            const int pend = starts ? __ffsll((long long)starts) - 1 : rows;
+            const int e = __shfl(my_e, p, kWave);
+            const uint8_t* w2 = a.b_dn + (size_t)e * a.d * (a.r / 2) + (size_t)(nvalid ? ncol : 0) * (a.r / 2);
+            const uint16_t* s2 = a.b_dn_s + (size_t)e * a.d * (a.r / gq_r) + (size_t)(nvalid ? ncol : 0) * (a.r / gq_r);
+            for (int k0 = 0; k0 < a.r; k0 += KC) {
+                const uint4 raw2 = nvalid ? load_b_i4(w2, k0 + 32 * c, a.r) : make_uint4(0, 0, 0, 0);
+                uint4 af2[NSUB][4];
+#pragma unroll
+                for (int ms = 0; ms < NSUB; ++ms) {
+                    const int i = ms * 16 + li;
+                    const bool v = i >= p && i < pend;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        af2[ms][s] = (ms < nsub) ? load_a(a.z2 + (size_t)(tk.rbeg + (v ? i : 0)) * a.r,
+                                                          k0 + 32 * c + 8 * s, a.r, v)
+                                                 : make_uint4(0, 0, 0, 0);
+                }
+                mac_i4(acc, af2, nsub, raw2, s2, nvalid, k0, gq_r, min(KC, a.r - k0), c);
+            }
+        }
+    }
+
+    // ---- epilogue: lane holds rows 16 ms + 4 c + v, column ncol
+    if (!nvalid) return;
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms) {
+        if (ms >= nsub) break;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = ms * 16 + 4 * c + v;
+            if (i >= rows) continue;
+            const int r = tk.rbeg + i;
+            const float val = acc[ms][v];
+            if constexpr (MODE == M_Z1) {
+                a.z1[(size_t)r * a.r + ncol] = (uint16_t)f32_to_bf16_rne(val);
+            } else if constexpr (MODE == M_Z2) {
+                a.z2[(size_t)r * a.r + ncol] = (uint16_t)f32_to_bf16_rne(val);
+            } else if constexpr (MODE == M_HS) {
+                a.hs[(size_t)r * a.h + ncol] = val;
+            } else if constexpr (MODE == M_ACT) {
+                const float hv = val + a.hs[(size_t)a.db.row_u[r] * a.h + ncol];
+                a.act[(size_t)r * a.h + ncol] = (uint16_t)f32_to_bf16_rne(silu(hv));
+            } else {
+                a.o[(size_t)r * a.d + ncol] = val;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ LoRA inputs ----
+// zl[u] = R(U_up[g] x[t_u]) for the distinct tokens of each group and
+// zl2[row] = R(U_dn[g] a[row]) for the rows of each group.  N = rL <= 32, so
+// the 4 waves split K (chunks of 32, round robin) and their partial sums are
+// added in wave order through LDS.
+template <int DOWN>
+__global__ void __launch_bounds__(256)
+lora_in(LayerArgs a) {
+    __shared__ float red[4][2][NSUB][64][4];
+    Task tk;
+    if (!get_task(a, DOWN ? 2 : 1, tk)) return;
+    const int lane = lane_id(), wv = wave_id();
+    const int c = lane >> 4, li = lane & 15;
+    const int K = DOWN ? a.h : a.d;
+    const uint16_t* U = DOWN ? a.ld_u + (size_t)tk.seg * a.rL * a.h
+                             : a.lu_u + (size_t)tk.seg * a.rL * a.d;
+    const uint16_t* A = DOWN ? a.act : a.x;
+    const int rows = tk.rend - tk.rbeg;
+    const int nsub = (rows + 15) >> 4;
+    const uint16_t* arow[NSUB];
+    bool avalid[NSUB];
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms) {
+        const int i = ms * 16 + li;
+        avalid[ms] = i < rows;
+        const int r = tk.rbeg + (avalid[ms] ? i : 0);
+        arow[ms] = A + (size_t)(DOWN ? r : a.db.ut_tok[r]) * K;
+    }
+    floatx4 acc[2][NSUB];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms) acc[nt][ms] = zero4();
+    for (int k0 = 32 * wv; k0 < K; k0 += 128) {
+        uint4 af[NSUB];
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms)
+            af[ms] = ms < nsub ? load_a(arow[ms], k0 + 8 * c, K, avalid[ms]) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = nt * 16 + li;
+            if (nt * 16 >= a.rL) break;
+            const uint4 bv = n < a.rL ? *reinterpret_cast<const uint4*>(U + (size_t)n * K + k0 + 8 * c)
+                                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int ms = 0; ms < NSUB; ++ms)
+                if (ms < nsub) acc[nt][ms] = mfma_bf16(af[ms], bv, acc[nt][ms]);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[wv][nt][ms][lane][v] = acc[nt][ms][v];
+    __syncthreads();
+    if (wv != 0) return;
+    const int rLp = (a.rL + 7) & ~7;
+    uint16_t* Z = DOWN ? a.zl2 : a.zl;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int n = nt * 16 + li;
+        if (n >= a.rL) continue;
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms) {
+            if (ms >= nsub) break;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = ms * 16 + 4 * c + v;
+                if (i >= rows) continue;
+                const float s = ((red[0][nt][ms][lane][v] + red[1][nt][ms][lane][v]) +
+                                 red[2][nt][ms][lane][v]) + red[3][nt][ms][lane][v];
+                Z[(size_t)(tk.rbeg + i) * rLp + n] = (uint16_t)f32_to_bf16_rne(s);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ combine --------
+// y[t] = sum_j w[t, j] o[row(t, j)], j = 0..k-1 in order; a gather, no atomics.
+__global__ void __launch_bounds__(256)
+combine(const float* __restrict__ o, const float* __restrict__ w, const int32_t* __restrict__ slot_row,
+        float* __restrict__ y, int T, int d, int k) {
+    const int64_t i = blockIdx.x * 256ll + threadIdx.x;     // float4 index
+    const int d4 = d >> 2;
+    if (i >= (int64_t)T * d4) return;
+    const int t = (int)(i / d4), n4 = (int)(i % d4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[(size_t)t * k + j];
+        const float4 v = reinterpret_cast<const float4*>(o + (size_t)slot_row[(size_t)t * k + j] * d)[n4];
+        acc.x = fmaf(wj, v.x, acc.x);
+        acc.y = fmaf(wj, v.y, acc.y);
+        acc.z = fmaf(wj, v.z, acc.z);
+        acc.w = fmaf(wj, v.w, acc.w);
+    }
+    reinterpret_cast<float4*>(y + (size_t)t * d)[n4] = acc;
+}
+
+// ------------------------------------------------------------------ residual -------
+// x_out = bf16(x + y) with a single rounding: x (bf16) and y (fp32) sum exactly
+// in float64 for the layer's value ranges, and the float64 is rounded straight
+// to bf16 (nearest-even on the bit pattern) instead of through fp32.
+EM_DEV uint32_t f64_to_bf16_rne(double v) {
+    if (v == 0.0) return (uint32_t)(__double_as_longlong(v) >> 48) & 0x8000u;
+    int e;
+    frexp(v, &e);                             // |v| = m 2^e, m in [0.5, 1)
+    const double ulp = ldexp(1.0, e - 8);     // bf16 spacing in v's binade
+    const double r = rint(v / ulp) * ulp;     // exact scaling; rint is half-to-even
+    return f32_to_bf16_rne((float)r);         // r is a bf16 value: both conversions are exact
+}
+
+__global__ void __launch_bounds__(256)
+residual_add(const uint16_t* __restrict__ x, const float* __restrict__ y, uint16_t* __restrict__ xo,
+             int64_t n) {
+    const int64_t i = blockIdx.x * 256ll + threadIdx.x;
+    if (i >= n) return;
+    const double s = (double)bf16_to_f32(x[i]) + (double)y[i];
+    xo[i] = (uint16_t)f64_to_bf16_rne(s);
+}
+
+hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
+                           hipStream_t s) {
+    const int64_t n = (int64_t)T * d;
+    prof_begin(s);
+    residual_add<<<(int)((n + 255) / 256), 256, 0, s>>>(x, y, x_out, n);
+    prof_end(s, "residual_add");
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ launcher -------
+template <int MODE>
+static void launch_gemm(const LayerArgs& a, int tiles, int N, hipStream_t s, const char* name) {
+    dim3 grid(tiles, (N + 63) / 64);
+    prof_begin(s);
+    expert_gemm<MODE><<<grid, 256, 0, s>>>(a);
+    prof_end(s, name);
+}
+
+hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
+    // a4-a6 inputs: R1 (per row) and R2 (per distinct token of a group)
+    launch_gemm<M_Z1>(a, a.max_etiles, a.r, s, "gemm_z1");
+    prof_begin(s);
+    lora_in<0><<<a.max_gtiles_u, 256, 0, s>>>(a);
+    prof_end(s, "lora_in_up");
+    // a4 + a6: shared up + LoRA up, once per (token, group)
+    launch_gemm<M_HS>(a, a.max_gtiles_u, a.h, s, "gemm_shared_up");
+    // a5 + a7: delta up, sum, SiLU, R3
+    launch_gemm<M_ACT>(a, a.max_etiles, a.h, s, "gemm_delta_up_act");
+    // a9 / a10 inputs: R4 (per row), R5 (per row)
+    launch_gemm<M_Z2>(a, a.max_etiles, a.r, s, "gemm_z2");
+    prof_begin(s);
+    lora_in<1><<<a.max_gtiles_r, 256, 0, s>>>(a);
+    prof_end(s, "lora_in_down");
+    // a8 - a10: shared down + delta down + LoRA down
+    launch_gemm<M_OUT>(a, a.max_gtiles_r, a.d, s, "gemm_down");
+    // a11
+    const int64_t n4 = (int64_t)a.T * (a.d / 4);
+    prof_begin(s);
+    combine<<<(int)((n4 + 255) / 256), 256, 0, s>>>(a.o, a.topk_w, a.db.slot_row, a.y, a.T, a.d, a.k);
+    prof_end(s, "combine");
+    return hipGetLastError();
+}
+
+}  // namespace em

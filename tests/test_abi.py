@@ -1,0 +1,121 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load and export every function that include/edge_moe.h
+declares; validation that happens before any device call (dims, null or
+misaligned pointers, workspace size) is exercised with fake addresses that the
+library never dereferences.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import shared_matrix_expert_amd as em
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "edge_moe.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(edge_moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_set():
+    assert set(header_functions()) == set(em.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = em.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        ctypes.cast(getattr(lib, name), ctypes.c_void_p)
+
+
+def test_abi_version_and_status_strings():
+    assert em.edge_moe_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert em.status_string(st)
+    assert em.status_string(7) == "unknown status"
+
+
+def test_workspace_bytes_valid_and_invalid():
+    for cfg in (0, 1, 2, 3):
+        D = synth.config(cfg).dims
+        n = em.edge_moe_workspace_bytes(D)
+        assert n > 0 and n % 256 == 0
+    D = synth.config(1).dims
+    assert em.edge_moe_workspace_bytes(D.with_T(2)) > em.edge_moe_workspace_bytes(D.with_T(1))
+    bad = [D.with_T(0), synth.Dims(**{**D.__dict__, "n_experts": 500}),
+           synth.Dims(**{**D.__dict__, "top_k": 600}),
+           synth.Dims(**{**D.__dict__, "d": 4000}),
+           synth.Dims(**{**D.__dict__, "quant_group": 48}),
+           synth.Dims(**{**D.__dict__, "lora_rank": 3})]
+    for b in bad:
+        assert em.edge_moe_workspace_bytes(b) == 0, b
+
+
+class _Fake:
+    """Stand-in for a device tensor: an address that is never dereferenced."""
+    def __init__(self, addr, nbytes=1 << 40):
+        self.addr, self.nbytes = addr, nbytes
+
+
+def _call_forward(D, x=0x10000, idx=0x20000, w=0x30000, y=0x40000, ws=0x100000, ws_bytes=None,
+                  wptr=0x50000):
+    lib = em.load()
+    cw = em.CWeights(*([wptr] * len(em._WEIGHT_FIELDS)))
+    if ws_bytes is None:
+        ws_bytes = em.edge_moe_workspace_bytes(D)
+    return lib.edge_moe_forward(ctypes.byref(em.cdims(D)), x, idx, w, ctypes.byref(cw), y, ws,
+                                ws_bytes, None)
+
+
+def test_forward_validation_before_device():
+    D = synth.config(2).dims
+    assert _call_forward(D, x=None) == em.EDGE_MOE_EINVAL
+    assert _call_forward(D, x=0x10008) == em.EDGE_MOE_EINVAL          # not 16-byte aligned
+    assert _call_forward(D, y=0x40004) == em.EDGE_MOE_EINVAL
+    assert _call_forward(D, wptr=None) == em.EDGE_MOE_EINVAL
+    assert _call_forward(D, ws=None) == em.EDGE_MOE_EWORKSPACE
+    assert _call_forward(D, ws=0x100010) == em.EDGE_MOE_EINVAL        # not 256-byte aligned
+    assert _call_forward(D, ws_bytes=1024) == em.EDGE_MOE_EWORKSPACE
+    assert _call_forward(D.with_T(0)) == em.EDGE_MOE_EINVAL
+    assert _call_forward(synth.Dims(**{**D.__dict__, "delta_rank": 12})) == em.EDGE_MOE_EUNSUPPORTED
+    assert _call_forward(synth.Dims(**{**D.__dict__, "top_k": 40})) == em.EDGE_MOE_EUNSUPPORTED
+    lib = em.load()
+    assert lib.edge_moe_forward(None, 0x10000, 0x20000, 0x30000, None, 0x40000, 0x100000, 1 << 30,
+                                None) == em.EDGE_MOE_EINVAL
+
+
+def test_route_validation_before_device():
+    lib = em.load()
+    D = synth.config(2).dims
+    cd = ctypes.byref(em.cdims(D))
+    ok = dict(x=0x10000, wr=0x20000, b=None, idx=0x30000, w=0x40000, lg=None, ws=0x100000,
+              nb=em.edge_moe_workspace_bytes(D))
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.edge_moe_route(cd, a["x"], a["wr"], a["b"], a["idx"], a["w"], a["lg"], a["ws"],
+                                  a["nb"], None)
+    assert call(x=None) == em.EDGE_MOE_EINVAL
+    assert call(wr=0x20002) == em.EDGE_MOE_EINVAL
+    assert call(idx=0x30002) == em.EDGE_MOE_EINVAL
+    assert call(b=0x50001) == em.EDGE_MOE_EINVAL
+    assert call(ws=None) == em.EDGE_MOE_EWORKSPACE
+    assert call(nb=16) == em.EDGE_MOE_EWORKSPACE
+
+
+def test_binding_requires_the_library(tmp_path):
+    em_mod = em
+    saved = em_mod._lib
+    try:
+        em_mod._lib = None
+        with pytest.raises(RuntimeError):
+            em_mod.load(str(tmp_path / "missing.so"))
+    finally:
+        em_mod._lib = saved

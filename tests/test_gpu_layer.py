@@ -1,0 +1,177 @@
+"""GPU parity: the HIP library (through its C-ABI) against the float64 oracle.
+
+Gates: expert indices and their order bit-exact; routing weights |dw| <= 1e-6;
+logits bitwise (both sides round the exact dot product once); layer output
+|dy| <= 2e-3 + 2e-3 |y_ref| on every element; repeated runs bitwise equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+import shared_matrix_expert_amd as em
+import synth
+from oracle.layer import moe_forward, residual, route
+from gpu_helpers import (Layer, bits_to_dev, expected_permutation, f32_to_dev, say,
+                         y_within_tolerance)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+GPU_TINY = synth.Dims(T=5, d=128, h=256, n_experts=16, experts_per_group=4, top_k=3,
+                      delta_rank=8, lora_rank=2, quant_group=32)
+
+
+def _inputs(cfg, seed, layer=0, T=None):
+    x = synth.make_activations(cfg, seed, T=T, layer=layer)
+    wr, bias = synth.make_router(cfg, seed, layer)
+    return x, wr, bias
+
+
+def _check_route(D, x, wr, bias, lay, sample=None):
+    idx, w, lg = lay.route(bits_to_dev(x), bits_to_dev(wr), f32_to_dev(bias))
+    torch.cuda.synchronize()
+    rows = np.arange(D.T) if sample is None else sample
+    ref = route(x[rows], wr, bias, D.top_k)
+    g_idx = idx.cpu().numpy()[rows]
+    g_w = w.cpu().numpy()[rows]
+    g_lg = lg.cpu().numpy()[rows]
+    assert np.array_equal(g_lg.astype(np.float64), ref["logits"]), "logits differ"
+    assert np.array_equal(g_idx, ref["idx"]), "expert indices differ"
+    assert np.max(np.abs(g_w - ref["w"])) <= 1e-6
+    return idx, w, ref
+
+
+def _run_parity(D, x, wr, bias, Wdev, sample=None, keep=False):
+    lay = Layer(D, Wdev)
+    idx, w, ref = _check_route(D, x, wr, bias, lay, sample)
+    y, tr = lay.forward(bits_to_dev(x), idx, w, trace=keep)
+    torch.cuda.synchronize()
+    rows = np.arange(D.T) if sample is None else sample
+    Wh = synth.weights_to_numpy(Wdev)
+    fw = moe_forward(x[rows], ref["idx"], ref["w"], Wh, D.experts_per_group, keep=keep)
+    ok, ratio = y_within_tolerance(y.cpu().numpy()[rows], fw["y"])
+    say(f"  worst |dy| / bound = {ratio:.3g}")
+    assert ok, f"y outside tolerance (worst ratio {ratio:.3g})"
+    return lay, idx, w, y, tr, fw
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_layer(seed):
+    say(f"case: tiny C0 seed={seed}")
+    D = synth.config(0).dims
+    x, wr, bias = _inputs(0, seed)
+    W = synth.make_weights(0, seed, device="cuda")
+    _run_parity(D, x, wr, bias, W)
+
+
+def test_tiny_multi_group_layer():
+    say("case: tiny multi-group")
+    D = GPU_TINY
+    rng = np.random.default_rng(11)
+    x = synth.bf16_bits_from_f32(rng.standard_normal((D.T, D.d), dtype=np.float32))
+    wr = synth.bf16_bits_from_f32(rng.standard_normal((D.n_experts, D.d), dtype=np.float32) * np.float32(0.1))
+    from helpers import random_weights
+    Wh = random_weights(D, 3)
+    Wdev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to("cuda")
+            for k, v in Wh.items()}
+    _run_parity(D, x, wr, None, Wdev)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_layer(seed):
+    say(f"case: decode C1 seed={seed}")
+    D = synth.config(1).dims
+    x, wr, bias = _inputs(1, seed)
+    _run_parity(D, x, wr, bias, synth.make_weights(1, seed, device="cuda"))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_verify_skewed_layer(seed):
+    say(f"case: verify C2 seed={seed}")
+    D = synth.config(2).dims
+    x, wr, bias = _inputs(2, seed)
+    lay, idx, w, y, tr, fw = _run_parity(D, x, wr, bias, synth.make_weights(2, seed, device="cuda"),
+                                         keep=True)
+    # permutation bit-exact against a numpy lexsort
+    offs, rt, rs = expected_permutation(idx.cpu().numpy(), D.n_experts)
+    assert np.array_equal(tr["expert_offsets"].cpu().numpy(), offs)
+    assert np.array_equal(tr["row_token"].cpu().numpy(), rt)
+    assert np.array_equal(tr["row_slot"].cpu().numpy(), rs)
+    # activations: each bf16 equals the oracle's or is one bf16 step away (a
+    # rounding decided on the other side of a midpoint), and such flips are rare
+    act = tr["act"].cpu().numpy().view(np.uint16)
+    ref_a = fw["a"][rt, rs]
+    ref_bits = (ref_a.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+    diff = np.abs(act.astype(np.int64) - ref_bits)
+    assert diff.max() <= 1 and np.mean(diff) < 1e-3, (diff.max(), np.mean(diff))
+    # determinism
+    y2, _ = lay.forward(bits_to_dev(x), idx, w)
+    assert torch.equal(y, y2)
+
+
+def test_prefill_layer_sampled():
+    say("case: prefill C3 seed=0, sampled tokens")
+    D = synth.config(3).dims
+    x, wr, bias = _inputs(3, 0)
+    rng = np.random.default_rng(0)
+    sample = np.unique(np.concatenate([[0, D.T - 1], rng.choice(D.T, 30, replace=False)]))
+    lay, idx, w, y, _, _ = _run_parity(D, x, wr, bias, synth.make_weights(3, 0, device="cuda"),
+                                       sample=sample)
+    y2, _ = lay.forward(bits_to_dev(x), idx, w)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("T", [2, 37, 200])
+def test_ragged_batches(T):
+    """Token counts that leave partial tiles and cross the router's small/large paths."""
+    say(f"case: ragged T={T}")
+    D = synth.config(1).dims.with_T(T)
+    x = synth.make_activations(1, 5, T=T)
+    wr, _ = synth.make_router(1, 5)
+    sample = np.unique(np.linspace(0, T - 1, min(T, 12)).astype(int))
+    _run_parity(D, x, wr, None, synth.make_weights(1, 5, device="cuda"), sample=sample)
+
+
+def test_zero_delta_zero_lora():
+    """Zero deltas and LoRA: every expert of a group is the same FFN (on the GPU too)."""
+    say("case: zero delta / LoRA, verify shapes")
+    D = synth.config(2).dims
+    x, wr, bias = _inputs(2, 0)
+    W = synth.make_weights(2, 0, device="cuda", zero_delta=True, zero_lora=True)
+    _run_parity(D, x, wr, bias, W)
+
+
+def test_top1_routing():
+    say("case: top-1")
+    D = synth.Dims(**{**synth.config(2).dims.__dict__, "top_k": 1})
+    x, wr, _ = _inputs(2, 1)
+    lay = Layer(D, synth.make_weights(2, 1, device="cuda"))
+    idx, w, _ = _check_route(D, x, wr, None, lay)
+    assert torch.all(w == 1.0)
+
+
+def test_residual_bit_exact():
+    say("case: residual")
+    rng = np.random.default_rng(4)
+    x = synth.bf16_bits_from_f32(rng.standard_normal((8, 4096), dtype=np.float32))
+    y = (rng.standard_normal((8, 4096)) * 0.5).astype(np.float32)
+    y[0, :4] = [2.0 ** -8, 3 * 2.0 ** -8, 0.0, -1.0]
+    x[0, :4] = synth.bf16_bits_from_f32(np.array([1.0, 1.0, 0.0, 1.0], dtype=np.float32))
+    xd = bits_to_dev(x)
+    out = torch.empty_like(xd)
+    em.edge_moe_residual(xd, f32_to_dev(y), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), residual(x, y))
+
+
+def test_workspace_too_small_is_rejected():
+    D = synth.config(2).dims
+    x, wr, bias = _inputs(2, 0)
+    lay = Layer(D, synth.make_weights(2, 0, device="cuda"))
+    idx, w, _ = lay.route(bits_to_dev(x), bits_to_dev(wr), f32_to_dev(bias))
+    y = torch.empty(D.T, D.d, dtype=torch.float32, device="cuda")
+    with pytest.raises(em.EdgeMoeError) as ei:
+        em.edge_moe_forward(D, bits_to_dev(x), idx, w, lay.W, y, lay.ws[:1024])
+    assert ei.value.status == em.EDGE_MOE_EWORKSPACE

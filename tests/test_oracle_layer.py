@@ -15,7 +15,7 @@ import pytest
 
 import synth
 from oracle import codecs
-from oracle.layer import moe_forward, route
+from oracle.layer import moe_forward, residual, route
 from helpers import TINY, bf16_from, random_router, random_weights, random_x, set_int4, zero_weights
 
 
@@ -288,3 +288,16 @@ def test_per_element_loops_contract_mode():
             for n in range(d):
                 yt[n] += rt["w"][t, j] * o[n]
         np.testing.assert_allclose(got[t], yt, rtol=1e-12, atol=1e-14)
+
+
+def test_residual_closed_forms():
+    x = bf16_from(np.array([[1.0, 1.0, -1.0, 0.0, 3.0, 2.0 ** -20]], dtype=np.float32))
+    y = np.array([[2.0 ** -8, 3 * 2.0 ** -8, -(2.0 ** -8 + 2.0 ** -30), 0.1, -3.0, 1.0]],
+                 dtype=np.float32)
+    out = codecs.bf16_to_f64(residual(x, y))[0]
+    assert out[0] == 1.0                          # 1 + 2^-8: tie, to even
+    assert out[1] == 1.0 + 2.0 ** -6              # 1 + 3 * 2^-8: tie, to even (up)
+    assert out[2] == -(1.0 + 2.0 ** -7)           # just past the midpoint
+    assert out[3] == 0.10009765625                # bf16(fp32(0.1)) = 205 / 2048
+    assert out[4] == 0.0
+    assert out[5] == 1.0
