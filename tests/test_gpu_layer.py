@@ -99,13 +99,16 @@ def test_verify_skewed_layer(seed):
     assert np.array_equal(tr["expert_offsets"].cpu().numpy(), offs)
     assert np.array_equal(tr["row_token"].cpu().numpy(), rt)
     assert np.array_equal(tr["row_slot"].cpu().numpy(), rs)
-    # activations: each bf16 equals the oracle's or is one bf16 step away (a
-    # rounding decided on the other side of a midpoint), and such flips are rare
+    # activations: a bf16 value differs from the oracle's only where the fp32
+    # pre-activation landed on the other side of a rounding midpoint, i.e. by one
+    # bf16 step of a (2^-8 relative) plus the pre-activation's own fp32 error;
+    # such flips are rare
     act = tr["act"].cpu().numpy().view(np.uint16)
+    a_gpu = (act.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     ref_a = fw["a"][rt, rs]
-    ref_bits = (ref_a.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
-    diff = np.abs(act.astype(np.int64) - ref_bits)
-    assert diff.max() <= 1 and np.mean(diff) < 1e-3, (diff.max(), np.mean(diff))
+    dev = np.abs(a_gpu - ref_a)
+    assert np.all(dev <= 2.0 ** -7 * np.abs(ref_a) + 1e-4), float(np.max(dev))
+    assert np.mean(a_gpu != ref_a) < 1e-3, float(np.mean(a_gpu != ref_a))
     # determinism
     y2, _ = lay.forward(bits_to_dev(x), idx, w)
     assert torch.equal(y, y2)
