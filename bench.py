@@ -1,0 +1,347 @@
+"""Benchmark of the shared-matrix MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole layer (router, permutation, shared / delta /
+LoRA products, activation, combine) over one batch already resident in HBM.
+The headline line measures the T=8 speculative-verify batch with skewed
+routing (the launch post's Scheduling paragraph verifies several draft tokens
+per weight read); each step uses the next of 4 layer instances so that the
+~400 MB a step touches cannot be served from the 256 MB Infinity Cache.  The
+same JSON line carries the 16K-token prefill measurement (byteiota page,
+Benchmark Numbers: 16K prefill).
+
+Printed: ONE JSON line on stdout.  Per-kernel times go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+METRIC = "MoE-layer tokens/s at T=8 verify & 16K prefill; % peak HBM GB/s / % MFMA"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic work ---
+
+def weight_bytes(D):
+    """Bytes of each weight unit: per group (shared pair + LoRA), per expert (deltas)."""
+    d, h, r, rL = D.d, D.h, D.delta_rank, D.lora_rank
+    gs = lambda K: min(D.quant_group, K)  # noqa: E731
+    i4 = lambda N, K: N * K // 2 + N * (K // gs(K)) * 2  # noqa: E731
+    per = {
+        "s_up": i4(h, d), "s_dn": i4(d, h),
+        "lu_u": rL * d * 2, "lu_v": h * rL * 2, "ld_u": rL * h * 2, "ld_v": d * rL * 2,
+        "a_up": i4(r, d), "b_up": i4(h, r), "a_dn": i4(r, h), "b_dn": i4(d, r),
+        "w_router": D.n_experts * D.d * 2,
+    }
+    return per
+
+
+def kernel_bytes(D, idx: np.ndarray):
+    """Algorithmic HBM bytes per launch of each kernel for one routed batch:
+    the weight bytes it must stream (each touched group / distinct expert once)
+    plus the activations it must read and write once."""
+    per = weight_bytes(D)
+    T, k = idx.shape
+    G = len(np.unique(idx // D.experts_per_group))
+    X = len(np.unique(idx))
+    R = T * k
+    U = sum(len(np.unique(np.nonzero((idx // D.experts_per_group) == g)[0]))
+            for g in range(D.n_experts // D.experts_per_group))
+    d, h, r = D.d, D.h, D.delta_rank
+    return {
+        "router_logits_small": per["w_router"] + T * d * 2 + T * D.n_experts * 4,
+        "router_logits_tiled": per["w_router"] + T * d * 2 + T * D.n_experts * 4,
+        "gemm_z1": X * per["a_up"] + R * d * 2 + R * r * 2,
+        "lora_in_up": G * per["lu_u"] + U * d * 2,
+        "gemm_shared_up": G * (per["s_up"] + per["lu_v"]) + U * d * 2 + U * h * 4,
+        "gemm_delta_up_act": X * per["b_up"] + R * r * 2 + R * h * 4 + R * h * 2,
+        "gemm_z2": X * per["a_dn"] + R * h * 2,
+        "lora_in_down": G * per["ld_u"] + R * h * 2,
+        "gemm_down": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2 + R * d * 4,
+        "combine": R * d * 4 + T * d * 4,
+    }, {"groups": G, "experts": X, "rows": R, "unique": U}
+
+
+def step_bytes(D, idx):
+    """Whole-step algorithmic bytes: touched weights once + router weights."""
+    per = weight_bytes(D)
+    G = len(np.unique(idx // D.experts_per_group))
+    X = len(np.unique(idx))
+    g_b = per["s_up"] + per["s_dn"] + per["lu_u"] + per["lu_v"] + per["ld_u"] + per["ld_v"]
+    e_b = per["a_up"] + per["b_up"] + per["a_dn"] + per["b_dn"]
+    return per["w_router"] + G * g_b + X * e_b
+
+
+def kernel_flops(D, idx):
+    """Algorithmic MFMA flops per launch (shared up once per (token, group))."""
+    T, k = idx.shape
+    R = T * k
+    U = sum(len(np.unique(np.nonzero((idx // D.experts_per_group) == g)[0]))
+            for g in range(D.n_experts // D.experts_per_group))
+    d, h, r, rL = D.d, D.h, D.delta_rank, D.lora_rank
+    return {
+        "gemm_z1": 2 * R * r * d,
+        "lora_in_up": 2 * U * rL * d,
+        "gemm_shared_up": 2 * U * h * d + 2 * U * h * rL,
+        "gemm_delta_up_act": 2 * R * h * r,
+        "gemm_z2": 2 * R * r * h,
+        "lora_in_down": 2 * R * rL * h,
+        "gemm_down": 2 * R * d * h + 2 * R * d * r + 2 * R * d * rL,
+    }
+
+
+# ---------------------------------------------------------------- device workload ----
+
+class Workload:
+    def __init__(self, cfg_id, layers, seed=0):
+        import torch
+        import shared_matrix_expert_amd as em
+        import synth
+        self.torch, self.em = torch, em
+        c = synth.config(cfg_id)
+        self.D = c.dims
+        self.cfg_id = cfg_id
+        self.layers = []
+        x = synth.make_activations(cfg_id, seed)
+        self.x_host = x
+        self.x = torch.from_numpy(x.view(np.int16)).cuda()
+        for layer in range(layers):
+            wr, bias = synth.make_router(cfg_id, seed, layer)
+            self.layers.append({
+                "wr_host": wr, "bias_host": bias,
+                "wr": torch.from_numpy(wr.view(np.int16)).cuda(),
+                "bias": None if bias is None else torch.from_numpy(bias).cuda(),
+                "W": synth.make_weights(cfg_id, seed, layer, device="cuda"),
+            })
+        D = self.D
+        self.ws = torch.empty(em.edge_moe_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+        self.idx = torch.empty(D.T, D.top_k, dtype=torch.int32, device="cuda")
+        self.w = torch.empty(D.T, D.top_k, dtype=torch.float32, device="cuda")
+        self.y = torch.empty(D.T, D.d, dtype=torch.float32, device="cuda")
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i):
+        L = self.layers[i % len(self.layers)]
+        em, D = self.em, self.D
+        em.edge_moe_route(D, self.x, L["wr"], L["bias"], self.idx, self.w, None, self.ws, self.stream)
+        em.edge_moe_forward(D, self.x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
+
+    def routed_indices(self):
+        """Expert indices of every layer instance (from one step each)."""
+        out = []
+        for i in range(len(self.layers)):
+            self.step(i)
+            self.torch.cuda.synchronize()
+            out.append(self.idx.cpu().numpy().copy())
+        return out
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def kernel_times(self, steps):
+        """Average per-launch ms of every kernel, from HIP events recorded by the
+        library on the stream it launches on (a separate pass of `steps` steps)."""
+        em, torch = self.em, self.torch
+        em.edge_moe_prof_reset()
+        em.edge_moe_prof_enable(True)
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        em.edge_moe_prof_enable(False)
+        tab = em.edge_moe_prof_read()
+        em.edge_moe_prof_reset()
+        return {k: (n, ms / max(n, 1)) for k, (n, ms) in tab.items()}
+
+
+def roofline_hbm(D, idxs, ktimes):
+    """Dominant kernel by total time; achieved = its algorithmic bytes / its avg time."""
+    name = max(ktimes, key=lambda k: ktimes[k][0] * ktimes[k][1])
+    bytes_per = np.mean([kernel_bytes(D, ix)[0].get(name, 0) for ix in idxs])
+    avg_ms = ktimes[name][1]
+    gbs = bytes_per / (avg_ms * 1e-3) / 1e9
+    return name, {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": name, "avg_ms": round(avg_ms, 5), "bytes_per_launch": int(bytes_per)}
+
+
+def roofline_mfma(D, idxs, ktimes):
+    fl = {k: np.mean([kernel_flops(D, ix).get(k, 0) for ix in idxs]) for k in ktimes}
+    cand = {k: v for k, v in ktimes.items() if fl.get(k, 0) > 0}
+    name = max(cand, key=lambda k: cand[k][0] * cand[k][1])
+    avg_ms = ktimes[name][1]
+    tf = fl[name] / (avg_ms * 1e-3) / 1e12
+    return name, {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                  "kernel": name, "avg_ms": round(avg_ms, 4), "flops_per_launch": int(fl[name])}
+
+
+# ---------------------------------------------------------------- CPU baseline -------
+
+def cpu_baseline(wl: Workload, budget_s: float = 30.0):
+    """The oracle (float64 numpy) on the host cores, on a bounded sample: route +
+    expert layer for the first layer instance's batch, repeated while time allows."""
+    import synth
+    from oracle.layer import moe_forward, route
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    L = wl.layers[0]
+    Wh = synth.weights_to_numpy(L["W"])
+    D = wl.D
+    T = D.T
+    tokens = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        rt = route(wl.x_host, L["wr_host"], L["bias_host"], D.top_k)
+        moe_forward(wl.x_host, rt["idx"], rt["w"], Wh, D.experts_per_group)
+        tokens += T
+        reps += 1
+        if time.perf_counter() - t0 > budget_s / 3 or reps >= 3:
+            break
+    el = time.perf_counter() - t0
+    cores = min(len(os.sched_getaffinity(0)), blas_threads)
+    return {"value": round(tokens / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} x (route + expert layer) on the T={T} batch of layer instance 0, "
+                      f"float64 numpy, {el:.1f} s"}
+
+
+def cpu_baseline_prefill(wl: Workload, n_tokens: int = 16):
+    import synth
+    from oracle.layer import moe_forward, route
+    L = wl.layers[0]
+    Wh = synth.weights_to_numpy(L["W"])
+    D = wl.D
+    x = wl.x_host[:n_tokens]
+    t0 = time.perf_counter()
+    rt = route(x, L["wr_host"], L["bias_host"], D.top_k)
+    moe_forward(x, rt["idx"], rt["w"], Wh, D.experts_per_group)
+    el = time.perf_counter() - t0
+    return {"value": round(n_tokens / el, 3), "unit": "tokens/s",
+            "cores": int(len(os.sched_getaffinity(0))), "kind": "oracle",
+            "sample": f"first {n_tokens} of the 16384 prefill tokens, float64 numpy, {el:.1f} s"}
+
+
+# ---------------------------------------------------------------- main ---------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the layer shards by tokens or by expert group; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import shared_matrix_expert_amd as em
+    em.load()
+    torch.cuda.init()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+
+    # ---- verify T=8, skewed routing, rotating layer instances
+    log("building verify workload ...")
+    wl = Workload(2, args.layers)
+    D = wl.D
+    idxs = wl.routed_indices()
+    sec = wl.time_steps(args.steps, args.warmup)
+    ktimes = wl.kernel_times(max(20, args.steps // 4))
+    for k, (n, ms) in sorted(ktimes.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        log(f"  verify kernel {k:22s} launches {n:5d} avg {ms * 1e3:8.2f} us")
+    kname, roof = roofline_hbm(D, idxs, ktimes)
+    sb = float(np.mean([step_bytes(D, ix) for ix in idxs]))
+    line = {
+        "metric": METRIC,
+        "value": round(D.T / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "speculative-verify batch T=8, skewed routing (48 of 80 top-10 picks "
+                               "in 2 of 8 groups), one layer: d=4096 h=8192 E=512 (8 groups of 64) "
+                               "top-10, int4 shared/delta (Gq=128, fp16 scales), r=128, bf16 LoRA "
+                               "rL=16; steps rotate over %d layer instances" % args.layers,
+                   "T": D.T, "layers_rotated": args.layers},
+        "roofline": roof,
+        "step_hbm": {"bytes_per_step": int(sb), "achieved_GBs": round(sb / sec / 1e9, 1),
+                     "frac": round(sb / sec / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        log("building prefill workload ...")
+        wp = Workload(3, 1)
+        pidx = wp.routed_indices()
+        psec = wp.time_steps(args.prefill_steps, 2)
+        pk = wp.kernel_times(args.prefill_steps)
+        for k, (n, ms) in sorted(pk.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+            log(f"  prefill kernel {k:22s} launches {n:5d} avg {ms:9.3f} ms")
+        pname, proof = roofline_mfma(wp.D, pidx, pk)
+        total_fl = float(np.mean([sum(kernel_flops(wp.D, ix).values()) for ix in pidx]))
+        line["prefill_16k"] = {
+            "value": round(wp.D.T / psec, 1), "unit": "tokens/s", "steps": args.prefill_steps,
+            "ms_per_step": round(psec * 1e3, 3),
+            "workload": "prefill T=16384, one layer, router logits ~ N(0,1) (near-uniform load)",
+            "roofline": proof,
+            "step_mfma": {"flops_per_step": int(total_fl),
+                          "achieved_TFLOPs": round(total_fl / psec / 1e12, 2),
+                          "frac": round(total_fl / psec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        }
+        if not args.no_cpu_baseline:
+            line["prefill_16k"]["cpu_baseline"] = cpu_baseline_prefill(wp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -104,14 +104,14 @@ typedef struct edge_moe_weights {
 } edge_moe_weights;
 
 /* Optional per-stage outputs of edge_moe_forward_traced (device pointers; any
- * member may be NULL).  Rows are the (token, slot) pairs sorted by expert, then
- * token; R = T * top_k. */
+ * member may be NULL).  "Rows" are the R = T * top_k (token, slot) pairs sorted
+ * by expert, then token; "slot" s = t * top_k + j. */
 typedef struct edge_moe_trace {
     int32_t*  expert_offsets;  /* [E+1]  first row of each expert                    */
     int32_t*  row_token;       /* [R]    token of each row                           */
     int32_t*  row_slot;        /* [R]    slot j of each row                          */
-    uint16_t* act;             /* [R][h] bf16 activation a of each row               */
-    float*    expert_out;      /* [R][d] float32 expert output o of each row         */
+    uint16_t* act;             /* [R][h] bf16 activation a of each slot (slot order) */
+    float*    expert_out;      /* [R][d] float32 expert output o of each slot (slot order) */
 } edge_moe_trace;
 
 /* Bytes of device workspace needed by edge_moe_route and edge_moe_forward for

@@ -72,6 +72,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m shared_matrix_expert_amd.build`")
+    # PyTorch-ROCm ships its own HIP runtime; load it first so that the library
+    # binds to the same runtime instance as the streams and memory it is given.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.edge_moe_workspace_bytes.argtypes = [ctypes.POINTER(CDims)]

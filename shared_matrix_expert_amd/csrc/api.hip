@@ -1,12 +1,13 @@
 // C-ABI entry points: validation, workspace layout and launch sequencing.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
 
-#include "../../include/edge_moe.h"
+#include "edge_moe.h"
 #include "kernels.h"
 
 namespace {
@@ -90,6 +91,45 @@ Layout make_layout(const edge_moe_dims& d) {
     return L;
 }
 
+// Small-batch path: T <= 64 tokens and at most 1024 (token, slot) pairs.
+bool use_decode(const edge_moe_dims& d) {
+    // EDGE_MOE_GENERAL_PATH=1 forces the general path (used by tests to cover it)
+    static const bool force_general = [] {
+        const char* v = getenv("EDGE_MOE_GENERAL_PATH");
+        return v && v[0] == '1';
+    }();
+    return !force_general && d.T <= 64 && (int64_t)d.T * d.top_k <= 1024 && d.experts_per_group <= 64;
+}
+
+struct DecLayout {
+    size_t hs, z1p, zlp, act, z2p, z2, zl2, o, cnt_e, cnt_c, bytes;
+    int S1, cb2, ncb2, N2;
+};
+
+DecLayout make_dec_layout(const edge_moe_dims& d) {
+    DecLayout L{};
+    const int64_t T = d.T, R = (int64_t)d.T * d.top_k, G = d.n_experts / d.experts_per_group;
+    const int rLp = (d.lora_rank + 7) & ~7;
+    L.S1 = d.d % 512 == 0 ? d.d / 512 : d.d / 128;
+    L.cb2 = d.h % 512 == 0 ? 512 : (d.h % 256 == 0 ? 256 : 128);
+    L.ncb2 = d.h / L.cb2;
+    L.N2 = ((d.delta_rank + 15) & ~15) + ((d.lora_rank + 15) & ~15);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    L.hs = take((size_t)T * G * d.h * 4);
+    L.z1p = take((size_t)L.S1 * R * d.delta_rank * 4);
+    L.zlp = take((size_t)4 * L.S1 * T * G * rLp * 4);
+    L.act = take((size_t)R * d.h * 2);
+    L.z2p = take((size_t)L.ncb2 * R * L.N2 * 4);
+    L.z2 = take((size_t)R * d.delta_rank * 2);
+    L.zl2 = take((size_t)R * rLp * 2);
+    L.o = take((size_t)R * d.d * 4);
+    L.cnt_e = take((size_t)d.n_experts * 4);
+    L.cnt_c = take((size_t)(d.d / 64) * 4);
+    L.bytes = off;
+    return L;
+}
+
 bool aligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) == 0; }
 
 // gfx950 check, cached per device
@@ -169,7 +209,12 @@ extern "C" {
 size_t edge_moe_workspace_bytes(const edge_moe_dims* dims) {
     if (check_dims(dims) != EDGE_MOE_OK) return 0;
     const Layout L = make_layout(*dims);
-    return L.fwd_bytes > L.route_bytes ? L.fwd_bytes : L.route_bytes;
+    size_t n = L.fwd_bytes > L.route_bytes ? L.fwd_bytes : L.route_bytes;
+    if (use_decode(*dims)) {
+        const DecLayout D = make_dec_layout(*dims);
+        n = n > D.bytes ? n : D.bytes;
+    }
+    return n;
 }
 
 int edge_moe_route(const edge_moe_dims* dims, const uint16_t* x, const uint16_t* w_router,
@@ -196,6 +241,88 @@ int edge_moe_route(const edge_moe_dims* dims, const uint16_t* x, const uint16_t*
     return err == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
 }
 
+static em::DispatchBufs dispatch_bufs(const Layout& L, char* base) {
+    em::DispatchBufs db{};
+    db.bm = reinterpret_cast<uint32_t*>(base + L.bm);
+    db.pre = reinterpret_cast<uint32_t*>(base + L.pre);
+    db.total = reinterpret_cast<int32_t*>(base + L.total);
+    db.eoff = reinterpret_cast<int32_t*>(base + L.eoff);
+    db.uoff = reinterpret_cast<int32_t*>(base + L.uoff);
+    db.etile = reinterpret_cast<int32_t*>(base + L.etile);
+    db.gtile_u = reinterpret_cast<int32_t*>(base + L.gtile_u);
+    db.gtile_r = reinterpret_cast<int32_t*>(base + L.gtile_r);
+    db.row_tok = reinterpret_cast<int32_t*>(base + L.row_tok);
+    db.row_slot = reinterpret_cast<int32_t*>(base + L.row_slot);
+    db.row_exp = reinterpret_cast<int32_t*>(base + L.row_exp);
+    db.row_u = reinterpret_cast<int32_t*>(base + L.row_u);
+    db.slot_row = reinterpret_cast<int32_t*>(base + L.slot_row);
+    db.ut_tok = reinterpret_cast<int32_t*>(base + L.ut_tok);
+    return db;
+}
+
+static hipError_t copy_perm_trace(const edge_moe_trace* trace, const em::DispatchBufs& db,
+                                  const edge_moe_dims& d, hipStream_t s) {
+    const size_t R = (size_t)d.T * d.top_k;
+    hipError_t err = hipSuccess;
+    if (trace->expert_offsets)
+        err = hipMemcpyAsync(trace->expert_offsets, db.eoff, (size_t)(d.n_experts + 1) * 4, hipMemcpyDeviceToDevice, s);
+    if (err == hipSuccess && trace->row_token)
+        err = hipMemcpyAsync(trace->row_token, db.row_tok, R * 4, hipMemcpyDeviceToDevice, s);
+    if (err == hipSuccess && trace->row_slot)
+        err = hipMemcpyAsync(trace->row_slot, db.row_slot, R * 4, hipMemcpyDeviceToDevice, s);
+    return err;
+}
+
+static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint16_t* x,
+                          const int32_t* topk_idx, const float* topk_w, const edge_moe_weights* wt,
+                          float* y, void* ws, void* stream, const edge_moe_trace* trace) {
+    char* base = reinterpret_cast<char*>(ws);
+    em::DecodeArgs a{};
+    a.T = d.T; a.d = d.d; a.h = d.h; a.E = d.n_experts; a.P = d.experts_per_group;
+    a.G = d.n_experts / d.experts_per_group; a.k = d.top_k; a.r = d.delta_rank; a.rL = d.lora_rank;
+    a.rLp = (d.lora_rank + 7) & ~7; a.gq = d.quant_group; a.R = d.T * d.top_k;
+    a.S1 = L.S1; a.cb2 = L.cb2; a.ncb2 = L.ncb2;
+    const int rows_per_pass = 16 * em::decode_ns_down(d.T);
+    a.npass = (a.R + rows_per_pass - 1) / rows_per_pass;
+    a.nxmax = a.R < a.E ? a.R : a.E;
+    a.x = x; a.idx = topk_idx; a.topk_w = topk_w;
+    a.s_up = wt->s_up_q; a.s_up_s = wt->s_up_scale; a.s_dn = wt->s_dn_q; a.s_dn_s = wt->s_dn_scale;
+    a.a_up = wt->a_up_q; a.a_up_s = wt->a_up_scale; a.b_up = wt->b_up_q; a.b_up_s = wt->b_up_scale;
+    a.a_dn = wt->a_dn_q; a.a_dn_s = wt->a_dn_scale; a.b_dn = wt->b_dn_q; a.b_dn_s = wt->b_dn_scale;
+    a.lu_u = wt->lora_up_u; a.lu_v = wt->lora_up_v; a.ld_u = wt->lora_dn_u; a.ld_v = wt->lora_dn_v;
+    a.hs = reinterpret_cast<float*>(base + L.hs);
+    a.z1p = reinterpret_cast<float*>(base + L.z1p);
+    a.zlp = reinterpret_cast<float*>(base + L.zlp);
+    a.act = reinterpret_cast<uint16_t*>(base + L.act);
+    a.z2p = reinterpret_cast<float*>(base + L.z2p);
+    a.z2 = reinterpret_cast<uint16_t*>(base + L.z2);
+    a.zl2 = reinterpret_cast<uint16_t*>(base + L.zl2);
+    a.o = reinterpret_cast<float*>(base + L.o);
+    a.y = y;
+    a.cnt_e = reinterpret_cast<uint32_t*>(base + L.cnt_e);
+    a.cnt_c = reinterpret_cast<uint32_t*>(base + L.cnt_c);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err = em::launch_decode(a, s);
+    if (err != hipSuccess) return EDGE_MOE_EHIP;
+    if (trace) {
+        // intermediates are stored per slot here; the permutation arrays come
+        // from the general dispatch kernels, run after the copies (they reuse
+        // the workspace)
+        if (trace->act) err = hipMemcpyAsync(trace->act, a.act, (size_t)a.R * d.h * 2, hipMemcpyDeviceToDevice, s);
+        if (err == hipSuccess && trace->expert_out)
+            err = hipMemcpyAsync(trace->expert_out, a.o, (size_t)a.R * d.d * 4, hipMemcpyDeviceToDevice, s);
+        if (err != hipSuccess) return EDGE_MOE_EHIP;
+        if (trace->expert_offsets || trace->row_token || trace->row_slot) {
+            const Layout GL = make_layout(d);
+            em::DispatchBufs db = dispatch_bufs(GL, base);
+            err = em::launch_dispatch(topk_idx, db, d.T, d.top_k, d.n_experts, d.experts_per_group, 64, s);
+            if (err == hipSuccess) err = copy_perm_trace(trace, db, d, s);
+            if (err != hipSuccess) return EDGE_MOE_EHIP;
+        }
+    }
+    return EDGE_MOE_OK;
+}
+
 static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                         const float* topk_w, const edge_moe_weights* wt, float* y, void* ws,
                         size_t ws_bytes, void* stream, const edge_moe_trace* trace) {
@@ -213,11 +340,15 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     if (!ws) return EDGE_MOE_EWORKSPACE;
     if (!aligned(ws, kAlign)) return EDGE_MOE_EINVAL;
     const Layout L = make_layout(*dims);
-    if (ws_bytes < L.fwd_bytes) return EDGE_MOE_EWORKSPACE;
+    const bool dec = use_decode(*dims);
+    const DecLayout DL = dec ? make_dec_layout(*dims) : DecLayout{};
+    if (ws_bytes < (dec ? DL.bytes : L.fwd_bytes)) return EDGE_MOE_EWORKSPACE;
+    if (trace && ws_bytes < L.fwd_bytes) return EDGE_MOE_EWORKSPACE;
     st = check_device();
     if (st != EDGE_MOE_OK) return st;
 
     const edge_moe_dims& d = *dims;
+    if (dec) return forward_decode(d, DL, x, topk_idx, topk_w, wt, y, ws, stream, trace);
     char* base = reinterpret_cast<char*>(ws);
     em::LayerArgs a{};
     a.T = d.T; a.d = d.d; a.h = d.h; a.E = d.n_experts; a.P = d.experts_per_group;
@@ -236,21 +367,8 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     a.zl2 = reinterpret_cast<uint16_t*>(base + L.zl2);
     a.o = reinterpret_cast<float*>(base + L.o);
     a.y = y;
+    a.db = dispatch_bufs(L, base);
     em::DispatchBufs& db = a.db;
-    db.bm = reinterpret_cast<uint32_t*>(base + L.bm);
-    db.pre = reinterpret_cast<uint32_t*>(base + L.pre);
-    db.total = reinterpret_cast<int32_t*>(base + L.total);
-    db.eoff = reinterpret_cast<int32_t*>(base + L.eoff);
-    db.uoff = reinterpret_cast<int32_t*>(base + L.uoff);
-    db.etile = reinterpret_cast<int32_t*>(base + L.etile);
-    db.gtile_u = reinterpret_cast<int32_t*>(base + L.gtile_u);
-    db.gtile_r = reinterpret_cast<int32_t*>(base + L.gtile_r);
-    db.row_tok = reinterpret_cast<int32_t*>(base + L.row_tok);
-    db.row_slot = reinterpret_cast<int32_t*>(base + L.row_slot);
-    db.row_exp = reinterpret_cast<int32_t*>(base + L.row_exp);
-    db.row_u = reinterpret_cast<int32_t*>(base + L.row_u);
-    db.slot_row = reinterpret_cast<int32_t*>(base + L.slot_row);
-    db.ut_tok = reinterpret_cast<int32_t*>(base + L.ut_tok);
     const int64_t R = L.R;
     const int64_t G = L.G;
     const int64_t E = d.n_experts;
@@ -265,14 +383,11 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     err = em::launch_expert_layer(a, s);
     if (err != hipSuccess) return EDGE_MOE_EHIP;
     if (trace) {
-        auto cp = [&](void* dst, const void* src, size_t bytes) {
-            if (dst && bytes) err = err != hipSuccess ? err : hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
-        };
-        cp(trace->expert_offsets, db.eoff, (size_t)(E + 1) * 4);
-        cp(trace->row_token, db.row_tok, (size_t)R * 4);
-        cp(trace->row_slot, db.row_slot, (size_t)R * 4);
-        cp(trace->act, a.act, (size_t)R * d.h * 2);
-        cp(trace->expert_out, a.o, (size_t)R * d.d * 4);
+        err = copy_perm_trace(trace, db, d, s);
+        if (err == hipSuccess && trace->act)
+            err = em::launch_gather_rows(a.act, db.slot_row, trace->act, R, (int64_t)d.h * 2, s);
+        if (err == hipSuccess && trace->expert_out)
+            err = em::launch_gather_rows(a.o, db.slot_row, trace->expert_out, R, (int64_t)d.d * 4, s);
         if (err != hipSuccess) return EDGE_MOE_EHIP;
     }
     return EDGE_MOE_OK;

@@ -1,0 +1,815 @@
+// Expert layer for decode and speculative-verify batches (T <= 64 tokens).
+//
+// Generation reads weights far more than it computes with them (launch post
+// "Edge0-145B: Frontier AI Capabilities on Your Own Computer", Why On-Device
+// Models Have Stayed Small; Under the Hood, Scheduling paragraph: verifying
+// several draft tokens per weight read spreads that cost).  At these batch
+// sizes the layer is bound by HBM: every weight byte of the touched groups and
+// experts is streamed once, and the work is cut into three launches so that
+// the GPU spends its time streaming rather than between kernels:
+//
+//   dec_up   shared up (once per token and group), R1 / R2 products (split-K
+//            partial sums); zeroes the arrival counters of the next two.
+//   dec_act  delta up + LoRA up + shared part, SiLU, R3; then the R4 / R5
+//            products over the workgroup's columns as partial sums; the last
+//            workgroup of an expert adds the partials in a fixed order.
+//   dec_down shared down + delta down + LoRA down per group; the last
+//            workgroup of each column block forms y in slot order.
+//
+// No permutation kernel: every workgroup rebuilds the view of the routing it
+// needs (an expert's rows, a group's tokens or rows) from topk_idx in LDS.
+// Every cross-workgroup sum is taken in a fixed order, so results are
+// bitwise reproducible.
+#include "common.h"
+#include "kernels.h"
+#include "mfma_ops.h"
+#include "tile_stream.h"
+
+namespace em {
+
+constexpr int DEC_RMAX = 1024;
+constexpr int DEPTH = 4;
+
+// ------------------------------------------------------------------ routing views --
+struct RouteView {
+    int16_t idx[DEC_RMAX];    // expert of each slot (E <= 1024)
+    uint32_t ebits[32];
+    unsigned long long tmask[64];
+    int start[64];
+    int16_t rows[DEC_RMAX];   // row -> slot (t*k + j)
+    int8_t rtok[DEC_RMAX];    // row -> token (T <= 64)
+    int nrows;
+    int sel;
+    uint32_t flag;
+};
+
+EM_DEV void rv_load(RouteView& v, const int32_t* __restrict__ idx, int R) {
+    for (int i = threadIdx.x; i < R; i += blockDim.x) v.idx[i] = (int16_t)idx[i];
+    __syncthreads();
+}
+
+// The xi-th smallest expert that any slot selected, or -1.
+EM_DEV int rv_distinct_expert(RouteView& v, int R, int E, int xi) {
+    const int nw = (E + 31) >> 5;
+    if ((int)threadIdx.x < nw) v.ebits[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < R; i += blockDim.x) atomicOr(&v.ebits[v.idx[i] >> 5], 1u << (v.idx[i] & 31));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int sel = -1, acc = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int pc = __popc(v.ebits[w]);
+            if (xi < acc + pc) {
+                uint32_t b = v.ebits[w];
+                for (int r = xi - acc; r > 0; --r) b &= b - 1u;
+                sel = w * 32 + __ffs(b) - 1;
+                break;
+            }
+            acc += pc;
+        }
+        v.sel = sel;
+    }
+    __syncthreads();
+    return v.sel;
+}
+
+// Rows of expert e (one per token that chose it) in token order.
+EM_DEV int rv_expert_rows(RouteView& v, int e, int T, int k) {
+    if (threadIdx.x < 64) {
+        const int t = threadIdx.x;
+        int slot = -1;
+        if (t < T)
+            for (int j = 0; j < k; ++j)
+                if (v.idx[t * k + j] == e) slot = t * k + j;
+        const unsigned long long m = __ballot(slot >= 0);
+        if (slot >= 0) {
+            const int pos = __popcll(m & ((1ull << t) - 1ull));
+            v.rows[pos] = slot;
+            v.rtok[pos] = t;
+        }
+        if (t == 0) v.nrows = __popcll(m);
+    }
+    __syncthreads();
+    return v.nrows;
+}
+
+// Distinct tokens of group g in token order (rows[] = rtok[] = token).
+EM_DEV int rv_group_tokens(RouteView& v, int g, int T, int k, int P) {
+    if (threadIdx.x < 64) {
+        const int t = threadIdx.x;
+        bool in = false;
+        if (t < T)
+            for (int j = 0; j < k; ++j) in |= (v.idx[t * k + j] / P) == g;
+        const unsigned long long m = __ballot(in);
+        if (in) {
+            const int pos = __popcll(m & ((1ull << t) - 1ull));
+            v.rows[pos] = t;
+            v.rtok[pos] = t;
+        }
+        if (t == 0) v.nrows = __popcll(m);
+    }
+    __syncthreads();
+    return v.nrows;
+}
+
+// Slots of group g sorted by (expert, token).
+EM_DEV int rv_group_rows(RouteView& v, int g, int T, int k, int P, int R) {
+    if (threadIdx.x < 64) v.tmask[threadIdx.x] = 0ull;
+    __syncthreads();
+    for (int i = threadIdx.x; i < R; i += blockDim.x) {
+        const int e = v.idx[i];
+        if (e / P == g) atomicOr(&v.tmask[e - g * P], 1ull << (i / k));
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        const int cnt = l < P ? __popcll(v.tmask[l]) : 0;
+        int x = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (l >= off) x += y;
+        }
+        v.start[l] = x - cnt;
+        if (l == 63) v.nrows = x;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < R; i += blockDim.x) {
+        const int e = v.idx[i];
+        if (e / P == g) {
+            const int el = e - g * P, t = i / k;
+            const int r = v.start[el] + __popcll(v.tmask[el] & ((1ull << t) - 1ull));
+            v.rows[r] = i;
+            v.rtok[r] = t;
+        }
+    }
+    __syncthreads();
+    return v.nrows;
+}
+
+// Whether any slot selected an expert of group g (cheap test before building rows).
+EM_DEV bool rv_group_any(RouteView& v, int g, int P, int R) {
+    int c = 0;
+    for (int i = threadIdx.x; i < R; i += blockDim.x) c += (v.idx[i] / P) == g;
+    return __syncthreads_count(c > 0) != 0;
+}
+
+// Cross-workgroup data of the arrival patterns below is written and read with
+// agent-scope relaxed atomic accesses, which are coherent across the XCDs'
+// L2s without an L2 write-back or invalidation (a release or acquire fence at
+// agent scope would flush or invalidate the whole L2 of the XCD, and every
+// workgroup would pay for it).
+EM_DEV void st_agent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+EM_DEV float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Count this workgroup's arrival at `counter` once its agent-scope stores have
+// completed, and return (to every thread) whether it arrived last of `expected`.
+EM_DEV bool arrive_last(RouteView& v, uint32_t* counter, uint32_t expected) {
+    __builtin_amdgcn_s_waitcnt(0);        // this wave's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.flag = (old == expected - 1u) ? 1u : 0u;
+    }
+    __syncthreads();
+    return v.flag != 0u;
+}
+
+// Sum of n partials at p[0], p[stride], ... in index order, read with agent
+// scope, loads issued eight at a time.
+EM_DEV float ordered_sum_agent(const float* p, int n, size_t stride) {
+    float sum = 0.f;
+    for (int s0 = 0; s0 < n; s0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = ld_agent(p + (size_t)min(s0 + u, n - 1) * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < n) sum += t[u];
+    }
+    return sum;
+}
+
+// ------------------------------------------------------------------ kernel 1 -------
+// K elements per LDS block for NS activation subtiles
+template <int NS> struct KBlock { static constexpr int value = 512 / NS; };
+
+template <int NS, bool LDSP>
+__global__ void __launch_bounds__(256)
+dec_up(DecodeArgs a) {
+    constexpr int KB = KBlock<NS>::value;
+    constexpr int LNS = LDSP ? NS : 1;                 // no LDS tiles in the fallback instance
+    constexpr int LKB = LDSP ? KB : 128;
+    __shared__ RouteView v;
+    __shared__ StreamLds<LNS, LKB> L;
+    __shared__ const uint16_t* arow_l[16 * NS];
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < a.E; i += blockDim.x) a.cnt_e[i] = 0u;
+        for (int i = threadIdx.x; i < a.d / 64; i += blockDim.x) a.cnt_c[i] = 0u;
+    }
+    rv_load(v, a.idx, a.R);
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    int b = blockIdx.x;
+    const int nbh = a.h / 64;
+    const int nHS = a.G * nbh;
+    const int nbr = (a.r + 63) / 64;
+    const int nZ1 = a.nxmax * a.S1 * nbr;
+    const int ks = a.d / a.S1;
+    const int gq = min(a.gq, a.d);
+    const bool fast = gq >= KC && (ks / KC) % DEPTH == 0 && (a.d / KC) % DEPTH == 0;
+    constexpr bool lds = LDSP;                         // workgroup streaming through LDS
+
+    if (b < nHS) {
+        // ---- shared up for the distinct tokens of group g, 64 columns
+        const int g = b / nbh, nb = b % nbh;
+        const int nrows = rv_group_tokens(v, g, a.T, a.k, a.P);
+        if (nrows == 0) return;
+        const int nsub = (nrows + 15) >> 4;
+        const int ncol = nb * 64 + wv * 16 + li;
+        floatx4 acc[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+        if constexpr (lds) {
+            if ((int)threadIdx.x < 16 * NS)
+                arow_l[threadIdx.x] = a.x + (size_t)v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0] * a.d;
+            __syncthreads();
+            const size_t r0 = (size_t)g * a.h + nb * 64;
+            const StreamArgs sa{a.s_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.s_up_s + r0 * (a.d / gq),
+                                (size_t)(a.d / gq), 64, gq};
+            stream_gemm<NS, KB>(acc, L, sa, arow_l, nrows, 0, a.d);
+        } else {
+            const uint8_t* wrow = a.s_up + ((size_t)g * a.h + ncol) * (a.d / 2);
+            const uint16_t* srow = a.s_up_s + ((size_t)g * a.h + ncol) * (a.d / gq);
+            const uint16_t* arow[NS];
+            bool av[NS];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) {
+                const int i = ms * 16 + li;
+                av[ms] = i < nrows;
+                arow[ms] = a.x + (size_t)v.rtok[av[ms] ? i : 0] * a.d;
+            }
+            if (fast) stream_i4_fast<NS, DEPTH>(acc, wrow, srow, 0, a.d, gq, arow, c);
+            else stream_i4<NS, DEPTH>(acc, wrow, srow, true, 0, a.d, a.d, gq, arow, av, nsub, c);
+        }
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ms * 16 + 4 * c + q;
+                if (i < nrows) a.hs[((size_t)v.rtok[i] * a.G + g) * a.h + ncol] = acc[ms][q];
+            }
+        return;
+    }
+    b -= nHS;
+    if (b < nZ1) {
+        // ---- R1 input: partial sums of A_up[e] x over one K slice
+        const int xi = b / (a.S1 * nbr);
+        const int rem = b % (a.S1 * nbr);
+        const int s = rem / nbr, nb = rem % nbr;
+        const int e = rv_distinct_expert(v, a.R, a.E, xi);
+        if (e < 0) return;
+        const int nrows = rv_expert_rows(v, e, a.T, a.k);
+        const int nsub = (nrows + 15) >> 4;
+        const int n0 = nb * 64 + wv * 16;
+        const int ncol = n0 + li;
+        const bool nvalid = ncol < a.r;
+        floatx4 acc[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+        if constexpr (lds) {
+            if ((int)threadIdx.x < 16 * NS)
+                arow_l[threadIdx.x] = a.x + (size_t)v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0] * a.d;
+            __syncthreads();
+            const size_t r0 = (size_t)e * a.r + nb * 64;
+            const StreamArgs sa{a.a_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.a_up_s + r0 * (a.d / gq),
+                                (size_t)(a.d / gq), min(64, a.r - nb * 64), gq};
+            stream_gemm<NS, KB>(acc, L, sa, arow_l, nrows, s * ks, (s + 1) * ks);
+        } else {
+            if (n0 >= a.r) return;
+            const uint8_t* wrow = a.a_up + ((size_t)e * a.r + (nvalid ? ncol : 0)) * (a.d / 2);
+            const uint16_t* srow = a.a_up_s + ((size_t)e * a.r + (nvalid ? ncol : 0)) * (a.d / gq);
+            const uint16_t* arow[NS];
+            bool av[NS];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) {
+                const int i = ms * 16 + li;
+                av[ms] = i < nrows;
+                arow[ms] = a.x + (size_t)v.rtok[av[ms] ? i : 0] * a.d;
+            }
+            if (fast) stream_i4_fast<NS, DEPTH>(acc, wrow, srow, s * ks, (s + 1) * ks, gq, arow, c);
+            else stream_i4<NS, DEPTH>(acc, wrow, srow, nvalid, s * ks, (s + 1) * ks, a.d, gq, arow, av, nsub, c);
+        }
+        if (!nvalid) return;
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ms * 16 + 4 * c + q;
+                if (i < nrows) a.z1p[((size_t)s * a.R + v.rows[i]) * a.r + ncol] = acc[ms][q];
+            }
+        return;
+    }
+    b -= nZ1;
+    {
+        // ---- R2 input: partial sums of U_up[g] x; wave wv takes a quarter of slice s
+        const int g = b / a.S1, s = b % a.S1;
+        if (g >= a.G) return;
+        const int nrows = rv_group_tokens(v, g, a.T, a.k, a.P);
+        if (nrows == 0) return;
+        const int kb = s * ks + wv * (ks / 4);
+        const int nstep = ks / 4 / 32;                 // 1 or 4
+        const uint16_t* arow[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) {
+            const int i = ms * 16 + li;
+            arow[ms] = a.x + (size_t)v.rtok[i < nrows ? i : 0] * a.d;
+        }
+        for (int nt = 0; nt * 16 < a.rL; ++nt) {
+            const int n = nt * 16 + li;
+            const bool nvalid = n < a.rL;
+            const uint16_t* urow = a.lu_u + ((size_t)g * a.rL + (nvalid ? n : 0)) * a.d;
+            uint4 bv[4], av4[4][NS];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int kk = kb + min(st, nstep - 1) * 32 + 8 * c;
+                bv[st] = ld16(urow + kk);
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms) av4[st][ms] = ld16(arow[ms] + kk);
+            }
+            floatx4 acc[NS];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                if (st < nstep)
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(av4[st][ms], bv[st], acc[ms]);
+            if (!nvalid) continue;
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = ms * 16 + 4 * c + q;
+                    if (i < nrows)
+                        a.zlp[(((size_t)(s * 4 + wv) * a.T + v.rtok[i]) * a.G + g) * a.rLp + n] = acc[ms][q];
+                }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ kernel 2 -------
+// LDS row strides (elements) of the staged bf16 operands, padded against bank conflicts.
+constexpr int ZS_W = 264;     // z1 rows, r <= 256
+constexpr int ZL_W = 40;      // zl rows, rLp <= 32
+constexpr int AS_W = 520;     // activation rows of the workgroup's columns, cb2 <= 512
+
+// bf16 operand from LDS: elements [kk, kk+8) of a row, zero beyond K or for an invalid row.
+EM_DEV uint4 lds_a(const uint16_t* row, int kk, int K, bool valid) {
+    uint4 v = zero_u4();
+    if (!valid || kk >= K) return v;
+    v = *reinterpret_cast<const uint4*>(row + kk);
+    const int n = K - kk;
+    if (n < 8) {
+        uint32_t* u = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (2 * i >= n) u[i] = 0u;
+            else if (2 * i + 1 >= n) u[i] &= 0xFFFFu;
+        }
+    }
+    return v;
+}
+
+template <int NS>
+__global__ void __launch_bounds__(256)
+dec_act(DecodeArgs a) {
+    __shared__ RouteView v;
+    __shared__ __attribute__((aligned(16))) uint16_t zs[16 * NS][ZS_W];
+    __shared__ __attribute__((aligned(16))) uint16_t zls[16 * NS][ZL_W];
+    __shared__ __attribute__((aligned(16))) uint16_t as_[16 * NS][AS_W];
+    rv_load(v, a.idx, a.R);
+    const int xi = blockIdx.x / a.ncb2, cb = blockIdx.x % a.ncb2;
+    const int e = rv_distinct_expert(v, a.R, a.E, xi);
+    if (e < 0) return;
+    const int nrows = rv_expert_rows(v, e, a.T, a.k);
+    const int g = e / a.P;
+    const int nsub = (nrows + 15) >> 4;
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    const int gq_r = min(a.gq, a.r);
+    const int gq_h = min(a.gq, a.h);
+    // one chunk, one scale, whole 16-byte rows of V: the branch-free variant
+    const bool fast = a.r == KC && gq_r == KC && a.rL % 8 == 0 && gq_h >= KC;
+
+    // ---- R1, R2: finish the split-K sums in slice order and round to bf16
+    for (int i = threadIdx.x; i < 16 * NS * ZS_W; i += blockDim.x) {
+        const int row = i / ZS_W, col = i % ZS_W;
+        if (row >= nrows || col >= a.r) zs[row][col] = 0;
+    }
+    for (int i = threadIdx.x; i < 16 * NS * ZL_W; i += blockDim.x) {
+        const int row = i / ZL_W, col = i % ZL_W;
+        if (row >= nrows || col >= a.rL) zls[row][col] = 0;
+    }
+    for (int i = threadIdx.x; i < nrows * a.r; i += blockDim.x) {
+        const int row = i / a.r, col = i % a.r;
+        const float sum = ordered_sum(a.z1p + (size_t)v.rows[row] * a.r + col, a.S1, (size_t)a.R * a.r);
+        zs[row][col] = (uint16_t)f32_to_bf16_rne(sum);
+    }
+    for (int i = threadIdx.x; i < nrows * a.rL; i += blockDim.x) {
+        const int row = i / a.rL, col = i % a.rL;
+        const float sum = ordered_sum(a.zlp + ((size_t)v.rtok[row] * a.G + g) * a.rLp + col, 4 * a.S1,
+                                      (size_t)a.T * a.G * a.rLp);
+        zls[row][col] = (uint16_t)f32_to_bf16_rne(sum);
+    }
+    __syncthreads();
+
+    // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h)) for this wave's columns
+    const int ncw = a.cb2 / 4;                        // columns per wave: 32, 64 or 128
+    const int col0 = cb * a.cb2 + wv * ncw;
+    int tq[NS][4];                                    // token of each output row of this lane
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = ms * 16 + 4 * c + q;
+            tq[ms][q] = v.rtok[i < nrows ? i : 0];
+        }
+    for (int nt0 = 0; nt0 < ncw / 16; nt0 += 4) {
+        // issue the loads of 4 column tiles before any arithmetic
+        uint4 raw[4], vb[4];
+        uint32_t sb[4];
+        float hv[4][NS][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int nt = min(nt0 + u, ncw / 16 - 1);
+            const int ncol = col0 + nt * 16 + li;
+            if (fast) {
+                raw[u] = ld16(a.b_up + ((size_t)e * a.h + ncol) * (KC / 2) + 16 * c);
+                sb[u] = a.b_up_s[(size_t)e * a.h + ncol];
+                const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
+                vb[u] = 8 * c < a.rL ? t : zero_u4();
+            }
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hv[u][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int nt = nt0 + u;
+            if (nt >= ncw / 16) break;
+            const int ncol = col0 + nt * 16 + li;
+            floatx4 acc[NS];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+            if (fast) {
+                uint4 af[NS][4];
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
+                mac_fast<NS>(acc, af, raw[u], sb[u]);
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+                    acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[u], acc[ms]);
+            } else {
+                const uint8_t* brow = a.b_up + ((size_t)e * a.h + ncol) * (a.r / 2);
+                const uint16_t* bsrow = a.b_up_s + ((size_t)e * a.h + ncol) * (a.r / gq_r);
+                const uint16_t* vrow = a.lu_v + ((size_t)g * a.h + ncol) * a.rL;
+                for (int k0 = 0; k0 < a.r; k0 += KC) {
+                    const int kv = min(KC, a.r - k0);
+                    const uint4 rw = load_b_i4(brow, k0 + 32 * c, a.r);
+                    const uint2 sc2 = load_scales(bsrow, k0, gq_r, kv, true);
+                    uint4 af[NS][4];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            af[ms][s] = lds_a(&zs[ms * 16 + li][0], k0 + 32 * c + 8 * s, a.r, true);
+                    mac_i4<NS>(acc, af, nsub, rw, sc2, gq_r, kv, c);
+                }
+                for (int kb = 0; kb < a.rL; kb += 32) {
+                    const uint4 bv = load_b_bf16(vrow, kb + 8 * c, a.rL);
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+                        acc[ms] = mfma_bf16(lds_a(&zls[ms * 16 + li][0], kb + 8 * c, a.rL, true), bv, acc[ms]);
+                }
+            }
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = ms * 16 + 4 * c + q;
+                    uint16_t ab = 0;
+                    if (i < nrows) {
+                        ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[u][ms][q]));
+                        a.act[(size_t)v.rows[i] * a.h + ncol] = ab;
+                    }
+                    as_[i][wv * ncw + nt * 16 + li] = ab;
+                }
+        }
+    }
+    __syncthreads();
+
+    // ---- R4, R5 inputs: partial sums over this workgroup's columns; columns
+    // [0, r16) hold A_dn[e] rows, [r16, r16 + rL) hold U_dn[g] rows
+    const int r16 = (a.r + 15) & ~15;
+    const int N2 = r16 + ((a.rL + 15) & ~15);
+    const int nt2n = N2 / 16;
+    for (int nt2 = wv; nt2 < nt2n; nt2 += 4) {
+        const int n2 = nt2 * 16 + li;
+        floatx4 acc[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+        if (nt2 * 16 < r16) {
+            const bool nvalid = n2 < a.r;
+            const uint8_t* wrow = a.a_dn + ((size_t)e * a.r + (nvalid ? n2 : 0)) * (a.h / 2);
+            const uint16_t* srow = a.a_dn_s + ((size_t)e * a.r + (nvalid ? n2 : 0)) * (a.h / gq_h);
+            if (fast && a.cb2 == 4 * KC) {
+                uint4 raw[4];
+                uint32_t sb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int kg = cb * a.cb2 + u * KC;
+                    raw[u] = ld16(wrow + ((kg + 32 * c) >> 1));
+                    sb[u] = srow[kg / gq_h];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    uint4 af[NS][4];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
+                    mac_fast<NS>(acc, af, raw[u], sb[u]);
+                }
+            } else {
+                for (int kk = 0; kk < a.cb2; kk += KC) {
+                    const int kg = cb * a.cb2 + kk;
+                    const uint4 rw = nvalid ? load_b_i4(wrow, kg + 32 * c, a.h) : zero_u4();
+                    const uint2 sb2 = load_scales(srow, kg, gq_h, KC, nvalid);
+                    uint4 af[NS][4];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            af[ms][s] = lds_a(&as_[ms * 16 + li][0], kk + 32 * c + 8 * s, a.cb2, true);
+                    mac_i4<NS>(acc, af, nsub, rw, sb2, gq_h, KC, c);
+                }
+            }
+        } else {
+            const int cl = n2 - r16;
+            const bool nvalid = cl < a.rL;
+            const uint16_t* urow = a.ld_u + ((size_t)g * a.rL + (nvalid ? cl : 0)) * a.h + cb * a.cb2;
+            for (int kk0 = 0; kk0 < a.cb2; kk0 += 128) {
+                uint4 bv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) bv[u] = ld16(urow + kk0 + 32 * u + 8 * c);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (!nvalid) bv[u] = zero_u4();
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+                        acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][kk0 + 32 * u + 8 * c]),
+                                            bv[u], acc[ms]);
+                }
+            }
+        }
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ms * 16 + 4 * c + q;
+                if (i < nrows) st_agent(&a.z2p[((size_t)cb * a.R + v.rows[i]) * N2 + n2], acc[ms][q]);
+            }
+    }
+
+    // ---- the last column block of expert e adds the partials in block order
+    if (!arrive_last(v, &a.cnt_e[e], (uint32_t)a.ncb2)) return;
+    for (int i = threadIdx.x; i < nrows * N2; i += blockDim.x) {
+        const int row = i / N2, n2 = i % N2;
+        const int slot = v.rows[row];
+        const float sum = ordered_sum_agent(a.z2p + (size_t)slot * N2 + n2, a.ncb2, (size_t)a.R * N2);
+        const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum);
+        if (n2 < a.r) a.z2[(size_t)slot * a.r + n2] = bits;
+        else if (n2 >= r16 && n2 - r16 < a.rL) a.zl2[(size_t)slot * a.rLp + (n2 - r16)] = bits;
+    }
+}
+
+// ------------------------------------------------------------------ kernel 3 -------
+template <int NS, bool LDSP>
+__global__ void __launch_bounds__(256)
+dec_down(DecodeArgs a) {
+    constexpr int KB = KBlock<NS>::value;
+    constexpr int LNS = LDSP ? NS : 1;
+    constexpr int LKB = LDSP ? KB : 128;
+    __shared__ RouteView v;
+    __shared__ StreamLds<LNS, LKB> L;
+    __shared__ const uint16_t* arow_l[16 * NS];
+    rv_load(v, a.idx, a.R);
+    const int nbd = a.d / 64;
+    const int pass = blockIdx.x / (a.G * nbd);
+    const int g = (blockIdx.x / nbd) % a.G;
+    const int nb = blockIdx.x % nbd;
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    const int m0 = pass * 16 * NS;
+    int nrows = 0;
+    if (rv_group_any(v, g, a.P, a.R)) nrows = rv_group_rows(v, g, a.T, a.k, a.P, a.R);
+    const int prow = min(nrows - m0, 16 * NS);          // rows of this pass
+    if (prow > 0) {
+        const int nsub = (prow + 15) >> 4;
+        const int ncol = nb * 64 + wv * 16 + li;
+        const int gq = min(a.gq, a.h);
+        const int gq_r = min(a.gq, a.r);
+        const bool fast = gq >= KC && (a.h / KC) % DEPTH == 0 && a.r == KC && gq_r == KC && a.rL % 8 == 0;
+        int slot_i[NS];                                  // slot of the A row this lane supplies
+        bool av[NS];
+        const uint16_t* arow[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) {
+            const int i = ms * 16 + li;
+            av[ms] = i < prow;
+            slot_i[ms] = v.rows[m0 + (av[ms] ? i : 0)];
+            arow[ms] = a.act + (size_t)slot_i[ms] * a.h;
+        }
+        // LoRA down operands, issued ahead of the main stream
+        const uint16_t* vrow = a.ld_v + ((size_t)g * a.d + ncol) * a.rL;
+        uint4 lv = zero_u4(), lz[NS];
+        if (fast) {
+            const uint4 t = ld16(vrow + min(8 * c, a.rL - 8));
+            lv = 8 * c < a.rL ? t : zero_u4();
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) {
+                const uint4 z = ld16(a.zl2 + (size_t)slot_i[ms] * a.rLp + min(8 * c, a.rLp - 8));
+                lz[ms] = (8 * c < a.rL) ? z : zero_u4();
+            }
+        }
+        floatx4 acc[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+        const uint8_t* wrow = a.s_dn + ((size_t)g * a.d + ncol) * (a.h / 2);
+        const uint16_t* srow = a.s_dn_s + ((size_t)g * a.d + ncol) * (a.h / gq);
+        if constexpr (LDSP) {
+            if ((int)threadIdx.x < 16 * NS)
+                arow_l[threadIdx.x] = a.act + (size_t)v.rows[m0 + ((int)threadIdx.x < prow ? threadIdx.x : 0)] * a.h;
+            __syncthreads();
+            const size_t r0 = (size_t)g * a.d + nb * 64;
+            const StreamArgs sa{a.s_dn + r0 * (a.h / 2), (size_t)(a.h / 2), a.s_dn_s + r0 * (a.h / gq),
+                                (size_t)(a.h / gq), 64, gq};
+            stream_gemm<NS, KB>(acc, L, sa, arow_l, prow, 0, a.h);
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(lz[ms], lv, acc[ms]);
+        } else if (fast) {
+            stream_i4_fast<NS, DEPTH>(acc, wrow, srow, 0, a.h, gq, arow, c);
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(lz[ms], lv, acc[ms]);
+        } else {
+            stream_i4<NS, DEPTH>(acc, wrow, srow, true, 0, a.h, a.h, gq, arow, av, nsub, c);
+            for (int kb = 0; kb < a.rL; kb += 32) {
+                const uint4 bv = load_b_bf16(vrow, kb + 8 * c, a.rL);
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+                    if (ms < nsub)
+                        acc[ms] = mfma_bf16(load_a(a.zl2 + (size_t)slot_i[ms] * a.rLp, kb + 8 * c, a.rL, av[ms]),
+                                            bv, acc[ms]);
+            }
+        }
+
+        // delta down: one pass per distinct expert among the pass's rows (rows are
+        // expert-sorted), the next expert's operands loaded while this one computes
+        int my_e = -1, prev_e = -1;
+        if (lane < prow) my_e = v.idx[v.rows[m0 + lane]];
+        if (lane >= 1 && lane - 1 < prow) prev_e = v.idx[v.rows[m0 + lane - 1]];
+        uint64_t starts = __ballot(lane < prow && (lane == 0 || my_e != prev_e));
+        if (fast) {
+            auto fetch = [&](int p, uint4& raw, uint32_t& sb, uint4 (&af)[NS][4]) {
+                const int e = __shfl(my_e, p, kWave);
+                raw = ld16(a.b_dn + ((size_t)e * a.d + ncol) * (KC / 2) + 16 * c);
+                sb = a.b_dn_s[(size_t)e * a.d + ncol];
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) af[ms][s] = ld16(a.z2 + (size_t)slot_i[ms] * KC + 32 * c + 8 * s);
+            };
+            uint4 raw, af[NS][4];
+            uint32_t sb;
+            int p = __ffsll((long long)starts) - 1;
+            fetch(p, raw, sb, af);
+            while (starts) {
+                starts &= starts - 1;
+                const int pn = starts ? __ffsll((long long)starts) - 1 : prow;
+                uint4 raw_n = raw, af_n[NS][4];
+                uint32_t sb_n = sb;
+                if (starts) fetch(pn, raw_n, sb_n, af_n);
+                // rows [p, pn) belong to this expert: zero the others' A rows
+                uint4 am[NS][4];
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms) {
+                    const int i = ms * 16 + li;
+                    const bool mine = i >= p && i < pn;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) am[ms][s] = mine ? af[ms][s] : zero_u4();
+                }
+                mac_fast<NS>(acc, am, raw, sb);
+                raw = raw_n;
+                sb = sb_n;
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) af[ms][s] = af_n[ms][s];
+                p = pn;
+            }
+        } else {
+            while (starts) {
+                const int p = __ffsll((long long)starts) - 1;
+                starts &= starts - 1;
+                const int pend = starts ? __ffsll((long long)starts) - 1 : prow;
+                const int e = __shfl(my_e, p, kWave);
+                const uint8_t* w2 = a.b_dn + ((size_t)e * a.d + ncol) * (a.r / 2);
+                const uint16_t* s2 = a.b_dn_s + ((size_t)e * a.d + ncol) * (a.r / gq_r);
+                for (int k0 = 0; k0 < a.r; k0 += KC) {
+                    const int kv = min(KC, a.r - k0);
+                    const uint4 raw2 = load_b_i4(w2, k0 + 32 * c, a.r);
+                    const uint2 sb = load_scales(s2, k0, gq_r, kv, true);
+                    uint4 af2[NS][4];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms) {
+                        const int i = ms * 16 + li;
+                        const bool ok = i >= p && i < pend;
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            af2[ms][s] = ms < nsub ? load_a(a.z2 + (size_t)slot_i[ms] * a.r, k0 + 32 * c + 8 * s, a.r, ok)
+                                                   : zero_u4();
+                    }
+                    mac_i4<NS>(acc, af2, nsub, raw2, sb, gq_r, kv, c);
+                }
+            }
+        }
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ms * 16 + 4 * c + q;
+                if (i < prow) st_agent(&a.o[(size_t)v.rows[m0 + i] * a.d + ncol], acc[ms][q]);
+            }
+    }
+
+    // ---- the last workgroup of this column block forms y = sum_j w_j o_j in slot order
+    if (!arrive_last(v, &a.cnt_c[nb], (uint32_t)(a.npass * a.G))) return;
+    for (int i = threadIdx.x; i < a.T * 64; i += blockDim.x) {
+        const int t = i / 64, col = nb * 64 + (i % 64);
+        float acc = 0.f;
+        for (int j0 = 0; j0 < a.k; j0 += 8) {
+            float wv8[8], ov8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = min(j0 + u, a.k - 1);
+                wv8[u] = a.topk_w[t * a.k + j];
+                ov8[u] = ld_agent(&a.o[(size_t)(t * a.k + j) * a.d + col]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (j0 + u < a.k) acc = fmaf(wv8[u], ov8[u], acc);
+        }
+        a.y[(size_t)t * a.d + col] = acc;
+    }
+}
+
+// ------------------------------------------------------------------ launcher -------
+template <int NS, bool LDSP>
+static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
+    const int nbh = a.h / 64, nbr = (a.r + 63) / 64;
+    const int g1 = a.G * nbh + a.nxmax * a.S1 * nbr + a.G * a.S1;
+    prof_begin(s);
+    dec_up<NS, LDSP><<<g1, 256, 0, s>>>(a);
+    prof_end(s, "dec_up");
+    prof_begin(s);
+    dec_act<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
+    prof_end(s, "dec_act");
+    const int g3 = a.npass * a.G * (a.d / 64);
+    prof_begin(s);
+    if (ns_down == 2) dec_down<2, LDSP><<<g3, 256, 0, s>>>(a);
+    else dec_down<4, LDSP><<<g3, 256, 0, s>>>(a);
+    prof_end(s, "dec_down");
+    return hipGetLastError();
+}
+
+int decode_ns_down(int T) { return T <= 16 ? 2 : 4; }
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+    const int nsd = decode_ns_down(a.T);
+    const int ns = a.T <= 16 ? 1 : (a.T <= 32 ? 2 : 4);
+    // streaming through LDS needs one scale per 128-chunk group and K-blocks
+    // that tile the K ranges of every product
+    const int kb_up = 512 / ns, kb_dn = 512 / nsd;
+    const bool lds = a.gq % KC == 0 && min(a.gq, a.d) % KC == 0 && min(a.gq, a.h) % KC == 0 &&
+                     (a.d / a.S1) % kb_up == 0 && a.h % kb_dn == 0 && a.r == KC && a.rL % 8 == 0;
+    if (ns == 1) return lds ? launch_ns<1, true>(a, s, nsd) : launch_ns<1, false>(a, s, nsd);
+    if (ns == 2) return lds ? launch_ns<2, true>(a, s, nsd) : launch_ns<2, false>(a, s, nsd);
+    return lds ? launch_ns<4, true>(a, s, nsd) : launch_ns<4, false>(a, s, nsd);
+}
+
+}  // namespace em

@@ -18,6 +18,7 @@
 // subtile, one fp16 group scale applied to the chunk's fp32 partial sum.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_ops.h"
 
 namespace em {
 
@@ -25,7 +26,6 @@ enum Mode { M_Z1 = 0, M_HS = 1, M_ACT = 2, M_Z2 = 3, M_OUT = 4 };
 
 constexpr int TASK_ROWS = 64;
 constexpr int NSUB = TASK_ROWS / 16;
-constexpr int KC = 128;
 
 EM_DEV int find_seg(const int32_t* __restrict__ pre, int n, int b) {
     if (b >= pre[n]) return -1;
@@ -35,99 +35,6 @@ EM_DEV int find_seg(const int32_t* __restrict__ pre, int n, int b) {
         if (pre[mid] <= b) lo = mid; else hi = mid;
     }
     return lo;
-}
-
-// int4 weights: 32 elements [kk, kk+32) of one row (kk multiple of 32), as 4 dwords.
-EM_DEV uint4 load_b_i4(const uint8_t* __restrict__ row, int kk, int K) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (kk >= K) return v;
-    if ((K & 31) == 0) return *reinterpret_cast<const uint4*>(row + (kk >> 1));
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(row + (kk >> 1));
-    if (kk + 0 < K) v.x = p[0];
-    if (kk + 8 < K) v.y = p[1];
-    if (kk + 16 < K) v.z = p[2];
-    if (kk + 24 < K) v.w = p[3];
-    return v;
-}
-
-// bf16 weights: elements [kk, kk+8) of one row (K even), zero beyond K.
-EM_DEV uint4 load_b_bf16(const uint16_t* __restrict__ row, int kk, int K) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(row + kk);
-    if (kk + 0 < K) v.x = p[0];
-    if (kk + 2 < K) v.y = p[1];
-    if (kk + 4 < K) v.z = p[2];
-    if (kk + 6 < K) v.w = p[3];
-    return v;
-}
-
-// bf16 activations: elements [kk, kk+8) of a row whose storage is padded to a
-// multiple of 8 elements; elements >= K read as zero.
-EM_DEV uint4 load_a(const uint16_t* __restrict__ row, int kk, int K, bool valid) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (!valid || kk >= K) return v;
-    v = *reinterpret_cast<const uint4*>(row + kk);
-    const int n = K - kk;                     // valid elements, > 0
-    if (n < 8) {
-        uint32_t* u = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (2 * i >= n) u[i] = 0u;
-            else if (2 * i + 1 >= n) u[i] &= 0xFFFFu;
-        }
-    }
-    return v;
-}
-
-EM_DEV void dequant_b(uint4 raw, uint4 b[4]) {
-    uint32_t q[4][4];
-    dequant8(raw.x, q[0]);
-    dequant8(raw.y, q[1]);
-    dequant8(raw.z, q[2]);
-    dequant8(raw.w, q[3]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = make_uint4(q[s][0], q[s][1], q[s][2], q[s][3]);
-}
-
-// One 128-wide int4 chunk: acc[ms] += scale * (A[ms] . W) for each active
-// subtile.  K-slot mapping: lane group c holds chunk elements [32c, 32c+32),
-// MFMA s uses elements [32c + 8s, 32c + 8s + 8).  With quant groups narrower
-// than the chunk (32 or 64) each group gets its own pass in which the A lanes
-// of other groups are zero, so every partial sum carries a single scale.
-EM_DEV void mac_i4(floatx4 acc[NSUB], const uint4 af[NSUB][4], int nsub, uint4 raw,
-                   const uint16_t* __restrict__ srow, bool nvalid, int k0, int gq, int kvalid,
-                   int c) {
-    uint4 b[4];
-    dequant_b(raw, b);
-    if (gq >= kvalid) {
-        const float sc = nvalid ? 16.0f * fp16_bits_to_f32(srow[k0 / gq]) : 0.0f;
-#pragma unroll
-        for (int ms = 0; ms < NSUB; ++ms) {
-            if (ms < nsub) {
-                floatx4 t = zero4();
-#pragma unroll
-                for (int s = 0; s < 4; ++s) t = mfma_bf16(af[ms][s], b[s], t);
-                acc[ms] = sc * t + acc[ms];
-            }
-        }
-    } else {
-        const int ng = kvalid / gq;
-        const int lanes_per = gq / 32;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        for (int gi = 0; gi < ng; ++gi) {
-            const bool mine = (c / lanes_per) == gi;
-            const float sc = nvalid ? 16.0f * fp16_bits_to_f32(srow[k0 / gq + gi]) : 0.0f;
-#pragma unroll
-            for (int ms = 0; ms < NSUB; ++ms) {
-                if (ms < nsub) {
-                    floatx4 t = zero4();
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) t = mfma_bf16(mine ? af[ms][s] : z, b[s], t);
-                    acc[ms] = sc * t + acc[ms];
-                }
-            }
-        }
-    }
 }
 
 struct Task {
@@ -218,7 +125,7 @@ expert_gemm(LayerArgs a) {
     for (int ms = 0; ms < NSUB; ++ms) acc[ms] = zero4();
 
     // ---- main K loop, one chunk of loads in flight ahead of the math
-    uint4 raw = nvalid ? load_b_i4(wrow, 32 * c, K) : make_uint4(0, 0, 0, 0);
+    uint4 raw = nvalid ? load_b_i4(wrow, 32 * c, K) : zero_u4();
     uint4 af[NSUB][4];
 #pragma unroll
     for (int ms = 0; ms < NSUB; ++ms)
@@ -238,7 +145,8 @@ expert_gemm(LayerArgs a) {
                     af_n[ms][s] = (ms < nsub) ? load_a(arow[ms], kn + 32 * c + 8 * s, K, avalid[ms])
                                               : make_uint4(0, 0, 0, 0);
         }
-        mac_i4(acc, af, nsub, raw, srow, nvalid, k0, gq, min(KC, K - k0), c);
+        mac_i4<NSUB>(acc, af, nsub, raw, load_scales(srow, k0, gq, min(KC, K - k0), nvalid), gq,
+                     min(KC, K - k0), c);
         raw = raw_n;
 #pragma unroll
         for (int ms = 0; ms < NSUB; ++ms)
@@ -295,7 +203,8 @@ expert_gemm(LayerArgs a) {
                                                           k0 + 32 * c + 8 * s, a.r, v)
                                                  : make_uint4(0, 0, 0, 0);
                 }
-                mac_i4(acc, af2, nsub, raw2, s2, nvalid, k0, gq_r, min(KC, a.r - k0), c);
+                mac_i4<NSUB>(acc, af2, nsub, raw2, load_scales(s2, k0, gq_r, min(KC, a.r - k0), nvalid),
+                             gq_r, min(KC, a.r - k0), c);
             }
         }
     }
@@ -454,6 +363,26 @@ hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint
     prof_begin(s);
     residual_add<<<(int)((n + 255) / 256), 256, 0, s>>>(x, y, x_out, n);
     prof_end(s, "residual_add");
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ trace copies ---
+// dst[s] = src[index[s]] for rows of `width` 16-bit units (a row copy by index).
+__global__ void __launch_bounds__(256)
+gather_rows_u16(const uint16_t* __restrict__ src, const int32_t* __restrict__ index,
+                uint16_t* __restrict__ dst, int64_t rows, int64_t width) {
+    const int64_t i = blockIdx.x * 256ll + threadIdx.x;
+    if (i >= rows * width) return;
+    const int64_t r = i / width, c = i % width;
+    dst[i] = src[(int64_t)index[r] * width + c];
+}
+
+hipError_t launch_gather_rows(const void* src, const int32_t* index, void* dst, int64_t rows,
+                              int64_t row_bytes, hipStream_t s) {
+    const int64_t width = row_bytes / 2;
+    const int64_t n = rows * width;
+    gather_rows_u16<<<(int)((n + 255) / 256), 256, 0, s>>>((const uint16_t*)src, index,
+                                                           (uint16_t*)dst, rows, width);
     return hipGetLastError();
 }
 

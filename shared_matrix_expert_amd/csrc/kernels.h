@@ -56,6 +56,40 @@ struct LayerArgs {
     int max_etiles, max_gtiles_u, max_gtiles_r;   // grid bounds
 };
 
+// Small-batch expert layer (T <= 64, T*k <= 1024): three launches, every
+// workgroup rebuilding its view of the routing from topk_idx in LDS.
+struct DecodeArgs {
+    int T, d, h, E, P, G, k, r, rL, rLp, gq, R;
+    int S1;      // K slices of the R1 / R2 products (d / S1 is a multiple of 128)
+    int cb2;     // columns per workgroup of the activation kernel (128, 256 or 512)
+    int ncb2;    // h / cb2
+    int npass;   // row passes of the down kernel
+    int nxmax;   // upper bound on distinct experts: min(E, R)
+    const uint16_t* x; const int32_t* idx; const float* topk_w;
+    const uint8_t* s_up; const uint16_t* s_up_s;
+    const uint8_t* s_dn; const uint16_t* s_dn_s;
+    const uint8_t* a_up; const uint16_t* a_up_s;
+    const uint8_t* b_up; const uint16_t* b_up_s;
+    const uint8_t* a_dn; const uint16_t* a_dn_s;
+    const uint8_t* b_dn; const uint16_t* b_dn_s;
+    const uint16_t* lu_u; const uint16_t* lu_v;
+    const uint16_t* ld_u; const uint16_t* ld_v;
+    float* hs;          // [T][G][h]      shared up, per (token, group)
+    float* z1p;         // [S1][R][r]     partial sums of A_up x
+    float* zlp;         // [4 S1][T][G][rLp] partial sums of U_up x
+    uint16_t* act;      // [R][h]         bf16 activation per slot
+    float* z2p;         // [ncb2][R][r + rL] partial sums of A_dn a, U_dn a
+    uint16_t* z2;       // [R][r]
+    uint16_t* zl2;      // [R][rLp]
+    float* o;           // [R][d]         expert output per slot
+    float* y;           // [T][d]
+    uint32_t* cnt_e;    // [E]     arrivals per expert (activation kernel)
+    uint32_t* cnt_c;    // [d/64]  arrivals per output column block (down kernel)
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+int decode_ns_down(int T);   // rows per down-kernel pass = 16 * decode_ns_down(T)
+
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias,
                          float* logits, int32_t* idx, float* w, int T, int d, int E, int k,
                          hipStream_t stream);
@@ -64,6 +98,9 @@ hipError_t launch_dispatch(const int32_t* idx, const DispatchBufs& db, int T, in
                            int P, int mt, hipStream_t stream);
 
 hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t stream);
+
+hipError_t launch_gather_rows(const void* src, const int32_t* index, void* dst, int64_t rows,
+                              int64_t row_bytes, hipStream_t stream);
 
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
                            hipStream_t stream);

@@ -14,59 +14,82 @@
 namespace em {
 
 // -------------------------------------------------------------- small batches ----
-// One wave per expert; every lane owns 8-element slices of the K axis, so the
-// expert's weight row streams once through the wave (16 bytes per lane per
-// step) and is applied to all T <= 16 tokens.  The T partial sums are reduced
-// with a fixed butterfly, so results are reproducible.
-template <int TMAX>
+// A workgroup of 4 waves takes 4 experts and up to 4 tokens: the tokens' rows
+// are staged once in LDS, each wave streams one expert's weight row (all of a
+// 4096-element block's loads issued before the arithmetic) and accumulates the
+// exact bf16 products in float64.  The 4 partial sums per lane are reduced
+// with a fixed butterfly, so the result is reproducible (and exact).
+constexpr int RS_TOK = 4;
+constexpr int RS_BLK = 4096;
+
 __global__ void __launch_bounds__(256)
 router_logits_small(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                     const float* __restrict__ bias, float* __restrict__ logits,
                     int T, int d, int E) {
-    const int lane = lane_id();
-    const int e = blockIdx.x * 4 + wave_id();
-    if (e >= E) return;
-    double acc[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) acc[t] = 0.0;
-    const uint16_t* wrow = wr + (size_t)e * d;
-    for (int k0 = lane * 8; k0 < d; k0 += kWave * 8) {
-        uint4 wv = *reinterpret_cast<const uint4*>(wrow + k0);
-        double wd[8];
-        const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wd[2 * i] = (double)bf16_to_f32(wu[i] & 0xFFFFu);
-            wd[2 * i + 1] = (double)bf16_to_f32(wu[i] >> 16);
+    __shared__ __attribute__((aligned(16))) uint16_t xs[RS_TOK][RS_BLK];
+    const int lane = lane_id(), wv = wave_id();
+    const int ntg = (T + RS_TOK - 1) / RS_TOK;
+    const int tg = blockIdx.x % ntg;
+    const int e = (blockIdx.x / ntg) * 4 + wv;
+    const int t0 = tg * RS_TOK;
+    const int nt = min(RS_TOK, T - t0);
+    double acc[RS_TOK] = {0.0, 0.0, 0.0, 0.0};
+    const uint16_t* wrow = wr + (size_t)(e < E ? e : 0) * d;
+    for (int kb = 0; kb < d; kb += RS_BLK) {
+        const int kn = min(RS_BLK, d - kb);
+        __syncthreads();
+        for (int i = threadIdx.x * 8; i < RS_TOK * kn; i += 256 * 8) {
+            const int t = i / kn, kk = i % kn;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (t < nt) v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * d + kb + kk);
+            *reinterpret_cast<uint4*>(&xs[t][kk]) = v;
         }
+        uint4 wv8[8];
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < T) {
-                uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)t * d + k0);
+        for (int i = 0; i < 8; ++i) {
+            const int kk = (i * kWave + lane) * 8;
+            wv8[i] = (e < E && kk < kn) ? *reinterpret_cast<const uint4*>(wrow + kb + kk)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = (i * kWave + lane) * 8;
+            if (kk >= kn) break;
+            const uint32_t wu[4] = {wv8[i].x, wv8[i].y, wv8[i].z, wv8[i].w};
+            double wd[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wd[2 * q] = (double)bf16_to_f32(wu[q] & 0xFFFFu);
+                wd[2 * q + 1] = (double)bf16_to_f32(wu[q] >> 16);
+            }
+#pragma unroll
+            for (int t = 0; t < RS_TOK; ++t) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(&xs[t][kk]);
                 const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[t] = fma((double)bf16_to_f32(xu[i] & 0xFFFFu), wd[2 * i], acc[t]);
-                    acc[t] = fma((double)bf16_to_f32(xu[i] >> 16), wd[2 * i + 1], acc[t]);
+                for (int q = 0; q < 4; ++q) {
+                    acc[t] = fma((double)bf16_to_f32(xu[q] & 0xFFFFu), wd[2 * q], acc[t]);
+                    acc[t] = fma((double)bf16_to_f32(xu[q] >> 16), wd[2 * q + 1], acc[t]);
                 }
             }
         }
     }
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
+    for (int t = 0; t < RS_TOK; ++t) {
         double v = acc[t];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
         acc[t] = v;
     }
-    if (lane < T) {
-        double v = 0.0;
+    if (e < E && lane < nt) {
+        double v = acc[0];
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t)
+        for (int t = 1; t < RS_TOK; ++t)
             if (t == lane) v = acc[t];
         float l = (float)v;
         if (bias) l = l + bias[e];
-        logits[(size_t)lane * E + e] = l;
+        logits[(size_t)(t0 + lane) * E + e] = l;
     }
 }
 
@@ -147,8 +170,12 @@ router_logits_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 }
 
 // -------------------------------------------------------------- top-k -----------
-// One wave per token: k rounds of a wave-wide arg-max (larger logit, or equal
-// logit and lower index), then the softmax over the selected logits in float64.
+// One wave per token.  Each lane keeps the best of its own logits; a round is a
+// wave-wide arg-max of those (larger logit, or equal logit and lower index),
+// after which only the winning lane rescans.  Then the softmax over the
+// selected logits in float64.
+EM_DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
 __global__ void __launch_bounds__(256)
 router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
             float* __restrict__ topk_w, int T, int E, int k) {
@@ -163,35 +190,41 @@ router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
         const int e = lane + kWave * i;
         v[i] = (e < E) ? row[e] : -INFINITY;
     }
-    uint64_t taken = 0;                   // bit i: element lane + 64 i already selected
-    float sel0 = 0.f, my_sel = 0.f;
-    int my_idx = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
+    uint32_t taken = 0;                   // bit i: element lane + 64 i already selected
+    auto local_best = [&](float& bv, int& bi) {
+        bv = -INFINITY;
+        bi = 0x7FFFFFFF;
 #pragma unroll
         for (int i = 0; i < MAXPER; ++i) {
             const int e = lane + kWave * i;
-            if (e < E && !((taken >> i) & 1ull)) {
-                if (v[i] > bv || (v[i] == bv && e < bi)) { bv = v[i]; bi = e; }
-            }
+            if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
         }
+    };
+    float lv;
+    int lidx;
+    local_best(lv, lidx);
+    float sel0 = 0.f, my_sel = 0.f;
+    int my_idx = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = lv;
+        int bi = lidx;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             const float ov = __shfl_xor(bv, off, kWave);
             const int oi = __shfl_xor(bi, off, kWave);
-            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
         }
-        if ((bi & (kWave - 1)) == lane) taken |= 1ull << (bi / kWave);
         if (j == 0) sel0 = bv;
         if (lane == j) { my_sel = bv; my_idx = bi; }
+        if ((bi & (kWave - 1)) == lane) {
+            taken |= 1u << (bi / kWave);
+            local_best(lv, lidx);
+        }
     }
     double u = (lane < k) ? exp((double)my_sel - (double)sel0) : 0.0;
     double s = u;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
-    // the butterfly gives every lane the same sum only up to rounding order;
-    // take lane 0's value so that all weights share one denominator
     s = __shfl(s, 0, kWave);
     if (lane < k) {
         topk_idx[(size_t)t * k + lane] = my_idx;
@@ -203,13 +236,10 @@ router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias,
                          float* logits, int32_t* idx, float* w, int T, int d, int E, int k,
                          hipStream_t stream) {
-    if (T <= 4) {
+    if (T <= 16) {
+        const int ntg = (T + RS_TOK - 1) / RS_TOK;
         prof_begin(stream);
-        router_logits_small<4><<<(E + 3) / 4, 256, 0, stream>>>(x, wr, bias, logits, T, d, E);
-        prof_end(stream, "router_logits_small");
-    } else if (T <= 16) {
-        prof_begin(stream);
-        router_logits_small<16><<<(E + 3) / 4, 256, 0, stream>>>(x, wr, bias, logits, T, d, E);
+        router_logits_small<<<((E + 3) / 4) * ntg, 256, 0, stream>>>(x, wr, bias, logits, T, d, E);
         prof_end(stream, "router_logits_small");
     } else {
         dim3 grid((T + RT_TILE - 1) / RT_TILE, (E + RT_TILE - 1) / RT_TILE);

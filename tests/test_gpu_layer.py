@@ -99,16 +99,22 @@ def test_verify_skewed_layer(seed):
     assert np.array_equal(tr["expert_offsets"].cpu().numpy(), offs)
     assert np.array_equal(tr["row_token"].cpu().numpy(), rt)
     assert np.array_equal(tr["row_slot"].cpu().numpy(), rs)
-    # activations: a bf16 value differs from the oracle's only where the fp32
-    # pre-activation landed on the other side of a rounding midpoint, i.e. by one
-    # bf16 step of a (2^-8 relative) plus the pre-activation's own fp32 error;
-    # such flips are rare
-    act = tr["act"].cpu().numpy().view(np.uint16)
+    # activations: a bf16 value differs from the oracle's where the fp32 pre-activation
+    # landed on the other side of a rounding midpoint (one bf16 step, 2^-7 |a|) or
+    # where a low-rank input (R1 / R2) rounded the other way, which shifts that
+    # row's pre-activations by at most |B_up| * one bf16 step of z (~2e-3); both
+    # are rare
+    act = tr["act"].cpu().numpy().view(np.uint16)               # slot order
     a_gpu = (act.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    ref_a = fw["a"][rt, rs]
+    ref_a = fw["a"].reshape(-1, D.h)
     dev = np.abs(a_gpu - ref_a)
-    assert np.all(dev <= 2.0 ** -7 * np.abs(ref_a) + 1e-4), float(np.max(dev))
-    assert np.mean(a_gpu != ref_a) < 1e-3, float(np.mean(a_gpu != ref_a))
+    assert np.all(dev <= 2.0 ** -7 * np.abs(ref_a) + 4e-3), float(np.max(dev))
+    assert np.mean(a_gpu != ref_a) < 5e-3, float(np.mean(a_gpu != ref_a))
+    # expert outputs per slot: a sanity bound (the gate is on y, where the k slots
+    # are averaged); a low-rank input rounded the other way moves a slot's o by ~1e-3
+    o_gpu = tr["expert_out"].cpu().numpy().astype(np.float64)
+    o_ref = fw["o"].reshape(-1, D.d)
+    assert np.all(np.abs(o_gpu - o_ref) <= 1e-2 + 1e-2 * np.abs(o_ref)), float(np.max(np.abs(o_gpu - o_ref)))
     # determinism
     y2, _ = lay.forward(bits_to_dev(x), idx, w)
     assert torch.equal(y, y2)
