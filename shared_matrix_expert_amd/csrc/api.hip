@@ -104,14 +104,16 @@ bool use_decode(const edge_moe_dims& d) {
 struct DecLayout {
     size_t hs, z1p, zlp, act, z2p, z2, zl2, o, cnt_e, cnt_c, bytes;
     int S1, cb2, ncb2, N2;
+    bool lds;
 };
 
 DecLayout make_dec_layout(const edge_moe_dims& d) {
     DecLayout L{};
     const int64_t T = d.T, R = (int64_t)d.T * d.top_k, G = d.n_experts / d.experts_per_group;
     const int rLp = (d.lora_rank + 7) & ~7;
-    L.S1 = d.d % 512 == 0 ? d.d / 512 : d.d / 128;
-    L.cb2 = d.h % 512 == 0 ? 512 : (d.h % 256 == 0 ? 256 : 128);
+    L.S1 = d.d % 256 == 0 ? 2 : 1;            // K slices of the R1 / R2 products
+    L.lds = em::decode_lds_ok(d.T, d.d, d.h, d.delta_rank, d.lora_rank, d.quant_group, L.S1);
+    L.cb2 = L.lds ? 256 : (d.h % 512 == 0 ? 512 : (d.h % 256 == 0 ? 256 : 128));
     L.ncb2 = d.h / L.cb2;
     L.N2 = ((d.delta_rank + 15) & ~15) + ((d.lora_rank + 15) & ~15);
     size_t off = 0;
@@ -281,7 +283,7 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.T = d.T; a.d = d.d; a.h = d.h; a.E = d.n_experts; a.P = d.experts_per_group;
     a.G = d.n_experts / d.experts_per_group; a.k = d.top_k; a.r = d.delta_rank; a.rL = d.lora_rank;
     a.rLp = (d.lora_rank + 7) & ~7; a.gq = d.quant_group; a.R = d.T * d.top_k;
-    a.S1 = L.S1; a.cb2 = L.cb2; a.ncb2 = L.ncb2;
+    a.S1 = L.S1; a.cb2 = L.cb2; a.ncb2 = L.ncb2; a.lds = L.lds ? 1 : 0;
     const int rows_per_pass = 16 * em::decode_ns_down(d.T);
     a.npass = (a.R + rows_per_pass - 1) / rows_per_pass;
     a.nxmax = a.R < a.E ? a.R : a.E;

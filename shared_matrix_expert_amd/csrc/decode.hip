@@ -204,7 +204,7 @@ dec_up(DecodeArgs a) {
     constexpr int LKB = LDSP ? KB : 128;
     __shared__ RouteView v;
     __shared__ StreamLds<LNS, LKB> L;
-    __shared__ const uint16_t* arow_l[16 * NS];
+    __shared__ int arow_l[16 * NS];
     if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < a.E; i += blockDim.x) a.cnt_e[i] = 0u;
         for (int i = threadIdx.x; i < a.d / 64; i += blockDim.x) a.cnt_c[i] = 0u;
@@ -233,11 +233,11 @@ dec_up(DecodeArgs a) {
         for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
         if constexpr (lds) {
             if ((int)threadIdx.x < 16 * NS)
-                arow_l[threadIdx.x] = a.x + (size_t)v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0] * a.d;
+                arow_l[threadIdx.x] = v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0];
             __syncthreads();
             const size_t r0 = (size_t)g * a.h + nb * 64;
             const StreamArgs sa{a.s_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.s_up_s + r0 * (a.d / gq),
-                                (size_t)(a.d / gq), 64, gq};
+                                (size_t)(a.d / gq), 64, gq, a.x, (size_t)a.d};
             stream_gemm<NS, KB>(acc, L, sa, arow_l, nrows, 0, a.d);
         } else {
             const uint8_t* wrow = a.s_up + ((size_t)g * a.h + ncol) * (a.d / 2);
@@ -280,11 +280,11 @@ dec_up(DecodeArgs a) {
         for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
         if constexpr (lds) {
             if ((int)threadIdx.x < 16 * NS)
-                arow_l[threadIdx.x] = a.x + (size_t)v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0] * a.d;
+                arow_l[threadIdx.x] = v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0];
             __syncthreads();
             const size_t r0 = (size_t)e * a.r + nb * 64;
             const StreamArgs sa{a.a_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.a_up_s + r0 * (a.d / gq),
-                                (size_t)(a.d / gq), min(64, a.r - nb * 64), gq};
+                                (size_t)(a.d / gq), min(64, a.r - nb * 64), gq, a.x, (size_t)a.d};
             stream_gemm<NS, KB>(acc, L, sa, arow_l, nrows, s * ks, (s + 1) * ks);
         } else {
             if (n0 >= a.r) return;
@@ -319,7 +319,7 @@ dec_up(DecodeArgs a) {
         const int nrows = rv_group_tokens(v, g, a.T, a.k, a.P);
         if (nrows == 0) return;
         const int kb = s * ks + wv * (ks / 4);
-        const int nstep = ks / 4 / 32;                 // 1 or 4
+        const int nstep = ks / 4 / 32;                 // steps of 32 elements for this wave
         const uint16_t* arow[NS];
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms) {
@@ -330,22 +330,24 @@ dec_up(DecodeArgs a) {
             const int n = nt * 16 + li;
             const bool nvalid = n < a.rL;
             const uint16_t* urow = a.lu_u + ((size_t)g * a.rL + (nvalid ? n : 0)) * a.d;
-            uint4 bv[4], av4[4][NS];
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int kk = kb + min(st, nstep - 1) * 32 + 8 * c;
-                bv[st] = ld16(urow + kk);
-#pragma unroll
-                for (int ms = 0; ms < NS; ++ms) av4[st][ms] = ld16(arow[ms] + kk);
-            }
             floatx4 acc[NS];
 #pragma unroll
             for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+            for (int st0 = 0; st0 < nstep; st0 += 4) {
+                uint4 bv[4], av4[4][NS];
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-                if (st < nstep)
+                for (int st = 0; st < 4; ++st) {
+                    const int kk = kb + min(st0 + st, nstep - 1) * 32 + 8 * c;
+                    bv[st] = ld16(urow + kk);
 #pragma unroll
-                    for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(av4[st][ms], bv[st], acc[ms]);
+                    for (int ms = 0; ms < NS; ++ms) av4[st][ms] = ld16(arow[ms] + kk);
+                }
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    if (st0 + st < nstep)
+#pragma unroll
+                        for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(av4[st][ms], bv[st], acc[ms]);
+            }
             if (!nvalid) continue;
 #pragma unroll
             for (int ms = 0; ms < NS; ++ms)
@@ -599,6 +601,185 @@ dec_act(DecodeArgs a) {
     }
 }
 
+// Activation kernel with every weight block staged through LDS (r = 128,
+// quant groups of 128, 256 columns per workgroup): the expert's B_up rows of
+// these columns (256 x 64 B, contiguous), its A_dn columns (128 rows x 128 B)
+// and the group's U_dn columns are loaded coalesced and up front.
+constexpr int CB_L = 256;
+
+template <int NS>
+__global__ void __launch_bounds__(256)
+dec_act_lds(DecodeArgs a) {
+    __shared__ RouteView v;
+    __shared__ __attribute__((aligned(16))) uint16_t zs[16 * NS][KC + 8];
+    __shared__ __attribute__((aligned(16))) uint16_t zls[16 * NS][ZL_W];
+    __shared__ __attribute__((aligned(16))) uint16_t as_[16 * NS][CB_L + 8];
+    __shared__ uint4 wb[CB_L * 5];          // B_up block [256][5] or A_dn block [128][9]
+    __shared__ uint4 ub[32 * 33];            // U_dn block [rL][33]
+    __shared__ uint16_t bsc[CB_L];
+    __shared__ uint16_t asc[KC][2];
+    rv_load(v, a.idx, a.R);
+    const int xi = blockIdx.x / a.ncb2, cb = blockIdx.x % a.ncb2;
+    const int e = rv_distinct_expert(v, a.R, a.E, xi);
+    if (e < 0) return;
+    const int nrows = rv_expert_rows(v, e, a.T, a.k);
+    const int g = e / a.P;
+    const int tid = threadIdx.x;
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    const int gq_h = min(a.gq, a.h);
+
+    // ---- issue every global load of the block first
+    uint4 rb[4], ra[4], ru[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = tid + 256 * i;
+        rb[i] = ld16(a.b_up + ((size_t)e * a.h + cb * CB_L) * (KC / 2) + 16 * q);
+        const int row = q >> 3, seg = q & 7;
+        ra[i] = ld16(a.a_dn + ((size_t)e * KC + row) * (a.h / 2) + cb * (CB_L / 2) + 16 * seg);
+        const int urow = q >> 5, useg = q & 31;
+        ru[i] = ld16(a.ld_u + ((size_t)g * a.rL + min(urow, a.rL - 1)) * a.h + cb * CB_L + 8 * useg);
+    }
+    const uint16_t bs = a.b_up_s[(size_t)e * a.h + cb * CB_L + tid];
+    const uint16_t as2 = a.a_dn_s[((size_t)e * KC + (tid >> 1)) * (a.h / gq_h) + (cb * CB_L + KC * (tid & 1)) / gq_h];
+    const int col0 = cb * CB_L + wv * 64;
+    uint4 vb[4];
+    float hv[4][NS][4];
+    int tq[NS][4];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = ms * 16 + 4 * c + q;
+            tq[ms][q] = v.rtok[i < nrows ? i : 0];
+        }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int ncol = col0 + nt * 16 + li;
+        const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
+        vb[nt] = 8 * c < a.rL ? t : zero_u4();
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
+    }
+
+    // ---- R1, R2: finish the split-K sums in slice order and round to bf16
+    for (int i = tid; i < 16 * NS * (KC + 8); i += 256) {
+        const int row = i / (KC + 8), col = i % (KC + 8);
+        if (row >= nrows || col >= KC) zs[row][col] = 0;
+    }
+    for (int i = tid; i < 16 * NS * ZL_W; i += 256) {
+        const int row = i / ZL_W, col = i % ZL_W;
+        if (row >= nrows || col >= a.rL) zls[row][col] = 0;
+    }
+    for (int i = tid; i < nrows * KC; i += 256) {
+        const int row = i / KC, col = i % KC;
+        zs[row][col] = (uint16_t)f32_to_bf16_rne(
+            ordered_sum(a.z1p + (size_t)v.rows[row] * KC + col, a.S1, (size_t)a.R * KC));
+    }
+    for (int i = tid; i < nrows * a.rL; i += 256) {
+        const int row = i / a.rL, col = i % a.rL;
+        zls[row][col] = (uint16_t)f32_to_bf16_rne(ordered_sum(
+            a.zlp + ((size_t)v.rtok[row] * a.G + g) * a.rLp + col, 4 * a.S1, (size_t)a.T * a.G * a.rLp));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = tid + 256 * i;
+        wb[(q >> 2) * 5 + (q & 3)] = rb[i];
+    }
+    bsc[tid] = bs;
+    __syncthreads();
+
+    // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h))
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int lrow = wv * 64 + nt * 16 + li;
+        const int ncol = cb * CB_L + lrow;
+        floatx4 acc[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+        uint4 af[NS][4];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
+        mac_fast<NS>(acc, af, wb[lrow * 5 + c], bsc[lrow]);
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+            acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt], acc[ms]);
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ms * 16 + 4 * c + q;
+                uint16_t ab = 0;
+                if (i < nrows) {
+                    ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
+                    a.act[(size_t)v.rows[i] * a.h + ncol] = ab;
+                }
+                as_[i][lrow] = ab;
+            }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = tid + 256 * i;
+        wb[(q >> 3) * 9 + (q & 7)] = ra[i];
+        if ((q >> 5) < a.rL) ub[(q >> 5) * 33 + (q & 31)] = ru[i];
+    }
+    asc[tid >> 1][tid & 1] = as2;
+    __syncthreads();
+
+    // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows
+    const int N2 = KC + ((a.rL + 15) & ~15);
+    for (int nt2 = wv; nt2 < N2 / 16; nt2 += 4) {
+        const int n2 = nt2 * 16 + li;
+        floatx4 acc[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+        if (nt2 * 16 < KC) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint4 af[NS][4];
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
+                mac_fast<NS>(acc, af, wb[n2 * 9 + u * 4 + c], asc[n2][u]);
+            }
+        } else {
+            const int cl = n2 - KC;
+            const bool nvalid = cl < a.rL;
+#pragma unroll
+            for (int st = 0; st < CB_L / 32; ++st) {
+                const uint4 bv = nvalid ? ub[cl * 33 + st * 4 + c] : zero_u4();
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+                    acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]), bv, acc[ms]);
+            }
+        }
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ms * 16 + 4 * c + q;
+                if (i < nrows) st_agent(&a.z2p[((size_t)cb * a.R + v.rows[i]) * N2 + n2], acc[ms][q]);
+            }
+    }
+
+    // ---- the last column block of expert e adds the partials in block order
+    if (!arrive_last(v, &a.cnt_e[e], (uint32_t)a.ncb2)) return;
+    for (int i = tid; i < nrows * N2; i += 256) {
+        const int row = i / N2, n2 = i % N2;
+        const int slot = v.rows[row];
+        const float sum = ordered_sum_agent(a.z2p + (size_t)slot * N2 + n2, a.ncb2, (size_t)a.R * N2);
+        const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum);
+        if (n2 < KC) a.z2[(size_t)slot * KC + n2] = bits;
+        else if (n2 - KC < a.rL) a.zl2[(size_t)slot * a.rLp + (n2 - KC)] = bits;
+    }
+}
+
 // ------------------------------------------------------------------ kernel 3 -------
 template <int NS, bool LDSP>
 __global__ void __launch_bounds__(256)
@@ -608,7 +789,7 @@ dec_down(DecodeArgs a) {
     constexpr int LKB = LDSP ? KB : 128;
     __shared__ RouteView v;
     __shared__ StreamLds<LNS, LKB> L;
-    __shared__ const uint16_t* arow_l[16 * NS];
+    __shared__ int arow_l[16 * NS];
     rv_load(v, a.idx, a.R);
     const int nbd = a.d / 64;
     const int pass = blockIdx.x / (a.G * nbd);
@@ -654,11 +835,11 @@ dec_down(DecodeArgs a) {
         const uint16_t* srow = a.s_dn_s + ((size_t)g * a.d + ncol) * (a.h / gq);
         if constexpr (LDSP) {
             if ((int)threadIdx.x < 16 * NS)
-                arow_l[threadIdx.x] = a.act + (size_t)v.rows[m0 + ((int)threadIdx.x < prow ? threadIdx.x : 0)] * a.h;
+                arow_l[threadIdx.x] = v.rows[m0 + ((int)threadIdx.x < prow ? threadIdx.x : 0)];
             __syncthreads();
             const size_t r0 = (size_t)g * a.d + nb * 64;
             const StreamArgs sa{a.s_dn + r0 * (a.h / 2), (size_t)(a.h / 2), a.s_dn_s + r0 * (a.h / gq),
-                                (size_t)(a.h / gq), 64, gq};
+                                (size_t)(a.h / gq), 64, gq, a.act, (size_t)a.h};
             stream_gemm<NS, KB>(acc, L, sa, arow_l, prow, 0, a.h);
 #pragma unroll
             for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(lz[ms], lv, acc[ms]);
@@ -685,42 +866,53 @@ dec_down(DecodeArgs a) {
         if (lane >= 1 && lane - 1 < prow) prev_e = v.idx[v.rows[m0 + lane - 1]];
         uint64_t starts = __ballot(lane < prow && (lane == 0 || my_e != prev_e));
         if (fast) {
-            auto fetch = [&](int p, uint4& raw, uint32_t& sb, uint4 (&af)[NS][4]) {
+            // the A rows (R4 outputs of this pass) are the same for every expert;
+            // only the row mask changes.  Each expert needs one 16-byte weight
+            // load and one scale, kept DEPTH experts ahead in a ring.
+            uint4 af[NS][4];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) af[ms][s] = ld16(a.z2 + (size_t)slot_i[ms] * KC + 32 * c + 8 * s);
+            uint64_t to_fetch = starts, to_do = starts;
+            uint4 ring[DEPTH];
+            uint32_t sring[DEPTH];
+#pragma unroll
+            for (int u = 0; u < DEPTH; ++u) {
+                const int p = to_fetch ? __ffsll((long long)to_fetch) - 1 : 0;
+                to_fetch &= to_fetch - 1;
                 const int e = __shfl(my_e, p, kWave);
-                raw = ld16(a.b_dn + ((size_t)e * a.d + ncol) * (KC / 2) + 16 * c);
-                sb = a.b_dn_s[(size_t)e * a.d + ncol];
+                const int ee = e < 0 ? 0 : e;
+                ring[u] = ld16(a.b_dn + ((size_t)ee * a.d + ncol) * (KC / 2) + 16 * c);
+                sring[u] = a.b_dn_s[(size_t)ee * a.d + ncol];
+            }
+            while (to_do) {
 #pragma unroll
-                for (int ms = 0; ms < NS; ++ms)
+                for (int u = 0; u < DEPTH; ++u) {
+                    if (!to_do) break;
+                    const int p = __ffsll((long long)to_do) - 1;
+                    to_do &= to_do - 1;
+                    const int pn = to_do ? __ffsll((long long)to_do) - 1 : prow;
+                    const uint4 cur = ring[u];
+                    const uint32_t scur = sring[u];
+                    if (to_fetch) {
+                        const int pf = __ffsll((long long)to_fetch) - 1;
+                        to_fetch &= to_fetch - 1;
+                        const int e = __shfl(my_e, pf, kWave);
+                        ring[u] = ld16(a.b_dn + ((size_t)e * a.d + ncol) * (KC / 2) + 16 * c);
+                        sring[u] = a.b_dn_s[(size_t)e * a.d + ncol];
+                    }
+                    // rows [p, pn) belong to this expert: zero the others' A rows
+                    uint4 am[NS][4];
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) af[ms][s] = ld16(a.z2 + (size_t)slot_i[ms] * KC + 32 * c + 8 * s);
-            };
-            uint4 raw, af[NS][4];
-            uint32_t sb;
-            int p = __ffsll((long long)starts) - 1;
-            fetch(p, raw, sb, af);
-            while (starts) {
-                starts &= starts - 1;
-                const int pn = starts ? __ffsll((long long)starts) - 1 : prow;
-                uint4 raw_n = raw, af_n[NS][4];
-                uint32_t sb_n = sb;
-                if (starts) fetch(pn, raw_n, sb_n, af_n);
-                // rows [p, pn) belong to this expert: zero the others' A rows
-                uint4 am[NS][4];
+                    for (int ms = 0; ms < NS; ++ms) {
+                        const int i = ms * 16 + li;
+                        const bool mine = i >= p && i < pn;
 #pragma unroll
-                for (int ms = 0; ms < NS; ++ms) {
-                    const int i = ms * 16 + li;
-                    const bool mine = i >= p && i < pn;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) am[ms][s] = mine ? af[ms][s] : zero_u4();
+                        for (int s = 0; s < 4; ++s) am[ms][s] = mine ? af[ms][s] : zero_u4();
+                    }
+                    mac_fast<NS>(acc, am, cur, scur);
                 }
-                mac_fast<NS>(acc, am, raw, sb);
-                raw = raw_n;
-                sb = sb_n;
-#pragma unroll
-                for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) af[ms][s] = af_n[ms][s];
-                p = pn;
             }
         } else {
             while (starts) {
@@ -787,7 +979,8 @@ static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
     dec_up<NS, LDSP><<<g1, 256, 0, s>>>(a);
     prof_end(s, "dec_up");
     prof_begin(s);
-    dec_act<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
+    if (LDSP) dec_act_lds<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
+    else dec_act<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
     prof_end(s, "dec_act");
     const int g3 = a.npass * a.G * (a.d / 64);
     prof_begin(s);
@@ -802,14 +995,18 @@ int decode_ns_down(int T) { return T <= 16 ? 2 : 4; }
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     const int nsd = decode_ns_down(a.T);
     const int ns = a.T <= 16 ? 1 : (a.T <= 32 ? 2 : 4);
-    // streaming through LDS needs one scale per 128-chunk group and K-blocks
-    // that tile the K ranges of every product
-    const int kb_up = 512 / ns, kb_dn = 512 / nsd;
-    const bool lds = a.gq % KC == 0 && min(a.gq, a.d) % KC == 0 && min(a.gq, a.h) % KC == 0 &&
-                     (a.d / a.S1) % kb_up == 0 && a.h % kb_dn == 0 && a.r == KC && a.rL % 8 == 0;
-    if (ns == 1) return lds ? launch_ns<1, true>(a, s, nsd) : launch_ns<1, false>(a, s, nsd);
-    if (ns == 2) return lds ? launch_ns<2, true>(a, s, nsd) : launch_ns<2, false>(a, s, nsd);
-    return lds ? launch_ns<4, true>(a, s, nsd) : launch_ns<4, false>(a, s, nsd);
+    if (ns == 1) return a.lds ? launch_ns<1, true>(a, s, nsd) : launch_ns<1, false>(a, s, nsd);
+    if (ns == 2) return a.lds ? launch_ns<2, true>(a, s, nsd) : launch_ns<2, false>(a, s, nsd);
+    return a.lds ? launch_ns<4, true>(a, s, nsd) : launch_ns<4, false>(a, s, nsd);
+}
+
+// Whether the LDS-streaming kernels apply: quant groups of whole 128-chunks,
+// r = 128, whole 16-byte LoRA rows and K ranges that the K-blocks tile.
+bool decode_lds_ok(int T, int d, int h, int r, int rL, int gq, int S1) {
+    const int ns = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+    const int nsd = decode_ns_down(T);
+    return gq % KC == 0 && r == KC && rL % 8 == 0 && rL <= 32 && h % CB_L == 0 &&
+           (d / S1) % (512 / ns) == 0 && h % (512 / nsd) == 0;
 }
 
 }  // namespace em

@@ -65,6 +65,7 @@ struct DecodeArgs {
     int ncb2;    // h / cb2
     int npass;   // row passes of the down kernel
     int nxmax;   // upper bound on distinct experts: min(E, R)
+    int lds;     // LDS-streaming kernels (see decode_lds_ok)
     const uint16_t* x; const int32_t* idx; const float* topk_w;
     const uint8_t* s_up; const uint16_t* s_up_s;
     const uint8_t* s_dn; const uint16_t* s_dn_s;
@@ -89,6 +90,7 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 int decode_ns_down(int T);   // rows per down-kernel pass = 16 * decode_ns_down(T)
+bool decode_lds_ok(int T, int d, int h, int r, int rL, int gq, int S1);
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias,
                          float* logits, int32_t* idx, float* w, int T, int d, int E, int k,

@@ -28,7 +28,9 @@ struct StreamLds {
 };
 
 // Operands of one streamed product: 64 weight rows (rows past nw are not
-// loaded and their results must not be stored) and up to 16*NS activation rows.
+// loaded and their results must not be stored) and up to 16*NS activation rows
+// a + arow[i] * a_stride (bf16).  The activation base is a plain global
+// pointer and the row list holds indexes, so every load is a global load.
 struct StreamArgs {
     const uint8_t* w;        // row 0 of the 64-row block, packed int4
     size_t w_stride;         // bytes between weight rows (K / 2)
@@ -36,61 +38,66 @@ struct StreamArgs {
     size_t s_stride;         // elements between scale rows (K / gq)
     int nw;                  // valid weight rows (<= 64)
     int gq;                  // quant group (>= 128, a multiple of 128)
+    const uint16_t* a;       // activation rows
+    size_t a_stride;         // elements between activation rows
 };
 
 template <int NS, int KB>
 struct StreamRegs {
     uint4 w[StreamLds<NS, KB>::NCH];                     // this thread's share of the weights
-    uint2 s;                                             // scales (threads < 64)
+    uint32_t s;                                          // one scale
     uint4 a[NS * KB / 128];                              // share of the activations
 };
 
-// Global -> registers for block [kb, kb + KB).  `arow` (LDS, 16*NS entries)
-// holds the activation row pointers; rows past na are not loaded.
+// Per-thread sources, fixed for the whole K range: the weight row, the scale
+// row and the activation rows this thread loads.  Rows past nw or na read a
+// valid row again, so every load is unconditional: the loads of one block are
+// a fixed sequence and the waits before the LDS stores count exactly the loads
+// of the block still in flight behind them.
 template <int NS, int KB>
-EM_DEV void stream_fetch(StreamRegs<NS, KB>& r, const StreamArgs& sa, const uint16_t* const* arow, int na,
-                         int kb) {
+struct StreamSrc {
+    const uint8_t* w[StreamLds<NS, KB>::NCH];
+    const uint16_t* s;
+    const uint16_t* a[NS * KB / 128];
+};
+
+template <int NS, int KB>
+EM_DEV void stream_src(StreamSrc<NS, KB>& p, const StreamArgs& sa, const int* arow, int na) {
     constexpr int NCH = KB / KC;
     constexpr int SEG = KB / 32;                         // 16-byte segments per weight row
+    constexpr int ASEG = KB / 8;                         // 16-byte segments per activation row
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int q = tid + 256 * i;
         const int row = q / SEG, seg = q % SEG;
-        const int rr = row < sa.nw ? row : 0;
-        r.w[i] = ld16(sa.w + rr * sa.w_stride + (kb >> 1) + 16 * seg);
+        p.w[i] = sa.w + (row < sa.nw ? row : 0) * sa.w_stride + 16 * seg;
     }
-    if (tid < 64) {
-        const int rr = tid < sa.nw ? tid : 0;
-        const uint16_t* sp = sa.s + rr * sa.s_stride + kb / sa.gq;
-        if (sa.gq == KC) {
-            // NCH consecutive scales (NCH <= 4), 8-byte aligned when NCH == 4
-            if constexpr (NCH == 4) {
-                r.s = *reinterpret_cast<const uint2*>(sp);
-            } else {
-                uint32_t h[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) h[i] = sp[i];
-                r.s = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-            }
-        } else {
-            // one scale covers gq / 128 chunks
-            uint32_t h[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) h[i] = sa.s[rr * sa.s_stride + (kb + i * KC) / sa.gq];
-            r.s = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        }
-    }
-    constexpr int ASEG = KB / 8;                         // 16-byte segments per activation row
+    const int srow = tid >> 2;
+    p.s = sa.s + (srow < sa.nw ? srow : 0) * sa.s_stride;
 #pragma unroll
     for (int i = 0; i < NS * KB / 128; ++i) {
         const int q = tid + 256 * i;
         const int row = q / ASEG, seg = q % ASEG;
-        const int rr = row < na ? row : 0;
-        r.a[i] = ld16(arow[rr] + kb + 8 * seg);
+        p.a[i] = sa.a + (size_t)arow[row < na ? row : 0] * sa.a_stride + 8 * seg;
     }
 }
 
+// Global -> registers for block [kb, kb + KB).
+template <int NS, int KB>
+EM_DEV void stream_fetch(StreamRegs<NS, KB>& r, const StreamSrc<NS, KB>& p, int gq, int kb) {
+    constexpr int NCH = KB / KC;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) r.w[i] = ld16(p.w[i] + (kb >> 1));
+    // thread (row, chunk) = (tid / 4, tid % 4); chunks past NCH repeat the last
+    const int ch = min((int)(threadIdx.x & 3), NCH - 1);
+    r.s = p.s[(kb + ch * KC) / gq];
+#pragma unroll
+    for (int i = 0; i < NS * KB / 128; ++i) r.a[i] = ld16(p.a[i] + kb);
+}
+
+// Activation rows past na hold copies of row 0: they only reach output rows
+// that are never stored (an MFMA output row depends on its own A row alone).
 template <int NS, int KB>
 EM_DEV void stream_store(StreamLds<NS, KB>& L, int buf, const StreamRegs<NS, KB>& r) {
     constexpr int NCH = KB / KC;
@@ -102,11 +109,7 @@ EM_DEV void stream_store(StreamLds<NS, KB>& L, int buf, const StreamRegs<NS, KB>
         const int row = q / SEG, seg = q % SEG;
         L.w[buf][row][seg] = r.w[i];
     }
-    if (tid < 64) {
-        const uint32_t h[4] = {r.s.x & 0xFFFFu, r.s.x >> 16, r.s.y & 0xFFFFu, r.s.y >> 16};
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) L.s[buf][tid][i] = (uint16_t)h[i];
-    }
+    if ((tid & 3) < NCH) L.s[buf][tid >> 2][tid & 3] = (uint16_t)r.s;
     constexpr int ASEG = KB / 8;
 #pragma unroll
     for (int i = 0; i < NS * KB / 128; ++i) {
@@ -138,23 +141,54 @@ EM_DEV void stream_compute(floatx4 (&acc)[NS], const StreamLds<NS, KB>& L, int b
 }
 
 // acc += W[64 rows] . A over K range [k0, k1) (multiples of KB).  Every thread
-// of the workgroup must call this; it synchronises the workgroup.
+// of the workgroup must call this; it synchronises the workgroup.  Global loads
+// run two blocks ahead of the arithmetic (two register sets), so each block's
+// load latency overlaps two blocks of work instead of one.
 template <int NS, int KB>
 EM_DEV void stream_gemm(floatx4 (&acc)[NS], StreamLds<NS, KB>& L, const StreamArgs& sa,
-                        const uint16_t* const* arow, int na, int k0, int k1) {
-    StreamRegs<NS, KB> r;
-    stream_fetch<NS, KB>(r, sa, arow, na, k0);
-    stream_store<NS, KB>(L, 0, r);
+                        const int* arow, int na, int k0, int k1) {
+    StreamSrc<NS, KB> p;
+    stream_src<NS, KB>(p, sa, arow, na);
+    StreamRegs<NS, KB> r0, r1;
+    const int nb = (k1 - k0) / KB;
+    // the second fetch is unconditional (a single block loads itself twice)
+    stream_fetch<NS, KB>(r0, p, sa.gq, k0);
+    stream_fetch<NS, KB>(r1, p, sa.gq, k0 + (nb > 1 ? KB : 0));
+    stream_store<NS, KB>(L, 0, r0);
     __syncthreads();
-    int buf = 0;
-    for (int kb = k0; kb < k1; kb += KB) {
-        const bool more = kb + KB < k1;
-        if (more) stream_fetch<NS, KB>(r, sa, arow, na, kb + KB);
-        stream_compute<NS, KB>(acc, L, buf);
-        if (more) stream_store<NS, KB>(L, buf ^ 1, r);
+    // Steady state: block b sits in LDS buffer 0, r1 holds block b + 1 and r0
+    // receives block b + 2.  The loop only runs while blocks b + 2 and b + 3
+    // exist, so its loads are unconditional and the waits exact.
+    int b = 0;
+    for (; b + 3 < nb; b += 2) {
+        stream_fetch<NS, KB>(r0, p, sa.gq, k0 + (b + 2) * KB);
+        stream_compute<NS, KB>(acc, L, 0);
+        stream_store<NS, KB>(L, 1, r1);
         __syncthreads();
-        buf ^= 1;
+        stream_fetch<NS, KB>(r1, p, sa.gq, k0 + (b + 3) * KB);
+        stream_compute<NS, KB>(acc, L, 1);
+        stream_store<NS, KB>(L, 0, r0);
+        __syncthreads();
     }
+    // the last one, two or three blocks
+    if (b + 2 < nb) {
+        stream_fetch<NS, KB>(r0, p, sa.gq, k0 + (b + 2) * KB);
+        stream_compute<NS, KB>(acc, L, 0);
+        stream_store<NS, KB>(L, 1, r1);
+        __syncthreads();
+        stream_compute<NS, KB>(acc, L, 1);
+        stream_store<NS, KB>(L, 0, r0);
+        __syncthreads();
+        stream_compute<NS, KB>(acc, L, 0);
+    } else if (b + 1 < nb) {
+        stream_compute<NS, KB>(acc, L, 0);
+        stream_store<NS, KB>(L, 1, r1);
+        __syncthreads();
+        stream_compute<NS, KB>(acc, L, 1);
+    } else {
+        stream_compute<NS, KB>(acc, L, 0);
+    }
+    __syncthreads();
 }
 
 }  // namespace em
