@@ -62,10 +62,25 @@ def kernel_bytes(D, idx: np.ndarray):
     R = T * k
     U = sum(len(np.unique(np.nonzero((idx // D.experts_per_group) == g)[0]))
             for g in range(D.n_experts // D.experts_per_group))
-    d, h, r = D.d, D.h, D.delta_rank
+    d, h, r, rL, E = D.d, D.h, D.delta_rank, D.lora_rank, D.n_experts
+    x_b = T * d * 2                       # the batch, bf16
+    logits_b = T * E * 4
+    gw_up = per["s_up"] + per["lu_u"] + per["lu_v"]
+    gw_dn = per["s_dn"] + per["ld_u"] + per["ld_v"]
     return {
-        "router_logits_small": per["w_router"] + T * d * 2 + T * D.n_experts * 4,
-        "router_logits_tiled": per["w_router"] + T * d * 2 + T * D.n_experts * 4,
+        # router (both paths)
+        "router_logits_small": per["w_router"] + x_b + logits_b,
+        "router_logits_tiled": per["w_router"] + x_b + logits_b,
+        "router_topk": logits_b + R * 8,
+        # decode / verify path: each touched group's and expert's weights once,
+        # the kernel's inputs read once and its outputs written once
+        "dec_up": G * (per["s_up"] + per["lu_u"]) + X * per["a_up"] + x_b
+                  + U * h * 4 + R * r * 4 + U * rL * 4,
+        "dec_act": X * (per["b_up"] + per["a_dn"]) + G * (per["lu_v"] + per["ld_u"])
+                   + U * h * 4 + R * r * 4 + U * rL * 4 + R * h * 2 + R * (r + rL) * 2,
+        "dec_down": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2
+                    + R * (r + rL) * 2 + R * 4 + T * d * 4,
+        # general (prefill) path
         "gemm_z1": X * per["a_up"] + R * d * 2 + R * r * 2,
         "lora_in_up": G * per["lu_u"] + U * d * 2,
         "gemm_shared_up": G * (per["s_up"] + per["lu_v"]) + U * d * 2 + U * h * 4,
@@ -74,7 +89,7 @@ def kernel_bytes(D, idx: np.ndarray):
         "lora_in_down": G * per["ld_u"] + R * h * 2,
         "gemm_down": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2 + R * d * 4,
         "combine": R * d * 4 + T * d * 4,
-    }, {"groups": G, "experts": X, "rows": R, "unique": U}
+    }, {"groups": G, "experts": X, "rows": R, "unique": U, "gw_up": gw_up, "gw_dn": gw_dn}
 
 
 def step_bytes(D, idx):
@@ -108,7 +123,7 @@ def kernel_flops(D, idx):
 # ---------------------------------------------------------------- device workload ----
 
 class Workload:
-    def __init__(self, cfg_id, layers, seed=0):
+    def __init__(self, cfg_id, layers, seed=0, host_init=False):
         import torch
         import shared_matrix_expert_amd as em
         import synth
@@ -126,7 +141,7 @@ class Workload:
                 "wr_host": wr, "bias_host": bias,
                 "wr": torch.from_numpy(wr.view(np.int16)).cuda(),
                 "bias": None if bias is None else torch.from_numpy(bias).cuda(),
-                "W": synth.make_weights(cfg_id, seed, layer, device="cuda"),
+                "W": self._weights(synth, cfg_id, seed, layer, host_init),
             })
         D = self.D
         self.ws = torch.empty(em.edge_moe_workspace_bytes(D), dtype=torch.uint8, device="cuda")
@@ -134,6 +149,14 @@ class Workload:
         self.w = torch.empty(D.T, D.top_k, dtype=torch.float32, device="cuda")
         self.y = torch.empty(D.T, D.d, dtype=torch.float32, device="cuda")
         self.stream = torch.cuda.current_stream()
+
+    @staticmethod
+    def _weights(synth, cfg_id, seed, layer, host_init):
+        """Weights made on the device, or (host_init) on the host and copied over,
+        so that no kernel but the library's runs in the process (counter runs)."""
+        if not host_init:
+            return synth.make_weights(cfg_id, seed, layer, device="cuda")
+        return {k: v.cuda() for k, v in synth.make_weights(cfg_id, seed, layer, device="cpu").items()}
 
     def step(self, i):
         L = self.layers[i % len(self.layers)]
@@ -185,6 +208,30 @@ def roofline_hbm(D, idxs, ktimes):
     return name, {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                   "kernel": name, "avg_ms": round(avg_ms, 5), "bytes_per_launch": int(bytes_per)}
+
+
+def stored_traffic(kernel: str, workload_tag: str):
+    """HBM bytes per launch of `kernel` from the counter summary under profiles/,
+    or None when there is none or it was taken with other kernel sources."""
+    from shared_matrix_expert_amd.build import sources_digest
+    from shared_matrix_expert_amd.profsum import read_traffic
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    t = read_traffic(path)
+    if t.get("sources_sha256") != sources_digest():
+        return None
+    return int(float(t["traffic_bytes_per_dispatch"]))
+
+
+def kernel_table(D, idxs, ktimes):
+    """Per-kernel average time, algorithmic bytes and the HBM rate they imply."""
+    out = {}
+    for k, (n, ms) in sorted(ktimes.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        b = float(np.mean([kernel_bytes(D, ix)[0].get(k, 0) for ix in idxs]))
+        out[k] = {"avg_us": round(ms * 1e3, 2), "bytes": int(b),
+                  "GBs": round(b / (ms * 1e-3) / 1e9, 1) if b else None}
+    return out
 
 
 def roofline_mfma(D, idxs, ktimes):
@@ -260,6 +307,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--host-init", action="store_true",
+                    help="make the weights on the host (no kernel but the library's runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -276,13 +325,13 @@ def main():
         n = args.calib_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
-        b.copy_(a)
+        em.edge_moe_copy(b, a)
         torch.cuda.synchronize()
         log(f"calibration copy of {n} bytes done")
 
     # ---- verify T=8, skewed routing, rotating layer instances
     log("building verify workload ...")
-    wl = Workload(2, args.layers)
+    wl = Workload(2, args.layers, host_init=args.host_init)
     D = wl.D
     idxs = wl.routed_indices()
     sec = wl.time_steps(args.steps, args.warmup)
@@ -290,6 +339,7 @@ def main():
     for k, (n, ms) in sorted(ktimes.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
         log(f"  verify kernel {k:22s} launches {n:5d} avg {ms * 1e3:8.2f} us")
     kname, roof = roofline_hbm(D, idxs, ktimes)
+    roof["traffic"] = stored_traffic(kname, "verify_t8")
     sb = float(np.mean([step_bytes(D, ix) for ix in idxs]))
     line = {
         "metric": METRIC,
@@ -310,6 +360,7 @@ def main():
                                "rL=16; steps rotate over %d layer instances" % args.layers,
                    "T": D.T, "layers_rotated": args.layers},
         "roofline": roof,
+        "kernels": kernel_table(D, idxs, ktimes),
         "step_hbm": {"bytes_per_step": int(sb), "achieved_GBs": round(sb / sec / 1e9, 1),
                      "frac": round(sb / sec / 1e9 / HBM_PEAK_GBS, 4)},
     }
@@ -321,13 +372,14 @@ def main():
 
     if not args.no_prefill:
         log("building prefill workload ...")
-        wp = Workload(3, 1)
+        wp = Workload(3, 1, host_init=args.host_init)
         pidx = wp.routed_indices()
         psec = wp.time_steps(args.prefill_steps, 2)
         pk = wp.kernel_times(args.prefill_steps)
         for k, (n, ms) in sorted(pk.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
             log(f"  prefill kernel {k:22s} launches {n:5d} avg {ms:9.3f} ms")
         pname, proof = roofline_mfma(wp.D, pidx, pk)
+        proof["traffic"] = stored_traffic(pname, "prefill_16k")
         total_fl = float(np.mean([sum(kernel_flops(wp.D, ix).values()) for ix in pidx]))
         line["prefill_16k"] = {
             "value": round(wp.D.T / psec, 1), "unit": "tokens/s", "steps": args.prefill_steps,

@@ -162,6 +162,13 @@ int edge_moe_forward_traced(const edge_moe_dims* dims, const uint16_t* x,
 int edge_moe_residual(int32_t T, int32_t d, const uint16_t* x, const float* y, uint16_t* x_out,
                       void* stream);
 
+/* Plain device copy of `bytes` bytes (dst and src 16-byte aligned, bytes a
+ * multiple of 16, non-overlapping), enqueued on `stream` as one kernel that
+ * reads every source byte once and writes every destination byte once.  Not a
+ * step of the layer: it is the reference workload of known size used to
+ * calibrate the memory-traffic counters of a profiler against bytes. */
+int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* edge_moe_status_string(int status);
 

@@ -27,7 +27,7 @@ EDGE_MOE_EHIP = -4
 
 EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_forward_traced", "edge_moe_residual", "edge_moe_status_string",
-            "edge_moe_abi_version",
+            "edge_moe_abi_version", "edge_moe_copy",
             "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset")
 
 
@@ -90,6 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_moe_forward_traced.restype = i32
     lib.edge_moe_residual.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     lib.edge_moe_residual.restype = i32
+    lib.edge_moe_copy.argtypes = [vp, vp, sz, vp]
+    lib.edge_moe_copy.restype = i32
     lib.edge_moe_status_string.argtypes = [i32]
     lib.edge_moe_status_string.restype = ctypes.c_char_p
     lib.edge_moe_abi_version.argtypes = []
@@ -131,6 +133,16 @@ def cweights(weights: dict) -> CWeights:
 
 def status_string(status: int) -> str:
     return load().edge_moe_status_string(int(status)).decode()
+
+
+def edge_moe_copy(dst, src, stream=None) -> None:
+    """Plain device copy of src into dst (same byte size), one library kernel."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("edge_moe_copy: dst and src differ in size")
+    st = load().edge_moe_copy(_ptr(dst), _ptr(src), n, _stream(stream))
+    if st != EDGE_MOE_OK:
+        raise EdgeMoeError("edge_moe_copy", st)
 
 
 def edge_moe_abi_version() -> int:

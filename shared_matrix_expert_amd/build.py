@@ -23,6 +23,18 @@ SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "decode.hip"]
 ARCH = "gfx950"
 
 
+def sources_digest() -> str:
+    """sha256 over the library's sources and public header: identifies the
+    kernels a stored profile was taken from."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for f in files + ["../../include/edge_moe.h"]:
+        with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):

@@ -418,6 +418,17 @@ int edge_moe_residual(int32_t T, int32_t d, const uint16_t* x, const float* y, u
                                                                                      : EDGE_MOE_EHIP;
 }
 
+int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!dst || !src || bytes % 16 || !aligned(dst, 16) || !aligned(src, 16)) return EDGE_MOE_EINVAL;
+    const char* d8 = static_cast<const char*>(dst);
+    const char* s8 = static_cast<const char*>(src);
+    if (d8 < s8 + bytes && s8 < d8 + bytes) return EDGE_MOE_EINVAL;
+    const int st = check_device();
+    if (st != EDGE_MOE_OK) return st;
+    if (bytes == 0) return EDGE_MOE_OK;
+    return em::launch_copy(dst, src, bytes, (hipStream_t)stream) == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
+}
+
 const char* edge_moe_status_string(int status) {
     switch (status) {
         case EDGE_MOE_OK: return "ok";

@@ -386,7 +386,7 @@ EM_DEV uint4 lds_a(const uint16_t* row, int kk, int K, bool valid) {
 
 template <int NS>
 __global__ void __launch_bounds__(256)
-dec_act(DecodeArgs a) {
+dec_act_direct(DecodeArgs a) {
     __shared__ RouteView v;
     __shared__ __attribute__((aligned(16))) uint16_t zs[16 * NS][ZS_W];
     __shared__ __attribute__((aligned(16))) uint16_t zls[16 * NS][ZL_W];
@@ -602,14 +602,14 @@ dec_act(DecodeArgs a) {
 }
 
 // Activation kernel with every weight block staged through LDS (r = 128,
-// quant groups of 128, 256 columns per workgroup): the expert's B_up rows of
+// quant groups a multiple of 128, 256 columns per workgroup): the expert's B_up rows of
 // these columns (256 x 64 B, contiguous), its A_dn columns (128 rows x 128 B)
 // and the group's U_dn columns are loaded coalesced and up front.
 constexpr int CB_L = 256;
 
 template <int NS>
 __global__ void __launch_bounds__(256)
-dec_act_lds(DecodeArgs a) {
+dec_act(DecodeArgs a) {
     __shared__ RouteView v;
     __shared__ __attribute__((aligned(16))) uint16_t zs[16 * NS][KC + 8];
     __shared__ __attribute__((aligned(16))) uint16_t zls[16 * NS][ZL_W];
@@ -979,9 +979,13 @@ static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
     dec_up<NS, LDSP><<<g1, 256, 0, s>>>(a);
     prof_end(s, "dec_up");
     prof_begin(s);
-    if (LDSP) dec_act_lds<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
-    else dec_act<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
-    prof_end(s, "dec_act");
+    if (LDSP) {
+        dec_act<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
+        prof_end(s, "dec_act");
+    } else {
+        dec_act_direct<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
+        prof_end(s, "dec_act_direct");
+    }
     const int g3 = a.npass * a.G * (a.d / 64);
     prof_begin(s);
     if (ns_down == 2) dec_down<2, LDSP><<<g3, 256, 0, s>>>(a);

@@ -357,6 +357,23 @@ residual_add(const uint16_t* __restrict__ x, const float* __restrict__ y, uint16
     xo[i] = (uint16_t)f64_to_bf16_rne(s);
 }
 
+// Plain copy, 16 bytes per thread per step, grid-stride.
+__global__ void __launch_bounds__(256)
+copy_bytes(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        dst[i] = src[i];
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    const size_t want = (n16 + 255) / 256, cap = 256 * 16;
+    const size_t blocks = want < cap ? want : cap;
+    prof_begin(stream);
+    copy_bytes<<<(unsigned)blocks, 256, 0, stream>>>(static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16);
+    prof_end(stream, "copy_bytes");
+    return hipGetLastError();
+}
+
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
                            hipStream_t s) {
     const int64_t n = (int64_t)T * d;

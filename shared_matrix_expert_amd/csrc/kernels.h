@@ -104,6 +104,7 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_gather_rows(const void* src, const int32_t* index, void* dst, int64_t rows,
                               int64_t row_bytes, hipStream_t stream);
 
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
                            hipStream_t stream);
 

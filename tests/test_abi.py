@@ -119,3 +119,15 @@ def test_binding_requires_the_library(tmp_path):
             em_mod.load(str(tmp_path / "missing.so"))
     finally:
         em_mod._lib = saved
+
+
+def test_copy_validation_before_any_device_call():
+    lib = em.load()
+    base = 1 << 40                          # never dereferenced: rejected first
+    cases = [(base + 8, base + 4096, 64),   # misaligned dst
+             (base, base + 4096 + 8, 64),   # misaligned src
+             (base, base + 4096, 24),       # not a multiple of 16
+             (base, base + 32, 64),         # overlapping
+             (0, base, 64)]                 # null
+    for dst, src, n in cases:
+        assert lib.edge_moe_copy(ctypes.c_void_p(dst), ctypes.c_void_p(src), n, None) == em.EDGE_MOE_EINVAL
