@@ -46,7 +46,7 @@ int check_dims(const edge_moe_dims* p) {
 struct Layout {
     size_t bm, pre, total, eoff, uoff, etile, gtile_u, gtile_r;
     size_t row_tok, row_slot, row_exp, row_u, slot_row, ut_tok;
-    size_t z1, zl, hs, act, z2, zl2, o;
+    size_t xg, z1, zl, hs, act, z2, zl2, o;
     size_t logits;
     size_t fwd_bytes, route_bytes;
     int64_t R, Umax;
@@ -78,6 +78,7 @@ Layout make_layout(const edge_moe_dims& d) {
     L.row_u = take(L.R * 4);
     L.slot_row = take(L.R * 4);
     L.ut_tok = take(L.Umax * 4);
+    L.xg = take((size_t)L.Umax * d.d * 2);
     L.z1 = take((size_t)L.R * d.delta_rank * 2);
     L.zl = take((size_t)L.Umax * L.rLp * 2);
     L.hs = take((size_t)L.Umax * d.h * 4);
@@ -99,6 +100,16 @@ bool use_decode(const edge_moe_dims& d) {
         return v && v[0] == '1';
     }();
     return !force_general && d.T <= 64 && (int64_t)d.T * d.top_k <= 1024 && d.experts_per_group <= 64;
+}
+
+// EDGE_MOE_OLD_GEMM=1 keeps large batches on the per-wave streaming GEMMs
+// instead of the LDS-tiled shared-matrix GEMMs (used by tests to cover both).
+bool force_old_gemm() {
+    static const bool v = [] {
+        const char* e = getenv("EDGE_MOE_OLD_GEMM");
+        return e && e[0] == '1';
+    }();
+    return v;
 }
 
 struct DecLayout {
@@ -361,6 +372,7 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     a.a_up = wt->a_up_q; a.a_up_s = wt->a_up_scale; a.b_up = wt->b_up_q; a.b_up_s = wt->b_up_scale;
     a.a_dn = wt->a_dn_q; a.a_dn_s = wt->a_dn_scale; a.b_dn = wt->b_dn_q; a.b_dn_s = wt->b_dn_scale;
     a.lu_u = wt->lora_up_u; a.lu_v = wt->lora_up_v; a.ld_u = wt->lora_dn_u; a.ld_v = wt->lora_dn_v;
+    a.xg = reinterpret_cast<uint16_t*>(base + L.xg);
     a.z1 = reinterpret_cast<uint16_t*>(base + L.z1);
     a.zl = reinterpret_cast<uint16_t*>(base + L.zl);
     a.hs = reinterpret_cast<float*>(base + L.hs);
@@ -377,6 +389,9 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     a.max_etiles = (int)((R + a.mt - 1) / a.mt + (E < R ? E : R));
     a.max_gtiles_u = (int)((L.Umax + a.mt - 1) / a.mt + G);
     a.max_gtiles_r = (int)((R + a.mt - 1) / a.mt + G);
+    a.pf = em::prefill_gemm_ok(d.d, d.h, d.delta_rank, d.lora_rank, d.quant_group) && !force_old_gemm() ? 1 : 0;
+    a.umax = L.Umax;
+    a.rmax = R;
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t err = em::launch_dispatch(topk_idx, db, d.T, d.top_k, d.n_experts, d.experts_per_group,

@@ -419,7 +419,13 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
     lora_in<0><<<a.max_gtiles_u, 256, 0, s>>>(a);
     prof_end(s, "lora_in_up");
     // a4 + a6: shared up + LoRA up, once per (token, group)
-    launch_gemm<M_HS>(a, a.max_gtiles_u, a.h, s, "gemm_shared_up");
+    if (a.pf) {
+        hipError_t e = launch_gather_x(a, a.umax, s);
+        if (e == hipSuccess) e = launch_prefill_gemm(a, PF_HS, a.umax, s);
+        if (e != hipSuccess) return e;
+    } else {
+        launch_gemm<M_HS>(a, a.max_gtiles_u, a.h, s, "gemm_shared_up");
+    }
     // a5 + a7: delta up, sum, SiLU, R3
     launch_gemm<M_ACT>(a, a.max_etiles, a.h, s, "gemm_delta_up_act");
     // a9 / a10 inputs: R4 (per row), R5 (per row)
@@ -428,7 +434,12 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
     lora_in<1><<<a.max_gtiles_r, 256, 0, s>>>(a);
     prof_end(s, "lora_in_down");
     // a8 - a10: shared down + delta down + LoRA down
-    launch_gemm<M_OUT>(a, a.max_gtiles_r, a.d, s, "gemm_down");
+    if (a.pf) {
+        const hipError_t e = launch_prefill_gemm(a, PF_OUT, a.rmax, s);
+        if (e != hipSuccess) return e;
+    } else {
+        launch_gemm<M_OUT>(a, a.max_gtiles_r, a.d, s, "gemm_down");
+    }
     // a11
     const int64_t n4 = (int64_t)a.T * (a.d / 4);
     prof_begin(s);

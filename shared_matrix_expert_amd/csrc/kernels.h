@@ -44,6 +44,7 @@ struct LayerArgs {
     const uint16_t* lu_u; const uint16_t* lu_v;
     const uint16_t* ld_u; const uint16_t* ld_v;
     // intermediates (workspace)
+    uint16_t* xg;               // [Umax][d] bf16: x rows of each group's distinct tokens (prefill GEMMs)
     uint16_t* z1;               // [R][r]   bf16
     uint16_t* zl;               // [Umax][rL] bf16 (per unique token of a group)
     float* hs;                  // [Umax][h] shared-up + LoRA-up, fp32
@@ -54,6 +55,8 @@ struct LayerArgs {
     float* y;                   // [T][d]   output
     DispatchBufs db;
     int max_etiles, max_gtiles_u, max_gtiles_r;   // grid bounds
+    int pf;                     // shared up / down on the LDS-tiled prefill GEMMs (prefill_gemm_ok)
+    int64_t umax, rmax;         // bounds on distinct (token, group) pairs and rows
 };
 
 // Small-batch expert layer (T <= 64, T*k <= 1024): three launches, every
@@ -104,6 +107,11 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_gather_rows(const void* src, const int32_t* index, void* dst, int64_t rows,
                               int64_t row_bytes, hipStream_t stream);
 
+// LDS-tiled shared-matrix GEMMs of large batches (prefill.hip)
+enum PfMode { PF_HS = 0, PF_OUT = 1 };
+bool prefill_gemm_ok(int d, int h, int r, int rL, int gq);
+hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, hipStream_t s);
+hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
                            hipStream_t stream);

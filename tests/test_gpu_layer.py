@@ -87,13 +87,7 @@ def test_decode_layer(seed):
     _run_parity(D, x, wr, bias, synth.make_weights(1, seed, device="cuda"))
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_verify_skewed_layer(seed):
-    say(f"case: verify C2 seed={seed}")
-    D = synth.config(2).dims
-    x, wr, bias = _inputs(2, seed)
-    lay, idx, w, y, tr, fw = _run_parity(D, x, wr, bias, synth.make_weights(2, seed, device="cuda"),
-                                         keep=True)
+def _check_trace(D, idx, tr, fw):
     # permutation bit-exact against a numpy lexsort
     offs, rt, rs = expected_permutation(idx.cpu().numpy(), D.n_experts)
     assert np.array_equal(tr["expert_offsets"].cpu().numpy(), offs)
@@ -115,6 +109,16 @@ def test_verify_skewed_layer(seed):
     o_gpu = tr["expert_out"].cpu().numpy().astype(np.float64)
     o_ref = fw["o"].reshape(-1, D.d)
     assert np.all(np.abs(o_gpu - o_ref) <= 1e-2 + 1e-2 * np.abs(o_ref)), float(np.max(np.abs(o_gpu - o_ref)))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_verify_skewed_layer(seed):
+    say(f"case: verify C2 seed={seed}")
+    D = synth.config(2).dims
+    x, wr, bias = _inputs(2, seed)
+    lay, idx, w, y, tr, fw = _run_parity(D, x, wr, bias, synth.make_weights(2, seed, device="cuda"),
+                                         keep=True)
+    _check_trace(D, idx, tr, fw)
     # determinism
     y2, _ = lay.forward(bits_to_dev(x), idx, w)
     assert torch.equal(y, y2)
@@ -141,6 +145,20 @@ def test_ragged_batches(T):
     wr, _ = synth.make_router(1, 5)
     sample = np.unique(np.linspace(0, T - 1, min(T, 12)).astype(int))
     _run_parity(D, x, wr, None, synth.make_weights(1, 5, device="cuda"), sample=sample)
+
+
+def test_general_path_traced():
+    """A batch above the decode limit (T=72, full shapes): permutation kernels,
+    the LDS-tiled shared-matrix GEMMs over partial row tiles, every slot's
+    activation and expert output against the oracle."""
+    say("case: general path T=72 traced")
+    D = synth.config(1).dims.with_T(72)
+    x = synth.make_activations(1, 3, T=72)
+    wr, _ = synth.make_router(1, 3)
+    lay, idx, w, y, tr, fw = _run_parity(D, x, wr, None, synth.make_weights(1, 3, device="cuda"), keep=True)
+    _check_trace(D, idx, tr, fw)
+    y2, _ = lay.forward(bits_to_dev(x), idx, w)
+    assert torch.equal(y, y2)
 
 
 def test_zero_delta_zero_lora():
