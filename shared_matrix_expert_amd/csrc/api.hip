@@ -78,11 +78,11 @@ Layout make_layout(const edge_moe_dims& d) {
     L.row_u = take(L.R * 4);
     L.slot_row = take(L.R * 4);
     L.ut_tok = take(L.Umax * 4);
-    L.xg = take((size_t)L.Umax * d.d * 2);
+    L.xg = take((size_t)(L.Umax + em::kPfSpareRows) * d.d * 2);   // + spare rows read by the last row tile
     L.z1 = take((size_t)L.R * d.delta_rank * 2);
     L.zl = take((size_t)L.Umax * L.rLp * 2);
     L.hs = take((size_t)L.Umax * d.h * 4);
-    L.act = take((size_t)L.R * d.h * 2);
+    L.act = take((size_t)(L.R + em::kPfSpareRows) * d.h * 2);
     L.z2 = take((size_t)L.R * d.delta_rank * 2);
     L.zl2 = take((size_t)L.R * L.rLp * 2);
     L.o = take((size_t)L.R * d.d * 4);

@@ -74,6 +74,17 @@ EM_DEV floatx4 mfma_bf16(uint4 a, uint4 b, floatx4 c) {
 
 EM_DEV floatx4 zero4() { floatx4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// acc + s * t, one fused multiply-add per element (a scaled chunk sum added to
+// its accumulator with a single rounding).
+EM_DEV floatx4 fma4(float s, floatx4 t, floatx4 acc) {
+    floatx4 r;
+    r.x = __builtin_fmaf(s, t.x, acc.x);
+    r.y = __builtin_fmaf(s, t.y, acc.y);
+    r.z = __builtin_fmaf(s, t.z, acc.z);
+    r.w = __builtin_fmaf(s, t.w, acc.w);
+    return r;
+}
+
 // ---------------------------------------------------------------- misc ----------
 EM_DEV int lane_id() { return threadIdx.x & (kWave - 1); }
 EM_DEV int wave_id() { return threadIdx.x >> 6; }

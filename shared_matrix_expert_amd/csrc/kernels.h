@@ -109,6 +109,7 @@ hipError_t launch_gather_rows(const void* src, const int32_t* index, void* dst, 
 
 // LDS-tiled shared-matrix GEMMs of large batches (prefill.hip)
 enum PfMode { PF_HS = 0, PF_OUT = 1 };
+constexpr int kPfSpareRows = 128;    // readable rows past the end of xg and act (one row tile)
 bool prefill_gemm_ok(int d, int h, int r, int rL, int gq);
 hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, hipStream_t s);
 hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);

@@ -105,7 +105,7 @@ EM_DEV void mac_i4(floatx4 (&acc)[NS], const uint4 (&af)[NS][4], int nsub, uint4
                 floatx4 t = zero4();
 #pragma unroll
                 for (int s = 0; s < 4; ++s) t = mfma_bf16(af[ms][s], b[s], t);
-                acc[ms] = sc * t + acc[ms];
+                acc[ms] = fma4(sc, t, acc[ms]);
             }
         }
     } else {
@@ -121,7 +121,7 @@ EM_DEV void mac_i4(floatx4 (&acc)[NS], const uint4 (&af)[NS][4], int nsub, uint4
                     floatx4 t = zero4();
 #pragma unroll
                     for (int s = 0; s < 4; ++s) t = mfma_bf16(mine ? af[ms][s] : z, b[s], t);
-                    acc[ms] = sc * t + acc[ms];
+                    acc[ms] = fma4(sc, t, acc[ms]);
                 }
             }
         }
@@ -202,7 +202,7 @@ EM_DEV void mac_fast(floatx4 (&acc)[NS], const uint4 (&af)[NS][4], uint4 raw, ui
         floatx4 t = zero4();
 #pragma unroll
         for (int s = 0; s < 4; ++s) t = mfma_bf16(af[ms][s], b[s], t);
-        acc[ms] = sc * t + acc[ms];
+        acc[ms] = fma4(sc, t, acc[ms]);
     }
 }
 

@@ -8,16 +8,17 @@
 // times S_up (up), the group's rows times S_dn (down).  At 16K tokens these
 // two GEMMs are ~95 % of the layer's flops.
 //
-// Tile: 256 rows x 128 columns per workgroup of 4 waves (2 x 2, each wave 128
-// rows x 64 columns = 8 x 4 MFMA 16x16 subtiles), K in steps of 128 = one
-// quant group.  The activation tile (256 x 128 bf16 = 64 KB) moves from global
-// memory straight into LDS (global_load_lds_dwordx4, no registers), double
-// buffered, with the 16-byte slots of each row XOR-swizzled by the row so that
-// the MFMA fragment reads are free of bank conflicts.  The int4 weights go
-// into LDS the same way (128 columns x 64 bytes per step) and each wave converts
-// its 64 columns exactly to bf16 in registers; every 128-element chunk is accumulated in
-// a fresh fp32 tile and added to the result times 16 x its fp16 scale, so the
-// weight values are exactly q x s.
+// Tile: 128 rows x 256 columns per workgroup of 4 waves (each wave all 128
+// rows x its own 64 columns = 8 x 4 MFMA 16x16 subtiles), K in steps of 128 =
+// one quant group.  The activation tile (128 x 128 bf16 = 32 KB) and the
+// weight tile (256 columns x 128 int4 = 16 KB) move from global memory
+// straight into LDS (global_load_lds_dwordx4, no registers), three buffer sets
+// deep so that every step's loads have two steps of math to arrive in; the
+// 16-byte slots are XOR-swizzled so that the MFMA fragment reads are free of
+// bank conflicts.  Each wave converts its 64 columns exactly to bf16 in
+// registers; every 128-element chunk is accumulated in a fresh fp32 tile and
+// added to the result times 16 x its fp16 scale, so the weight values are
+// exactly q x s.
 //
 // Workgroup order: blockIdx is remapped so that each XCD (blockIdx mod 8) runs
 // a contiguous range of tiles, columns fastest: the workgroups that share an
@@ -30,11 +31,17 @@ namespace em {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 128;
+constexpr int BM = 128, BN = 256, BK = 128;
 constexpr int SLOTS = BK / 8;                    // 16-byte slots per activation row
+constexpr int WN = BN / 4;                       // columns per wave
+static_assert(BM <= kPfSpareRows, "the last row tile reads up to BM - 1 rows past the end");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// s_waitcnt with vmcnt = n and the other counters left free (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 struct PfTile {
     int g;          // group
@@ -62,53 +69,73 @@ EM_DEV bool pf_tile(const LayerArgs& a, int b, int ntn, PfTile& t) {
     return false;
 }
 
-// Activation tile for K step k0 into LDS: 256 rows x 16 slots.  Wave w, round
-// i covers rows 16 i + 4 w .. + 3 (1 KB, lane-contiguous); lane l writes slot
-// l % 16 of row 16 i + 4 w + l / 16 and fetches the row's global segment
-// (l % 16) ^ (row % 16).  Rows past r1 repeat row r1 - 1.
-EM_DEV void pf_fetch_a(uint4* As, const uint16_t* A, size_t lda, int r0, int r1, int k0) {
+// Per-thread sources, fixed for the whole K range: round i of the activation
+// DMA reads row r0 + 16 i + (4 w + l / 16) and round i of the weight DMA column
+// 64 i + 16 w + l / 4, so one base pointer per operand and a uniform stride
+// give every round.  Activation rows past r1 read the next rows of the buffer
+// (the workspace holds BM spare rows past the last one); they only reach
+// output rows that are never stored.
+struct PfSrc {
+    const uint16_t* a;              // round 0's activation row, at this lane's 16-byte segment
+    size_t a_step;                  // elements between rounds (16 rows)
+    const uint8_t* b;               // round 0's weight column, at this lane's 16-byte segment
+    size_t b_step;                  // bytes between rounds (64 columns)
+    const uint16_t* s;              // scale row of this lane's first column
+    size_t sstride;                 // elements between the scale rows of 16 columns
+};
+
+// Activation tile: 128 rows x 16 slots; wave w, round i covers rows 16 i + 4 w
+// .. + 3 (1 KB, lane-contiguous); lane l writes slot l % 16 of its row and
+// fetches the row's global segment (l % 16) ^ (row % 16), so that a fragment
+// read (16 rows, one segment) hits 16 distinct bank groups.  Weight tile: 256
+// columns x 4 slots of 16 bytes, slot = c ^ ((col / 4) % 4) holding the
+// column's bytes [16c, 16c + 16); wave w, round i covers columns 64 i + 16 w
+// .. + 15.
+EM_DEV void pf_src(PfSrc& p, const uint16_t* A, size_t lda, const uint8_t* Wt, size_t wstride,
+                   const uint16_t* srow0, size_t sstride, int r0) {
     const int w = wave_id(), l = lane_id();
     const int rsub = 4 * w + (l >> 4);
     const int seg = (l & 15) ^ (rsub & 15);
-#pragma unroll
-    for (int i = 0; i < BM / 16; ++i) {
-        const int row = r0 + 16 * i + rsub;
-        const uint16_t* src = A + (size_t)min(row, r1 - 1) * lda + k0 + 8 * seg;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(As + (16 * i + 4 * w) * SLOTS), 16, 0, 0);
-    }
+    p.a = A + (size_t)(r0 + rsub) * lda + 8 * seg;
+    p.a_step = 16 * lda;
+    const int col = 16 * w + (l >> 2);
+    p.b = Wt + (size_t)col * wstride + 16 * ((l & 3) ^ ((col >> 2) & 3));
+    p.b_step = 64 * wstride;
+    p.s = srow0;
+    p.sstride = sstride;
 }
 
-// Weight tile for K step k0 into LDS: 128 columns x 64 bytes (one int4 chunk
-// per column), 4 slots of 16 bytes per column with slot = c ^ ((col / 4) % 4)
-// holding the column's bytes [16c, 16c + 16), so that 16 lanes reading 16
-// consecutive columns hit 16 distinct bank groups.  Wave w, round i covers
-// columns 32 i + 16 w .. + 15 ... (two 1 KB rounds per wave).
-EM_DEV void pf_fetch_b(uint4* Bs, const uint8_t* W, size_t wstride, int k0) {
-    const int w = wave_id(), l = lane_id();
+// Step k0's loads: the 4 scales of this lane's columns first, then the weight
+// and activation tiles (12 DMA instructions per thread).
+EM_DEV void pf_fetch(uint4* As, uint4* Bs, uint32_t (&sb)[4], const PfSrc& p, int gq, int k0) {
+    const int w = wave_id();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int col = 64 * i + 16 * w + (l >> 2);
-        const int cseg = (l & 3) ^ ((col >> 2) & 3);
-        const uint8_t* src = W + (size_t)col * wstride + (k0 >> 1) + 16 * cseg;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(Bs + (64 * i + 16 * w) * 4), 16, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) sb[j] = p.s[(size_t)(16 * j) * p.sstride + k0 / gq];
+#pragma unroll
+    for (int i = 0; i < BN / 64; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.b + i * p.b_step + (k0 >> 1)),
+                                         (lds_ptr_t)(Bs + (64 * i + 16 * w) * 4), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BM / 16; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.a + i * p.a_step + k0),
+                                         (lds_ptr_t)(As + (16 * i + 4 * w) * SLOTS), 16, 0, 0);
 }
+constexpr int PF_STEP_VM = 4 + BN / 64 + BM / 16;      // vector-memory instructions per step and thread
 
 // acc[i][j] += (A rows of subtile i) x (16 x scale_j x dequant(B_j)) over one chunk.
-EM_DEV void pf_compute(floatx4 (&acc)[8][4], const uint4* As, const uint4* Bs, const uint32_t (&sbits)[4],
-                       int wm, int wn) {
+EM_DEV void pf_compute(floatx4 (&acc)[8][4], const uint4* As, const uint4* Bs, const uint32_t (&sbits)[4]) {
     const int l = lane_id(), c = l >> 4, li = l & 15;
     uint4 bq[4][4];
     float sc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int col = 64 * wn + 16 * j + li;
+        const int col = WN * wave_id() + 16 * j + li;
         dequant_b(Bs[col * 4 + (c ^ ((col >> 2) & 3))], bq[j]);
         sc[j] = 16.0f * fp16_bits_to_f32((uint16_t)sbits[j]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int row = 128 * wm + 16 * i + li;
+        const int row = 16 * i + li;
         uint4 af[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) af[s] = As[row * SLOTS + ((4 * c + s) ^ li)];
@@ -118,25 +145,36 @@ EM_DEV void pf_compute(floatx4 (&acc)[8][4], const uint4* As, const uint4* Bs, c
             t = mfma_bf16(af[1], bq[j][1], t);
             t = mfma_bf16(af[2], bq[j][2], t);
             t = mfma_bf16(af[3], bq[j][3], t);
-            acc[i][j] = sc[j] * t + acc[i][j];
+            acc[i][j] = fma4(sc[j], t, acc[i][j]);
         }
     }
 }
 
-EM_DEV void pf_fetch_s(uint32_t (&sb)[4], const uint16_t* srow0, size_t sstride, int gq, int k0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sb[j] = srow0[(size_t)(16 * j) * sstride + k0 / gq];
-}
-
 }  // namespace
+
+// One K step in buffer set X of 3: compute step k (in X) while step k + 2 loads
+// into X's predecessor, then wait until only step k + 2's loads are in flight.
+#define PF_STEP(X, XN, K0)                                                        \
+    if ((K0) + 2 * BK < K) {                                                      \
+        pf_fetch(As##XN, Bs##XN, s##XN, src, gq, (K0) + 2 * BK);                  \
+        pf_compute(acc, As##X, Bs##X, s##X);                                      \
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF_STEP_VM));                       \
+    } else {                                                                      \
+        pf_compute(acc, As##X, Bs##X, s##X);                                      \
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                \
+    }                                                                             \
+    __syncthreads();                                                              \
+    if ((K0) + BK >= K) break;
 
 template <int MODE>
 __global__ void __launch_bounds__(256)
 pf_gemm(LayerArgs a) {
     __shared__ uint4 As0[BM * SLOTS];
     __shared__ uint4 As1[BM * SLOTS];
+    __shared__ uint4 As2[BM * SLOTS];
     __shared__ uint4 Bs0[BN * 4];
     __shared__ uint4 Bs1[BN * 4];
+    __shared__ uint4 Bs2[BN * 4];
     const int ntn = (MODE == PF_HS ? a.h : a.d) / BN;
     // XCD-aware order: XCD x = blockIdx % 8 takes tiles [x * per, (x + 1) * per)
     const int per = gridDim.x >> 3;
@@ -151,11 +189,11 @@ pf_gemm(LayerArgs a) {
     const uint8_t* W = MODE == PF_HS ? a.s_up : a.s_dn;
     const uint16_t* S = MODE == PF_HS ? a.s_up_s : a.s_dn_s;
     const int l = lane_id(), wv = wave_id(), c = l >> 4, li = l & 15;
-    const int wm = wv >> 1, wn = wv & 1;
+    const int wm = 0, wn = wv;
 
-    const uint8_t* Wt = W + ((size_t)t.g * N + t.n0) * (K / 2);          // the tile's 128 weight rows
-    const uint16_t* srow0 = S + ((size_t)t.g * N + t.n0 + 64 * wn + li) * (K / gq);
-    const size_t sstride = (size_t)(K / gq);
+    PfSrc src;
+    pf_src(src, A, (size_t)K, W + ((size_t)t.g * N + t.n0) * (K / 2), (size_t)(K / 2),
+           S + ((size_t)t.g * N + t.n0 + WN * wv + li) * (K / gq), (size_t)(K / gq), t.r0);
 
     floatx4 acc[8][4];
 #pragma unroll
@@ -163,33 +201,16 @@ pf_gemm(LayerArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
 
-    // ---- main loop: step k in buffers k % 2, the next step's loads in flight
-    uint32_t s0[4], s1[4];
-    pf_fetch_a(As0, A, (size_t)K, t.r0, t.r1, 0);
-    pf_fetch_b(Bs0, Wt, (size_t)(K / 2), 0);
-    pf_fetch_s(s0, srow0, sstride, gq, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    // ---- main loop: three buffer sets, loads two steps ahead of the math (K >= 3 BK)
+    uint32_t s0[4], s1[4], s2[4];
+    pf_fetch(As0, Bs0, s0, src, gq, 0);
+    pf_fetch(As1, Bs1, s1, src, gq, BK);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF_STEP_VM));
     __syncthreads();
-    for (int k0 = 0; k0 < K; k0 += 2 * BK) {
-        // even step: buffers 0
-        if (k0 + BK < K) {
-            pf_fetch_a(As1, A, (size_t)K, t.r0, t.r1, k0 + BK);
-            pf_fetch_b(Bs1, Wt, (size_t)(K / 2), k0 + BK);
-            pf_fetch_s(s1, srow0, sstride, gq, k0 + BK);
-        }
-        pf_compute(acc, As0, Bs0, s0, wm, wn);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (k0 + BK >= K) break;
-        // odd step: buffers 1
-        if (k0 + 2 * BK < K) {
-            pf_fetch_a(As0, A, (size_t)K, t.r0, t.r1, k0 + 2 * BK);
-            pf_fetch_b(Bs0, Wt, (size_t)(K / 2), k0 + 2 * BK);
-            pf_fetch_s(s0, srow0, sstride, gq, k0 + 2 * BK);
-        }
-        pf_compute(acc, As1, Bs1, s1, wm, wn);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    for (int k0 = 0; k0 < K; k0 += 3 * BK) {
+        PF_STEP(0, 2, k0)
+        PF_STEP(1, 0, k0 + BK)
+        PF_STEP(2, 1, k0 + 2 * BK)
     }
 
     // ---- LoRA branch: V[g] (bf16 [N][rL]) x the rounded LoRA input rows (bf16 [rows][rLp])
@@ -202,12 +223,12 @@ pf_gemm(LayerArgs a) {
             uint4 bv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int n = t.n0 + 64 * wn + 16 * j + li;
+                const int n = t.n0 + WN * wn + 16 * j + li;
                 bv[j] = kv ? ld16(V + (size_t)n * a.rL + kb + 8 * c) : zero_u4();
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int row = min(t.r0 + 128 * wm + 16 * i + li, t.r1 - 1);
+                const int row = min(t.r0 + 16 * i + li, t.r1 - 1);
                 const uint4 av = kv ? ld16(Z + (size_t)row * rLp + kb + 8 * c) : zero_u4();
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(av, bv[j], acc[i][j]);
@@ -228,13 +249,13 @@ pf_gemm(LayerArgs a) {
                 float sc[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const size_t n = (size_t)e * a.d + t.n0 + 64 * wn + 16 * j + li;
+                    const size_t n = (size_t)e * a.d + t.n0 + WN * wn + 16 * j + li;
                     dequant_b(ld16(a.b_dn + n * (a.r / 2) + (k0 >> 1) + 16 * c), bq[j]);
                     sc[j] = 16.0f * fp16_bits_to_f32(a.b_dn_s[n * (a.r / gq_r) + k0 / gq_r]);
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int rl = 128 * wm + 16 * i;                  // subtile rows [rl, rl + 16)
+                    const int rl = 16 * i;                  // subtile rows [rl, rl + 16)
                     if (rl + 16 <= p || rl >= q) continue;             // wave-uniform
                     const int row = rl + li;
                     const bool mine = row >= p && row < q;
@@ -248,7 +269,7 @@ pf_gemm(LayerArgs a) {
                         tt = mfma_bf16(af[1], bq[j][1], tt);
                         tt = mfma_bf16(af[2], bq[j][2], tt);
                         tt = mfma_bf16(af[3], bq[j][3], tt);
-                        acc[i][j] = sc[j] * tt + acc[i][j];
+                        acc[i][j] = fma4(sc[j], tt, acc[i][j]);
                     }
                 }
             }
@@ -261,9 +282,9 @@ pf_gemm(LayerArgs a) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int row = t.r0 + 128 * wm + 16 * i + 4 * c + v;
+            const int row = t.r0 + 16 * i + 4 * c + v;
             if (row >= t.r1) continue;
-            float* orow = out + (size_t)row * N + t.n0 + 64 * wn + li;
+            float* orow = out + (size_t)row * N + t.n0 + WN * wn + li;
 #pragma unroll
             for (int j = 0; j < 4; ++j) orow[16 * j] = acc[i][j][v];
         }
@@ -285,7 +306,7 @@ pf_gather_x(const uint16_t* __restrict__ x, const int32_t* __restrict__ ut_tok, 
 
 bool prefill_gemm_ok(int d, int h, int r, int rL, int gq) {
     return gq % KC == 0 && r % KC == 0 && rL % 8 == 0 && rL <= 32 && d % BN == 0 && h % BN == 0 &&
-           d % BK == 0 && h % BK == 0;
+           d >= 3 * BK && h >= 3 * BK;
 }
 
 hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, hipStream_t s) {
