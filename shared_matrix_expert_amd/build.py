@@ -48,9 +48,14 @@ def _flags():
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
+# Per-source code-generation options: the prefill GEMMs keep their MFMA
+# results in ordinary VGPRs (the scaled chunk sums are added by VALU FMAs).
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

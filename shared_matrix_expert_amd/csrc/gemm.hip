@@ -427,7 +427,12 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
         launch_gemm<M_HS>(a, a.max_gtiles_u, a.h, s, "gemm_shared_up");
     }
     // a5 + a7: delta up, sum, SiLU, R3
-    launch_gemm<M_ACT>(a, a.max_etiles, a.h, s, "gemm_delta_up_act");
+    if (a.pf && a.r == KC && a.h % 256 == 0) {
+        const hipError_t e = launch_act(a, s);
+        if (e != hipSuccess) return e;
+    } else {
+        launch_gemm<M_ACT>(a, a.max_etiles, a.h, s, "gemm_delta_up_act");
+    }
     // a9 / a10 inputs: R4 (per row), R5 (per row)
     launch_gemm<M_Z2>(a, a.max_etiles, a.r, s, "gemm_z2");
     prof_begin(s);

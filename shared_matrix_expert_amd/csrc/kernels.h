@@ -113,6 +113,7 @@ constexpr int kPfSpareRows = 128;    // readable rows past the end of xg and act
 bool prefill_gemm_ok(int d, int h, int r, int rL, int gq);
 hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, hipStream_t s);
 hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);
+hipError_t launch_act(const LayerArgs& a, hipStream_t s);     // needs r == 128, h % 256 == 0
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
                            hipStream_t stream);

@@ -290,6 +290,86 @@ pf_gemm(LayerArgs a) {
         }
 }
 
+// Delta up, sum and activation for large batches (steps a5 and a7, r = 128):
+// a[row] = RNbf16(SiLU(Hs[u(row)] + 16 s * (B_up[e] . z1[row]))) for a 64-row
+// task of expert e and 256 columns.  The z1 fragments are loaded once and
+// serve four 64-column blocks; each block's 64 x 64 fp32 result goes through
+// LDS so that Hs is read and a written as whole row segments (256 and 128
+// bytes per row) instead of 64- and 32-byte pieces.
+__global__ void __launch_bounds__(256)
+pf_act(LayerArgs a) {
+    __shared__ float ot[64][64 + 4];
+    const int b = blockIdx.x;
+    const int s_e = [&] {                                // expert of this 64-row tile
+        const int32_t* tiles = a.db.etile;
+        if (b >= tiles[a.E]) return -1;
+        int lo = 0, hi = a.E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tiles[mid] <= b) lo = mid; else hi = mid;
+        }
+        return lo;
+    }();
+    if (s_e < 0) return;
+    const int rbeg = a.db.eoff[s_e] + (b - a.db.etile[s_e]) * 64;
+    const int rows = min(a.db.eoff[s_e + 1] - rbeg, 64);
+    if (rows <= 0) return;
+    const int l = lane_id(), wv = wave_id(), c = l >> 4, li = l & 15;
+    const int n0 = blockIdx.y * 256;
+
+    uint4 af[4][4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+        const int r = rbeg + min(16 * ms + li, rows - 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) af[ms][s] = ld16(a.z1 + (size_t)r * KC + 32 * c + 8 * s);
+    }
+    const int tr = threadIdx.x >> 2, tq = threadIdx.x & 3;   // epilogue: row, 16-column quarter
+    const int u = tr < rows ? a.db.row_u[rbeg + tr] : 0;
+    for (int cb = 0; cb < 4; ++cb) {
+        const size_t n = (size_t)s_e * a.h + n0 + 64 * cb + 16 * wv + li;
+        const uint4 raw = ld16(a.b_up + n * (KC / 2) + 16 * c);
+        const uint32_t sb = a.b_up_s[n];
+        floatx4 acc[4];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) acc[ms] = zero4();
+        mac_fast<4>(acc, af, raw, sb);
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ot[16 * ms + 4 * c + v][16 * wv + li] = acc[ms][v];
+        __syncthreads();
+        if (tr < rows) {
+            const int col = n0 + 64 * cb + 16 * tq;
+            const float4* hp = reinterpret_cast<const float4*>(a.hs + (size_t)u * a.h + col);
+            uint32_t ob[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 hv = hp[q];
+                const float* o = &ot[tr][16 * tq + 4 * q];
+                const uint32_t b0 = f32_to_bf16_rne(silu(o[0] + hv.x));
+                const uint32_t b1 = f32_to_bf16_rne(silu(o[1] + hv.y));
+                const uint32_t b2 = f32_to_bf16_rne(silu(o[2] + hv.z));
+                const uint32_t b3 = f32_to_bf16_rne(silu(o[3] + hv.w));
+                ob[2 * q] = b0 | (b1 << 16);
+                ob[2 * q + 1] = b2 | (b3 << 16);
+            }
+            uint4* ap = reinterpret_cast<uint4*>(a.act + (size_t)(rbeg + tr) * a.h + col);
+            ap[0] = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+            ap[1] = make_uint4(ob[4], ob[5], ob[6], ob[7]);
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_act(const LayerArgs& a, hipStream_t s) {
+    dim3 grid(a.max_etiles, a.h / 256);
+    prof_begin(s);
+    pf_act<<<grid, 256, 0, s>>>(a);
+    prof_end(s, "pf_delta_up_act");
+    return hipGetLastError();
+}
+
 // xg[u] = x[ut_tok[u]]: the activation rows of every group's distinct tokens,
 // contiguous per group, 16 bytes per thread.
 __global__ void __launch_bounds__(256)
