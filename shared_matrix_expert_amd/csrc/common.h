@@ -89,6 +89,12 @@ EM_DEV floatx4 fma4(float s, floatx4 t, floatx4 acc) {
 EM_DEV int lane_id() { return threadIdx.x & (kWave - 1); }
 EM_DEV int wave_id() { return threadIdx.x >> 6; }
 
-EM_DEV float silu(float v) { return v / (1.0f + expf(-v)); }
+// SiLU(v) = v / (1 + e^-v) from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32, each within about 1 ulp): a few fp32 ulps from the
+// exact value, far inside the bf16 rounding that follows it.
+EM_DEV float silu(float v) {
+    const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 }  // namespace em

@@ -28,6 +28,7 @@
 namespace em {
 
 constexpr int DEC_RMAX = 1024;
+constexpr int HS_RB = 2;          // 64-column blocks per shared-up workgroup (h / 64 a multiple)
 constexpr int DEPTH = 4;
 
 // ------------------------------------------------------------------ routing views --
@@ -213,7 +214,7 @@ dec_up(DecodeArgs a) {
     const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
     int b = blockIdx.x;
     const int nbh = a.h / 64;
-    const int nHS = a.G * nbh;
+    const int nHS = a.G * (nbh / HS_RB);
     const int nbr = (a.r + 63) / 64;
     const int nZ1 = a.nxmax * a.S1 * nbr;
     const int ks = a.d / a.S1;
@@ -222,44 +223,56 @@ dec_up(DecodeArgs a) {
     constexpr bool lds = LDSP;                         // workgroup streaming through LDS
 
     if (b < nHS) {
-        // ---- shared up for the distinct tokens of group g, 64 columns
-        const int g = b / nbh, nb = b % nbh;
+        // ---- shared up for the distinct tokens of group g, HS_RB blocks of 64 columns
+        const int g = b / (nbh / HS_RB), nb0 = (b % (nbh / HS_RB)) * HS_RB;
         const int nrows = rv_group_tokens(v, g, a.T, a.k, a.P);
         if (nrows == 0) return;
-        const int nsub = (nrows + 15) >> 4;
-        const int ncol = nb * 64 + wv * 16 + li;
-        floatx4 acc[NS];
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
         if constexpr (lds) {
             if ((int)threadIdx.x < 16 * NS)
                 arow_l[threadIdx.x] = v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0];
             __syncthreads();
-            const size_t r0 = (size_t)g * a.h + nb * 64;
+            const size_t r0 = (size_t)g * a.h + nb0 * 64;
             const StreamArgs sa{a.s_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.s_up_s + r0 * (a.d / gq),
                                 (size_t)(a.d / gq), 64, gq, a.x, (size_t)a.d};
-            stream_gemm<NS, KB>(acc, L, sa, arow_l, nrows, 0, a.d);
+            stream_gemm_rows<NS, KB>(L, sa, (size_t)64 * (a.d / 2), (size_t)64 * (a.d / gq), HS_RB, arow_l, nrows,
+                                     0, a.d, [&](int rb, const floatx4 (&acc)[NS]) {
+                const int ncol = (nb0 + rb) * 64 + wv * 16 + li;
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = ms * 16 + 4 * c + q;
+                        if (i < nrows) a.hs[((size_t)v.rtok[i] * a.G + g) * a.h + ncol] = acc[ms][q];
+                    }
+            });
         } else {
-            const uint8_t* wrow = a.s_up + ((size_t)g * a.h + ncol) * (a.d / 2);
-            const uint16_t* srow = a.s_up_s + ((size_t)g * a.h + ncol) * (a.d / gq);
-            const uint16_t* arow[NS];
-            bool av[NS];
+            for (int rb = 0; rb < HS_RB; ++rb) {
+                const int ncol = (nb0 + rb) * 64 + wv * 16 + li;
+                floatx4 acc[NS];
 #pragma unroll
-            for (int ms = 0; ms < NS; ++ms) {
-                const int i = ms * 16 + li;
-                av[ms] = i < nrows;
-                arow[ms] = a.x + (size_t)v.rtok[av[ms] ? i : 0] * a.d;
+                for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+                const int nsub = (nrows + 15) >> 4;
+                const uint8_t* wrow = a.s_up + ((size_t)g * a.h + ncol) * (a.d / 2);
+                const uint16_t* srow = a.s_up_s + ((size_t)g * a.h + ncol) * (a.d / gq);
+                const uint16_t* arow[NS];
+                bool av[NS];
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms) {
+                    const int i = ms * 16 + li;
+                    av[ms] = i < nrows;
+                    arow[ms] = a.x + (size_t)v.rtok[av[ms] ? i : 0] * a.d;
+                }
+                if (fast) stream_i4_fast<NS, DEPTH>(acc, wrow, srow, 0, a.d, gq, arow, c);
+                else stream_i4<NS, DEPTH>(acc, wrow, srow, true, 0, a.d, a.d, gq, arow, av, nsub, c);
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = ms * 16 + 4 * c + q;
+                        if (i < nrows) a.hs[((size_t)v.rtok[i] * a.G + g) * a.h + ncol] = acc[ms][q];
+                    }
             }
-            if (fast) stream_i4_fast<NS, DEPTH>(acc, wrow, srow, 0, a.d, gq, arow, c);
-            else stream_i4<NS, DEPTH>(acc, wrow, srow, true, 0, a.d, a.d, gq, arow, av, nsub, c);
         }
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i = ms * 16 + 4 * c + q;
-                if (i < nrows) a.hs[((size_t)v.rtok[i] * a.G + g) * a.h + ncol] = acc[ms][q];
-            }
         return;
     }
     b -= nHS;
@@ -602,10 +615,49 @@ dec_act_direct(DecodeArgs a) {
 }
 
 // Activation kernel with every weight block staged through LDS (r = 128,
-// quant groups a multiple of 128, 256 columns per workgroup): the expert's B_up rows of
-// these columns (256 x 64 B, contiguous), its A_dn columns (128 rows x 128 B)
-// and the group's U_dn columns are loaded coalesced and up front.
+// quant groups a multiple of 128).  A workgroup takes one expert and ACT_CPB
+// consecutive blocks of 256 columns: per block the expert's B_up rows of those
+// columns (256 x 64 B, contiguous), its A_dn columns (128 rows x 128 B) and the
+// group's U_dn columns are loaded coalesced, the next block's loads issued
+// before this block's arithmetic.  The R4 / R5 partial sums stay in registers
+// over the workgroup's blocks, so each expert leaves h / (256 ACT_CPB) partials.
 constexpr int CB_L = 256;
+constexpr int ACT_CPB = 4;
+constexpr int ACT_RL = 16;        // LoRA rank bound of this kernel (its U_dn block)
+
+// One 256-column block's operands: the B_up share (phase 1) and the A_dn and
+// U_dn shares (phase 2), fetched separately so that each is in flight while
+// the other phase computes.
+struct ActUp {
+    uint4 rb[4];
+    uint32_t bs;
+};
+struct ActDn {
+    uint4 ra[4], ru[4];
+    uint32_t as2;
+};
+
+EM_DEV void act_fetch_up(ActUp& r, const DecodeArgs& a, int e, int cb) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r.rb[i] = ld16(a.b_up + ((size_t)e * a.h + cb * CB_L) * (KC / 2) + 16 * (tid + 256 * i));
+    r.bs = a.b_up_s[(size_t)e * a.h + cb * CB_L + tid];
+}
+
+EM_DEV void act_fetch_dn(ActDn& r, const DecodeArgs& a, int e, int g, int cb) {
+    const int tid = threadIdx.x;
+    const int gq_h = min(a.gq, a.h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = tid + 256 * i;
+        const int row = q >> 3, seg = q & 7;
+        r.ra[i] = ld16(a.a_dn + ((size_t)e * KC + row) * (a.h / 2) + cb * (CB_L / 2) + 16 * seg);
+        const int urow = q >> 5, useg = q & 31;
+        r.ru[i] = ld16(a.ld_u + ((size_t)g * a.rL + min(urow, a.rL - 1)) * a.h + cb * CB_L + 8 * useg);
+    }
+    r.as2 = a.a_dn_s[((size_t)e * KC + (tid >> 1)) * (a.h / gq_h) + (cb * CB_L + KC * (tid & 1)) / gq_h];
+}
 
 template <int NS>
 __global__ void __launch_bounds__(256)
@@ -614,36 +666,24 @@ dec_act(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t zs[16 * NS][KC + 8];
     __shared__ __attribute__((aligned(16))) uint16_t zls[16 * NS][ZL_W];
     __shared__ __attribute__((aligned(16))) uint16_t as_[16 * NS][CB_L + 8];
-    __shared__ uint4 wb[CB_L * 5];          // B_up block [256][5] or A_dn block [128][9]
-    __shared__ uint4 ub[32 * 33];            // U_dn block [rL][33]
+    __shared__ uint4 wb[CB_L * 5];           // B_up block [256][5], then A_dn block [128][9]
+    __shared__ uint4 ub[ACT_RL * 33];        // U_dn block [rL][33]
     __shared__ uint16_t bsc[CB_L];
     __shared__ uint16_t asc[KC][2];
     rv_load(v, a.idx, a.R);
-    const int xi = blockIdx.x / a.ncb2, cb = blockIdx.x % a.ncb2;
+    const int nw = a.ncb2 / ACT_CPB;                          // workgroups per expert
+    const int xi = blockIdx.x / nw, cw = blockIdx.x % nw;
     const int e = rv_distinct_expert(v, a.R, a.E, xi);
     if (e < 0) return;
     const int nrows = rv_expert_rows(v, e, a.T, a.k);
     const int g = e / a.P;
     const int tid = threadIdx.x;
     const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
-    const int gq_h = min(a.gq, a.h);
 
-    // ---- issue every global load of the block first
-    uint4 rb[4], ra[4], ru[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = tid + 256 * i;
-        rb[i] = ld16(a.b_up + ((size_t)e * a.h + cb * CB_L) * (KC / 2) + 16 * q);
-        const int row = q >> 3, seg = q & 7;
-        ra[i] = ld16(a.a_dn + ((size_t)e * KC + row) * (a.h / 2) + cb * (CB_L / 2) + 16 * seg);
-        const int urow = q >> 5, useg = q & 31;
-        ru[i] = ld16(a.ld_u + ((size_t)g * a.rL + min(urow, a.rL - 1)) * a.h + cb * CB_L + 8 * useg);
-    }
-    const uint16_t bs = a.b_up_s[(size_t)e * a.h + cb * CB_L + tid];
-    const uint16_t as2 = a.a_dn_s[((size_t)e * KC + (tid >> 1)) * (a.h / gq_h) + (cb * CB_L + KC * (tid & 1)) / gq_h];
-    const int col0 = cb * CB_L + wv * 64;
-    uint4 vb[4];
-    float hv[4][NS][4];
+    ActUp ru_;
+    ActDn rd_;
+    act_fetch_up(ru_, a, e, cw * ACT_CPB);
+    act_fetch_dn(rd_, a, e, g, cw * ACT_CPB);
     int tq[NS][4];
 #pragma unroll
     for (int ms = 0; ms < NS; ++ms)
@@ -652,16 +692,6 @@ dec_act(DecodeArgs a) {
             const int i = ms * 16 + 4 * c + q;
             tq[ms][q] = v.rtok[i < nrows ? i : 0];
         }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int ncol = col0 + nt * 16 + li;
-        const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
-        vb[nt] = 8 * c < a.rL ? t : zero_u4();
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
-    }
 
     // ---- R1, R2: finish the split-K sums in slice order and round to bf16
     for (int i = tid; i < 16 * NS * (KC + 8); i += 256) {
@@ -682,98 +712,133 @@ dec_act(DecodeArgs a) {
         zls[row][col] = (uint16_t)f32_to_bf16_rne(ordered_sum(
             a.zlp + ((size_t)v.rtok[row] * a.G + g) * a.rLp + col, 4 * a.S1, (size_t)a.T * a.G * a.rLp));
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = tid + 256 * i;
-        wb[(q >> 2) * 5 + (q & 3)] = rb[i];
-    }
-    bsc[tid] = bs;
-    __syncthreads();
 
-    // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h))
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int lrow = wv * 64 + nt * 16 + li;
-        const int ncol = cb * CB_L + lrow;
-        floatx4 acc[NS];
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
-        uint4 af[NS][4];
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
-        mac_fast<NS>(acc, af, wb[lrow * 5 + c], bsc[lrow]);
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms)
-            acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt], acc[ms]);
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i = ms * 16 + 4 * c + q;
-                uint16_t ab = 0;
-                if (i < nrows) {
-                    ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
-                    a.act[(size_t)v.rows[i] * a.h + ncol] = ab;
-                }
-                as_[i][lrow] = ab;
-            }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = tid + 256 * i;
-        wb[(q >> 3) * 9 + (q & 7)] = ra[i];
-        if ((q >> 5) < a.rL) ub[(q >> 5) * 33 + (q & 31)] = ru[i];
-    }
-    asc[tid >> 1][tid & 1] = as2;
-    __syncthreads();
-
-    // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows
     const int N2 = KC + ((a.rL + 15) & ~15);
-    for (int nt2 = wv; nt2 < N2 / 16; nt2 += 4) {
-        const int n2 = nt2 * 16 + li;
-        floatx4 acc[NS];
+    floatx4 z2acc[3][NS];                                     // this wave's R4 / R5 tiles nt2 = wv + 4 t
 #pragma unroll
-        for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
-        if (nt2 * 16 < KC) {
+    for (int t = 0; t < 3; ++t)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                uint4 af[NS][4];
+        for (int ms = 0; ms < NS; ++ms) z2acc[t][ms] = zero4();
+
+    for (int blk = 0; blk < ACT_CPB; ++blk) {
+        const int cb = cw * ACT_CPB + blk;
+        const int col0 = cb * CB_L + wv * 64;
+        uint4 vb[4];
+        float hv[4][NS][4];
 #pragma unroll
-                for (int ms = 0; ms < NS; ++ms)
+        for (int nt = 0; nt < 4; ++nt) {
+            const int ncol = col0 + nt * 16 + li;
+            const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
+            vb[nt] = 8 * c < a.rL ? t : zero_u4();
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
-                mac_fast<NS>(acc, af, wb[n2 * 9 + u * 4 + c], asc[n2][u]);
-            }
-        } else {
-            const int cl = n2 - KC;
-            const bool nvalid = cl < a.rL;
+            for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
-            for (int st = 0; st < CB_L / 32; ++st) {
-                const uint4 bv = nvalid ? ub[cl * 33 + st * 4 + c] : zero_u4();
+                for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
+        }
+        // this block's B_up into LDS; the next block's B_up loads go out at once
 #pragma unroll
-                for (int ms = 0; ms < NS; ++ms)
-                    acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]), bv, acc[ms]);
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + 256 * i;
+            wb[(q >> 2) * 5 + (q & 3)] = ru_.rb[i];
+        }
+        bsc[tid] = (uint16_t)ru_.bs;
+        __syncthreads();
+        if (blk + 1 < ACT_CPB) act_fetch_up(ru_, a, e, cb + 1);
+
+        // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h))
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int lrow = wv * 64 + nt * 16 + li;
+            const int ncol = cb * CB_L + lrow;
+            floatx4 acc[NS];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+            uint4 af[NS][4];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
+            mac_fast<NS>(acc, af, wb[lrow * 5 + c], bsc[lrow]);
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+                acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt], acc[ms]);
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = ms * 16 + 4 * c + q;
+                    uint16_t ab = 0;
+                    if (i < nrows) {
+                        ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
+                        a.act[(size_t)v.rows[i] * a.h + ncol] = ab;
+                    }
+                    as_[i][lrow] = ab;
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + 256 * i;
+            wb[(q >> 3) * 9 + (q & 7)] = rd_.ra[i];
+            if ((q >> 5) < a.rL) ub[(q >> 5) * 33 + (q & 31)] = rd_.ru[i];
+        }
+        asc[tid >> 1][tid & 1] = (uint16_t)rd_.as2;
+        __syncthreads();
+        if (blk + 1 < ACT_CPB) act_fetch_dn(rd_, a, e, g, cb + 1);
+
+        // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int nt2 = wv + 4 * t;
+            if (nt2 >= N2 / 16) break;
+            const int n2 = nt2 * 16 + li;
+            if (nt2 * 16 < KC) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    uint4 af[NS][4];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
+                    mac_fast<NS>(z2acc[t], af, wb[n2 * 9 + u * 4 + c], asc[n2][u]);
+                }
+            } else {
+                const int cl = n2 - KC;
+                const bool nvalid = cl < a.rL;
+#pragma unroll
+                for (int st = 0; st < CB_L / 32; ++st) {
+                    const uint4 bv = nvalid ? ub[cl * 33 + st * 4 + c] : zero_u4();
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+                        z2acc[t][ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]),
+                                                 bv, z2acc[t][ms]);
+                }
             }
         }
+        __syncthreads();
+    }
+
+    // ---- this workgroup's partial R4 / R5 inputs; the last of the expert's adds them in order
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        const int nt2 = wv + 4 * t;
+        if (nt2 >= N2 / 16) break;
+        const int n2 = nt2 * 16 + li;
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = ms * 16 + 4 * c + q;
-                if (i < nrows) st_agent(&a.z2p[((size_t)cb * a.R + v.rows[i]) * N2 + n2], acc[ms][q]);
+                if (i < nrows) st_agent(&a.z2p[((size_t)cw * a.R + v.rows[i]) * N2 + n2], z2acc[t][ms][q]);
             }
     }
-
-    // ---- the last column block of expert e adds the partials in block order
-    if (!arrive_last(v, &a.cnt_e[e], (uint32_t)a.ncb2)) return;
+    if (!arrive_last(v, &a.cnt_e[e], (uint32_t)nw)) return;
     for (int i = tid; i < nrows * N2; i += 256) {
         const int row = i / N2, n2 = i % N2;
         const int slot = v.rows[row];
-        const float sum = ordered_sum_agent(a.z2p + (size_t)slot * N2 + n2, a.ncb2, (size_t)a.R * N2);
+        const float sum = ordered_sum_agent(a.z2p + (size_t)slot * N2 + n2, nw, (size_t)a.R * N2);
         const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum);
         if (n2 < KC) a.z2[(size_t)slot * KC + n2] = bits;
         else if (n2 - KC < a.rL) a.zl2[(size_t)slot * a.rLp + (n2 - KC)] = bits;
@@ -974,13 +1039,13 @@ dec_down(DecodeArgs a) {
 template <int NS, bool LDSP>
 static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
     const int nbh = a.h / 64, nbr = (a.r + 63) / 64;
-    const int g1 = a.G * nbh + a.nxmax * a.S1 * nbr + a.G * a.S1;
+    const int g1 = a.G * (nbh / HS_RB) + a.nxmax * a.S1 * nbr + a.G * a.S1;
     prof_begin(s);
     dec_up<NS, LDSP><<<g1, 256, 0, s>>>(a);
     prof_end(s, "dec_up");
     prof_begin(s);
     if (LDSP) {
-        dec_act<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
+        dec_act<NS><<<a.nxmax * (a.ncb2 / ACT_CPB), 256, 0, s>>>(a);
         prof_end(s, "dec_act");
     } else {
         dec_act_direct<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
@@ -1009,7 +1074,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 bool decode_lds_ok(int T, int d, int h, int r, int rL, int gq, int S1) {
     const int ns = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
     const int nsd = decode_ns_down(T);
-    return gq % KC == 0 && r == KC && rL % 8 == 0 && rL <= 32 && h % CB_L == 0 &&
+    return gq % KC == 0 && r == KC && rL % 8 == 0 && rL <= ACT_RL && h % (CB_L * ACT_CPB) == 0 &&
            (d / S1) % (512 / ns) == 0 && h % (512 / nsd) == 0;
 }
 

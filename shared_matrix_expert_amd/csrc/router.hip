@@ -14,64 +14,66 @@
 namespace em {
 
 // -------------------------------------------------------------- small batches ----
-// A workgroup of 4 waves takes 4 experts and up to 4 tokens: the tokens' rows
-// are staged once in LDS, each wave streams one expert's weight row (all of a
-// 4096-element block's loads issued before the arithmetic) and accumulates the
-// exact bf16 products in float64.  The 4 partial sums per lane are reduced
-// with a fixed butterfly, so the result is reproducible (and exact).
-constexpr int RS_TOK = 4;
-constexpr int RS_BLK = 4096;
+// A workgroup of 4 waves takes 2 experts and up to 8 tokens: the tokens' rows
+// are staged once in LDS, waves 2e and 2e + 1 stream the two halves of expert
+// e's weight row (all loads issued before the arithmetic) and accumulate the
+// exact bf16 products in float64.  Lane sums are reduced with a fixed
+// butterfly and the two halves added through LDS, so the result is
+// reproducible (and exact).  A verify batch reads the router weights once,
+// spread over E/2 workgroups.
+constexpr int RS_TOK = 8;
+constexpr int RS_D = 4096;                // largest d of this path
 
 __global__ void __launch_bounds__(256)
 router_logits_small(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                     const float* __restrict__ bias, float* __restrict__ logits,
                     int T, int d, int E) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[RS_TOK][RS_BLK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[RS_TOK][RS_D];
+    __shared__ double part[2][RS_TOK];
     const int lane = lane_id(), wv = wave_id();
     const int ntg = (T + RS_TOK - 1) / RS_TOK;
     const int tg = blockIdx.x % ntg;
-    const int e = (blockIdx.x / ntg) * 4 + wv;
+    const int e = (blockIdx.x / ntg) * 2 + (wv >> 1);
+    const int half = wv & 1;
     const int t0 = tg * RS_TOK;
     const int nt = min(RS_TOK, T - t0);
-    double acc[RS_TOK] = {0.0, 0.0, 0.0, 0.0};
-    const uint16_t* wrow = wr + (size_t)(e < E ? e : 0) * d;
-    for (int kb = 0; kb < d; kb += RS_BLK) {
-        const int kn = min(RS_BLK, d - kb);
-        __syncthreads();
-        for (int i = threadIdx.x * 8; i < RS_TOK * kn; i += 256 * 8) {
-            const int t = i / kn, kk = i % kn;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (t < nt) v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * d + kb + kk);
-            *reinterpret_cast<uint4*>(&xs[t][kk]) = v;
-        }
-        uint4 wv8[8];
+    const int hd = d / 2;                          // elements per half (a multiple of 64)
+    for (int i = threadIdx.x * 8; i < RS_TOK * d; i += 256 * 8) {
+        const int t = i / d, kk = i % d;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (t < nt) v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * d + kk);
+        *reinterpret_cast<uint4*>(&xs[t][kk]) = v;
+    }
+    const uint16_t* wrow = wr + (size_t)(e < E ? e : 0) * d + half * hd;
+    uint4 wv8[RS_D / 2 / 512];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kk = (i * kWave + lane) * 8;
-            wv8[i] = (e < E && kk < kn) ? *reinterpret_cast<const uint4*>(wrow + kb + kk)
-                                        : make_uint4(0u, 0u, 0u, 0u);
-        }
-        __syncthreads();
+    for (int i = 0; i < RS_D / 2 / 512; ++i) {
+        const int kk = (i * kWave + lane) * 8;
+        wv8[i] = (e < E && kk < hd) ? *reinterpret_cast<const uint4*>(wrow + kk) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    double acc[RS_TOK];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kk = (i * kWave + lane) * 8;
-            if (kk >= kn) break;
-            const uint32_t wu[4] = {wv8[i].x, wv8[i].y, wv8[i].z, wv8[i].w};
-            double wd[8];
+    for (int t = 0; t < RS_TOK; ++t) acc[t] = 0.0;
+#pragma unroll
+    for (int i = 0; i < RS_D / 2 / 512; ++i) {
+        const int kk = (i * kWave + lane) * 8;
+        if (kk >= hd) break;
+        const uint32_t wu[4] = {wv8[i].x, wv8[i].y, wv8[i].z, wv8[i].w};
+        double wd[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wd[2 * q] = (double)bf16_to_f32(wu[q] & 0xFFFFu);
+            wd[2 * q + 1] = (double)bf16_to_f32(wu[q] >> 16);
+        }
+#pragma unroll
+        for (int t = 0; t < RS_TOK; ++t) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(&xs[t][half * hd + kk]);
+            const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                wd[2 * q] = (double)bf16_to_f32(wu[q] & 0xFFFFu);
-                wd[2 * q + 1] = (double)bf16_to_f32(wu[q] >> 16);
-            }
-#pragma unroll
-            for (int t = 0; t < RS_TOK; ++t) {
-                const uint4 xv = *reinterpret_cast<const uint4*>(&xs[t][kk]);
-                const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[t] = fma((double)bf16_to_f32(xu[q] & 0xFFFFu), wd[2 * q], acc[t]);
-                    acc[t] = fma((double)bf16_to_f32(xu[q] >> 16), wd[2 * q + 1], acc[t]);
-                }
+                acc[t] = fma((double)bf16_to_f32(xu[q] & 0xFFFFu), wd[2 * q], acc[t]);
+                acc[t] = fma((double)bf16_to_f32(xu[q] >> 16), wd[2 * q + 1], acc[t]);
             }
         }
     }
@@ -82,12 +84,20 @@ router_logits_small(const uint16_t* __restrict__ x, const uint16_t* __restrict__
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
         acc[t] = v;
     }
-    if (e < E && lane < nt) {
+    if (half == 1 && lane < RS_TOK) {
         double v = acc[0];
 #pragma unroll
         for (int t = 1; t < RS_TOK; ++t)
             if (t == lane) v = acc[t];
-        float l = (float)v;
+        part[wv >> 1][lane] = v;
+    }
+    __syncthreads();
+    if (half == 0 && e < E && lane < nt) {
+        double v = acc[0];
+#pragma unroll
+        for (int t = 1; t < RS_TOK; ++t)
+            if (t == lane) v = acc[t];
+        float l = (float)(v + part[wv >> 1][lane]);
         if (bias) l = l + bias[e];
         logits[(size_t)(t0 + lane) * E + e] = l;
     }
@@ -170,11 +180,40 @@ router_logits_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 }
 
 // -------------------------------------------------------------- top-k -----------
-// One wave per token.  Each lane keeps the best of its own logits; a round is a
-// wave-wide arg-max of those (larger logit, or equal logit and lower index),
-// after which only the winning lane rescans.  Then the softmax over the
+// One wave per token.  A candidate is the 64-bit key (order-preserving bits of
+// the logit, ~index): the larger key is the larger logit, or the equal logit
+// with the lower index.  Each lane keeps the best key among its own logits; a
+// round takes the wave-wide maximum with DPP row operations (no LDS), then
+// only the winning lane rescans its logits.  Then the softmax over the
 // selected logits in float64.
-EM_DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+EM_DEV uint64_t topk_key(float v, int i) {
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);     // order-preserving for non-NaN floats
+    if (v == 0.0f) u = 0x80000000u;                      // +0 and -0 tie
+    return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)i);
+}
+
+template <int CTRL, int ROW_MASK>
+EM_DEV uint64_t dpp_max_step(uint64_t x) {
+    const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > x ? o : x;
+}
+
+// Maximum key over the wave, the same value in every lane.
+EM_DEV uint64_t wave_max_key(uint64_t x) {
+    x = dpp_max_step<0xB1, 0xF>(x);      // quad_perm [1,0,3,2]
+    x = dpp_max_step<0x4E, 0xF>(x);      // quad_perm [2,3,0,1]
+    x = dpp_max_step<0x141, 0xF>(x);     // row_half_mirror
+    x = dpp_max_step<0x140, 0xF>(x);     // row_mirror: every lane holds its row's maximum
+    x = dpp_max_step<0x142, 0xA>(x);     // row_bcast:15 into rows 1 and 3
+    x = dpp_max_step<0x143, 0xC>(x);     // row_bcast:31 into rows 2 and 3: lane 63 holds the maximum
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
 
 __global__ void __launch_bounds__(256)
 router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
@@ -183,42 +222,32 @@ router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
     const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
     constexpr int MAXPER = 16;            // E <= 1024
-    float v[MAXPER];
+    uint64_t key[MAXPER];
     const float* row = logits + (size_t)t * E;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
         const int e = lane + kWave * i;
-        v[i] = (e < E) ? row[e] : -INFINITY;
+        key[i] = e < E ? topk_key(row[e], e) : 0ull;
     }
-    uint32_t taken = 0;                   // bit i: element lane + 64 i already selected
-    auto local_best = [&](float& bv, int& bi) {
-        bv = -INFINITY;
-        bi = 0x7FFFFFFF;
+    auto local_best = [&]() {
+        uint64_t b = 0ull;
 #pragma unroll
-        for (int i = 0; i < MAXPER; ++i) {
-            const int e = lane + kWave * i;
-            if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
-        }
+        for (int i = 0; i < MAXPER; ++i) b = key[i] > b ? key[i] : b;
+        return b;
     };
-    float lv;
-    int lidx;
-    local_best(lv, lidx);
-    float sel0 = 0.f, my_sel = 0.f;
+    uint64_t best = local_best();
+    float my_sel = 0.f, sel0 = 0.f;
     int my_idx = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = lv;
-        int bi = lidx;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
+        const uint64_t w = wave_max_key(best);
+        const int bi = (int)(~(uint32_t)w);
+        const uint32_t hb = (uint32_t)(w >> 32);
+        const float bv = __uint_as_float((hb & 0x80000000u) ? (hb & 0x7FFFFFFFu) : ~hb);
         if (j == 0) sel0 = bv;
         if (lane == j) { my_sel = bv; my_idx = bi; }
         if ((bi & (kWave - 1)) == lane) {
-            taken |= 1u << (bi / kWave);
-            local_best(lv, lidx);
+            key[bi / kWave] = 0ull;       // taken
+            best = local_best();
         }
     }
     double u = (lane < k) ? exp((double)my_sel - (double)sel0) : 0.0;
@@ -236,10 +265,10 @@ router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias,
                          float* logits, int32_t* idx, float* w, int T, int d, int E, int k,
                          hipStream_t stream) {
-    if (T <= 16) {
+    if (T <= 2 * RS_TOK && d <= RS_D && d % 128 == 0) {
         const int ntg = (T + RS_TOK - 1) / RS_TOK;
         prof_begin(stream);
-        router_logits_small<<<((E + 3) / 4) * ntg, 256, 0, stream>>>(x, wr, bias, logits, T, d, E);
+        router_logits_small<<<((E + 1) / 2) * ntg, 256, 0, stream>>>(x, wr, bias, logits, T, d, E);
         prof_end(stream, "router_logits_small");
     } else {
         dim3 grid((T + RT_TILE - 1) / RT_TILE, (E + RT_TILE - 1) / RT_TILE);

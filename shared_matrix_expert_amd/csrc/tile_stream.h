@@ -83,15 +83,17 @@ EM_DEV void stream_src(StreamSrc<NS, KB>& p, const StreamArgs& sa, const int* ar
     }
 }
 
-// Global -> registers for block [kb, kb + KB).
+// Global -> registers for block [kb, kb + KB); the weight and scale rows are
+// offset by woff bytes and soff elements (a later 64-row block).
 template <int NS, int KB>
-EM_DEV void stream_fetch(StreamRegs<NS, KB>& r, const StreamSrc<NS, KB>& p, int gq, int kb) {
+EM_DEV void stream_fetch(StreamRegs<NS, KB>& r, const StreamSrc<NS, KB>& p, int gq, int kb, size_t woff = 0,
+                         size_t soff = 0) {
     constexpr int NCH = KB / KC;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) r.w[i] = ld16(p.w[i] + (kb >> 1));
+    for (int i = 0; i < NCH; ++i) r.w[i] = ld16(p.w[i] + woff + (kb >> 1));
     // thread (row, chunk) = (tid / 4, tid % 4); chunks past NCH repeat the last
     const int ch = min((int)(threadIdx.x & 3), NCH - 1);
-    r.s = p.s[(kb + ch * KC) / gq];
+    r.s = p.s[soff + (kb + ch * KC) / gq];
 #pragma unroll
     for (int i = 0; i < NS * KB / 128; ++i) r.a[i] = ld16(p.a[i] + kb);
 }
@@ -187,6 +189,72 @@ EM_DEV void stream_gemm(floatx4 (&acc)[NS], StreamLds<NS, KB>& L, const StreamAr
         stream_compute<NS, KB>(acc, L, 1);
     } else {
         stream_compute<NS, KB>(acc, L, 0);
+    }
+    __syncthreads();
+}
+
+// Several 64-row weight blocks against the same activation rows: row block rb
+// (0 <= rb < nrb) uses the weight rows sa.w + rb * rb_w (bytes) and scales
+// sa.s + rb * rb_s (elements).  All (rb, K-block) steps run through one
+// pipeline in (rb, kb) order, so the next row block's first loads overlap the
+// current one's last blocks and the workgroup's start-up is paid once.
+// epi(rb, acc) runs after row block rb's last step; acc is then reset.  Every
+// thread of the workgroup must call this; it synchronises the workgroup.
+template <int NS, int KB, class Epi>
+EM_DEV void stream_gemm_rows(StreamLds<NS, KB>& L, const StreamArgs& sa, size_t rb_w, size_t rb_s, int nrb,
+                             const int* arow, int na, int k0, int k1, Epi&& epi) {
+    StreamSrc<NS, KB> p;
+    stream_src<NS, KB>(p, sa, arow, na);
+    const int nbk = (k1 - k0) / KB;
+    const int nb = nrb * nbk;
+    auto fetch = [&](StreamRegs<NS, KB>& r, int q) {
+        const int rb = q / nbk, kb = q - rb * nbk;
+        stream_fetch<NS, KB>(r, p, sa.gq, k0 + kb * KB, (size_t)rb * rb_w, (size_t)rb * rb_s);
+    };
+    floatx4 acc[NS];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+    auto compute = [&](int buf, int q) {
+        stream_compute<NS, KB>(acc, L, buf);
+        const int rb = q / nbk;
+        if (q - rb * nbk == nbk - 1) {
+            epi(rb, acc);
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+        }
+    };
+    StreamRegs<NS, KB> r0, r1;
+    fetch(r0, 0);
+    fetch(r1, nb > 1 ? 1 : 0);
+    stream_store<NS, KB>(L, 0, r0);
+    __syncthreads();
+    int b = 0;
+    for (; b + 3 < nb; b += 2) {
+        fetch(r0, b + 2);
+        compute(0, b);
+        stream_store<NS, KB>(L, 1, r1);
+        __syncthreads();
+        fetch(r1, b + 3);
+        compute(1, b + 1);
+        stream_store<NS, KB>(L, 0, r0);
+        __syncthreads();
+    }
+    if (b + 2 < nb) {
+        fetch(r0, b + 2);
+        compute(0, b);
+        stream_store<NS, KB>(L, 1, r1);
+        __syncthreads();
+        compute(1, b + 1);
+        stream_store<NS, KB>(L, 0, r0);
+        __syncthreads();
+        compute(0, b + 2);
+    } else if (b + 1 < nb) {
+        compute(0, b);
+        stream_store<NS, KB>(L, 1, r1);
+        __syncthreads();
+        compute(1, b + 1);
+    } else {
+        compute(0, b);
     }
     __syncthreads();
 }
