@@ -74,6 +74,47 @@ EM_DEV int rv_distinct_expert(RouteView& v, int R, int E, int xi) {
     return v.sel;
 }
 
+// Number of distinct experts that any slot selected (builds v.ebits).
+EM_DEV int rv_count_experts(RouteView& v, int R, int E) {
+    const int nw = (E + 31) >> 5;
+    if ((int)threadIdx.x < nw) v.ebits[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < R; i += blockDim.x) atomicOr(&v.ebits[v.idx[i] >> 5], 1u << (v.idx[i] & 31));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int n = 0;
+        for (int w = 0; w < nw; ++w) n += __popc(v.ebits[w]);
+        v.sel = n;
+    }
+    __syncthreads();
+    const int n = v.sel;
+    __syncthreads();
+    return n;
+}
+
+// The xi-th smallest selected expert (v.ebits built by rv_count_experts).
+EM_DEV int rv_nth_expert(RouteView& v, int E, int xi) {
+    if (threadIdx.x == 0) {
+        const int nw = (E + 31) >> 5;
+        int sel = -1, acc = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int pc = __popc(v.ebits[w]);
+            if (xi < acc + pc) {
+                uint32_t b = v.ebits[w];
+                for (int r = xi - acc; r > 0; --r) b &= b - 1u;
+                sel = w * 32 + __ffs(b) - 1;
+                break;
+            }
+            acc += pc;
+        }
+        v.sel = sel;
+    }
+    __syncthreads();
+    const int e = v.sel;
+    __syncthreads();
+    return e;
+}
+
 // Rows of expert e (one per token that chose it) in token order.
 EM_DEV int rv_expert_rows(RouteView& v, int e, int T, int k) {
     if (threadIdx.x < 64) {
@@ -615,14 +656,16 @@ dec_act_direct(DecodeArgs a) {
 }
 
 // Activation kernel with every weight block staged through LDS (r = 128,
-// quant groups a multiple of 128).  A workgroup takes one expert and ACT_CPB
-// consecutive blocks of 256 columns: per block the expert's B_up rows of those
-// columns (256 x 64 B, contiguous), its A_dn columns (128 rows x 128 B) and the
-// group's U_dn columns are loaded coalesced, the next block's loads issued
-// before this block's arithmetic.  The R4 / R5 partial sums stay in registers
-// over the workgroup's blocks, so each expert leaves h / (256 ACT_CPB) partials.
+// quant groups a multiple of 128).  The work items are (distinct expert, block
+// of 256 columns), expert-major, and a fixed grid of workgroups (all resident
+// at once) splits them into equal contiguous ranges, so a range spans at most
+// a few experts.  Per block the expert's B_up rows of those columns (256 x 64
+// B, contiguous), its A_dn columns (128 rows x 128 B) and the group's U_dn
+// columns are loaded coalesced, each phase's next-block loads issued before
+// the other phase's arithmetic.  A range keeps its R4 / R5 partial sums in
+// registers and stores them once; the expert's last range to arrive adds them
+// in block order.
 constexpr int CB_L = 256;
-constexpr int ACT_CPB = 4;
 constexpr int ACT_RL = 16;        // LoRA rank bound of this kernel (its U_dn block)
 
 // One 256-column block's operands: the B_up share (phase 1) and the A_dn and
@@ -660,7 +703,7 @@ EM_DEV void act_fetch_dn(ActDn& r, const DecodeArgs& a, int e, int g, int cb) {
 }
 
 template <int NS>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, NS == 1 ? 2 : 1)
 dec_act(DecodeArgs a) {
     __shared__ RouteView v;
     __shared__ __attribute__((aligned(16))) uint16_t zs[16 * NS][KC + 8];
@@ -671,177 +714,194 @@ dec_act(DecodeArgs a) {
     __shared__ uint16_t bsc[CB_L];
     __shared__ uint16_t asc[KC][2];
     rv_load(v, a.idx, a.R);
-    const int nw = a.ncb2 / ACT_CPB;                          // workgroups per expert
-    const int xi = blockIdx.x / nw, cw = blockIdx.x % nw;
-    const int e = rv_distinct_expert(v, a.R, a.E, xi);
-    if (e < 0) return;
-    const int nrows = rv_expert_rows(v, e, a.T, a.k);
-    const int g = e / a.P;
+    // Work items are (distinct expert, 256-column block), expert-major; each
+    // workgroup takes one contiguous range of them (at most a few experts).
+    const int X = rv_count_experts(v, a.R, a.E);
+    const int NB = a.ncb2;
+    const int items = X * NB;
+    const int per = (items + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int iend = min((int)blockIdx.x * per + per, items);
     const int tid = threadIdx.x;
     const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
-
-    ActUp ru_;
-    ActDn rd_;
-    act_fetch_up(ru_, a, e, cw * ACT_CPB);
-    act_fetch_dn(rd_, a, e, g, cw * ACT_CPB);
-    int tq[NS][4];
-#pragma unroll
-    for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = ms * 16 + 4 * c + q;
-            tq[ms][q] = v.rtok[i < nrows ? i : 0];
-        }
-
-    // ---- R1, R2: finish the split-K sums in slice order and round to bf16
-    for (int i = tid; i < 16 * NS * (KC + 8); i += 256) {
-        const int row = i / (KC + 8), col = i % (KC + 8);
-        if (row >= nrows || col >= KC) zs[row][col] = 0;
-    }
-    for (int i = tid; i < 16 * NS * ZL_W; i += 256) {
-        const int row = i / ZL_W, col = i % ZL_W;
-        if (row >= nrows || col >= a.rL) zls[row][col] = 0;
-    }
-    for (int i = tid; i < nrows * KC; i += 256) {
-        const int row = i / KC, col = i % KC;
-        zs[row][col] = (uint16_t)f32_to_bf16_rne(
-            ordered_sum(a.z1p + (size_t)v.rows[row] * KC + col, a.S1, (size_t)a.R * KC));
-    }
-    for (int i = tid; i < nrows * a.rL; i += 256) {
-        const int row = i / a.rL, col = i % a.rL;
-        zls[row][col] = (uint16_t)f32_to_bf16_rne(ordered_sum(
-            a.zlp + ((size_t)v.rtok[row] * a.G + g) * a.rLp + col, 4 * a.S1, (size_t)a.T * a.G * a.rLp));
-    }
-
     const int N2 = KC + ((a.rL + 15) & ~15);
-    floatx4 z2acc[3][NS];                                     // this wave's R4 / R5 tiles nt2 = wv + 4 t
-#pragma unroll
-    for (int t = 0; t < 3; ++t)
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms) z2acc[t][ms] = zero4();
+    for (int i0 = blockIdx.x * per; i0 < iend;) {
+        const int xi = i0 / NB, j0 = i0 % NB;
+        const int j1 = min(NB, j0 + (iend - i0));
+        const int e = rv_nth_expert(v, a.E, xi);
+        const int nrows = rv_expert_rows(v, e, a.T, a.k);
+        const int g = e / a.P;
 
-    for (int blk = 0; blk < ACT_CPB; ++blk) {
-        const int cb = cw * ACT_CPB + blk;
-        const int col0 = cb * CB_L + wv * 64;
-        uint4 vb[4];
-        float hv[4][NS][4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int ncol = col0 + nt * 16 + li;
-            const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
-            vb[nt] = 8 * c < a.rL ? t : zero_u4();
-#pragma unroll
-            for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
-        }
-        // this block's B_up into LDS; the next block's B_up loads go out at once
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + 256 * i;
-            wb[(q >> 2) * 5 + (q & 3)] = ru_.rb[i];
-        }
-        bsc[tid] = (uint16_t)ru_.bs;
-        __syncthreads();
-        if (blk + 1 < ACT_CPB) act_fetch_up(ru_, a, e, cb + 1);
-
-        // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h))
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int lrow = wv * 64 + nt * 16 + li;
-            const int ncol = cb * CB_L + lrow;
-            floatx4 acc[NS];
-#pragma unroll
-            for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
-            uint4 af[NS][4];
-#pragma unroll
-            for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
-            mac_fast<NS>(acc, af, wb[lrow * 5 + c], bsc[lrow]);
-#pragma unroll
-            for (int ms = 0; ms < NS; ++ms)
-                acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt], acc[ms]);
-#pragma unroll
-            for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int i = ms * 16 + 4 * c + q;
-                    uint16_t ab = 0;
-                    if (i < nrows) {
-                        ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
-                        a.act[(size_t)v.rows[i] * a.h + ncol] = ab;
-                    }
-                    as_[i][lrow] = ab;
-                }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + 256 * i;
-            wb[(q >> 3) * 9 + (q & 7)] = rd_.ra[i];
-            if ((q >> 5) < a.rL) ub[(q >> 5) * 33 + (q & 31)] = rd_.ru[i];
-        }
-        asc[tid >> 1][tid & 1] = (uint16_t)rd_.as2;
-        __syncthreads();
-        if (blk + 1 < ACT_CPB) act_fetch_dn(rd_, a, e, g, cb + 1);
-
-        // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const int nt2 = wv + 4 * t;
-            if (nt2 >= N2 / 16) break;
-            const int n2 = nt2 * 16 + li;
-            if (nt2 * 16 < KC) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    uint4 af[NS][4];
-#pragma unroll
-                    for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
-                    mac_fast<NS>(z2acc[t], af, wb[n2 * 9 + u * 4 + c], asc[n2][u]);
-                }
-            } else {
-                const int cl = n2 - KC;
-                const bool nvalid = cl < a.rL;
-#pragma unroll
-                for (int st = 0; st < CB_L / 32; ++st) {
-                    const uint4 bv = nvalid ? ub[cl * 33 + st * 4 + c] : zero_u4();
-#pragma unroll
-                    for (int ms = 0; ms < NS; ++ms)
-                        z2acc[t][ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]),
-                                                 bv, z2acc[t][ms]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- this workgroup's partial R4 / R5 inputs; the last of the expert's adds them in order
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
-        const int nt2 = wv + 4 * t;
-        if (nt2 >= N2 / 16) break;
-        const int n2 = nt2 * 16 + li;
+        ActUp ru_;
+        ActDn rd_;
+        act_fetch_up(ru_, a, e, j0);
+        act_fetch_dn(rd_, a, e, g, j0);
+        int tq[NS][4];
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = ms * 16 + 4 * c + q;
-                if (i < nrows) st_agent(&a.z2p[((size_t)cw * a.R + v.rows[i]) * N2 + n2], z2acc[t][ms][q]);
+                tq[ms][q] = v.rtok[i < nrows ? i : 0];
             }
-    }
-    if (!arrive_last(v, &a.cnt_e[e], (uint32_t)nw)) return;
-    for (int i = tid; i < nrows * N2; i += 256) {
-        const int row = i / N2, n2 = i % N2;
-        const int slot = v.rows[row];
-        const float sum = ordered_sum_agent(a.z2p + (size_t)slot * N2 + n2, nw, (size_t)a.R * N2);
-        const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum);
-        if (n2 < KC) a.z2[(size_t)slot * KC + n2] = bits;
-        else if (n2 - KC < a.rL) a.zl2[(size_t)slot * a.rLp + (n2 - KC)] = bits;
+
+        // ---- R1, R2: finish the split-K sums in slice order and round to bf16
+        for (int i = tid; i < 16 * NS * (KC + 8); i += 256) {
+            const int row = i / (KC + 8), col = i % (KC + 8);
+            if (row >= nrows || col >= KC) zs[row][col] = 0;
+        }
+        for (int i = tid; i < 16 * NS * ZL_W; i += 256) {
+            const int row = i / ZL_W, col = i % ZL_W;
+            if (row >= nrows || col >= a.rL) zls[row][col] = 0;
+        }
+        for (int i = tid; i < nrows * KC; i += 256) {
+            const int row = i / KC, col = i % KC;
+            zs[row][col] = (uint16_t)f32_to_bf16_rne(
+                ordered_sum(a.z1p + (size_t)v.rows[row] * KC + col, a.S1, (size_t)a.R * KC));
+        }
+        for (int i = tid; i < nrows * a.rL; i += 256) {
+            const int row = i / a.rL, col = i % a.rL;
+            zls[row][col] = (uint16_t)f32_to_bf16_rne(ordered_sum(
+                a.zlp + ((size_t)v.rtok[row] * a.G + g) * a.rLp + col, 4 * a.S1, (size_t)a.T * a.G * a.rLp));
+        }
+
+        floatx4 z2acc[3][NS];                                 // this wave's R4 / R5 tiles nt2 = wv + 4 t
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) z2acc[t][ms] = zero4();
+
+        for (int cb = j0; cb < j1; ++cb) {
+            const bool more = cb + 1 < j1;
+            const int col0 = cb * CB_L + wv * 64;
+            uint4 vb[4];
+            float hv[4][NS][4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int ncol = col0 + nt * 16 + li;
+                const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
+                vb[nt] = 8 * c < a.rL ? t : zero_u4();
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
+            }
+            // this block's B_up into LDS; the next block's B_up loads go out at once
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = tid + 256 * i;
+                wb[(q >> 2) * 5 + (q & 3)] = ru_.rb[i];
+            }
+            bsc[tid] = (uint16_t)ru_.bs;
+            __syncthreads();
+            if (more) act_fetch_up(ru_, a, e, cb + 1);
+
+            // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h))
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int lrow = wv * 64 + nt * 16 + li;
+                const int ncol = cb * CB_L + lrow;
+                floatx4 acc[NS];
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+                uint4 af[NS][4];
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
+                mac_fast<NS>(acc, af, wb[lrow * 5 + c], bsc[lrow]);
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+                    acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt], acc[ms]);
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = ms * 16 + 4 * c + q;
+                        uint16_t ab = 0;
+                        if (i < nrows) {
+                            ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
+                            a.act[(size_t)v.rows[i] * a.h + ncol] = ab;
+                        }
+                        as_[i][lrow] = ab;
+                    }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = tid + 256 * i;
+                wb[(q >> 3) * 9 + (q & 7)] = rd_.ra[i];
+                if ((q >> 5) < a.rL) ub[(q >> 5) * 33 + (q & 31)] = rd_.ru[i];
+            }
+            asc[tid >> 1][tid & 1] = (uint16_t)rd_.as2;
+            __syncthreads();
+            if (more) act_fetch_dn(rd_, a, e, g, cb + 1);
+
+            // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int nt2 = wv + 4 * t;
+                if (nt2 >= N2 / 16) break;
+                const int n2 = nt2 * 16 + li;
+                if (nt2 * 16 < KC) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        uint4 af[NS][4];
+#pragma unroll
+                        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                            for (int s = 0; s < 4; ++s)
+                                af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
+                        mac_fast<NS>(z2acc[t], af, wb[n2 * 9 + u * 4 + c], asc[n2][u]);
+                    }
+                } else {
+                    const int cl = n2 - KC;
+                    const bool nvalid = cl < a.rL;
+#pragma unroll
+                    for (int st = 0; st < CB_L / 32; ++st) {
+                        const uint4 bv = nvalid ? ub[cl * 33 + st * 4 + c] : zero_u4();
+#pragma unroll
+                        for (int ms = 0; ms < NS; ++ms)
+                            z2acc[t][ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]),
+                                                     bv, z2acc[t][ms]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+
+        // ---- this range's partial R4 / R5 inputs, stored at the range's first block;
+        // the last range of the expert to arrive adds them in block order
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int nt2 = wv + 4 * t;
+            if (nt2 >= N2 / 16) break;
+            const int n2 = nt2 * 16 + li;
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = ms * 16 + 4 * c + q;
+                    if (i < nrows) st_agent(&a.z2p[((size_t)j0 * a.R + v.rows[i]) * N2 + n2], z2acc[t][ms][q]);
+                }
+        }
+        const int s_first = (xi * NB) / per, s_last = ((xi + 1) * NB - 1) / per;
+        if (arrive_last(v, &a.cnt_e[e], (uint32_t)(s_last - s_first + 1))) {
+            for (int i = tid; i < nrows * N2; i += 256) {
+                const int row = i / N2, n2 = i % N2;
+                const int slot = v.rows[row];
+                float sum = 0.f;
+                for (int sg = s_first; sg <= s_last; ++sg) {
+                    const int j = max(xi * NB, sg * per) - xi * NB;
+                    sum += ld_agent(a.z2p + ((size_t)j * a.R + slot) * N2 + n2);
+                }
+                const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum);
+                if (n2 < KC) a.z2[(size_t)slot * KC + n2] = bits;
+                else if (n2 - KC < a.rL) a.zl2[(size_t)slot * a.rLp + (n2 - KC)] = bits;
+            }
+        }
+        __syncthreads();
+        i0 += j1 - j0;
     }
 }
 
@@ -1036,6 +1096,22 @@ dec_down(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ launcher -------
+// Workgroups of `kernel` (256 threads) that fit on the current device at once:
+// compute units x resident workgroups per unit, cached per kernel and device.
+template <class K>
+static int resident_grid(K kernel) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, 0) != hipSuccess || per <= 0) per = 1;
+        cached[dev] = cus * per;
+    }
+    return cached[dev];
+}
 template <int NS, bool LDSP>
 static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
     const int nbh = a.h / 64, nbr = (a.r + 63) / 64;
@@ -1045,7 +1121,7 @@ static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
     prof_end(s, "dec_up");
     prof_begin(s);
     if (LDSP) {
-        dec_act<NS><<<a.nxmax * (a.ncb2 / ACT_CPB), 256, 0, s>>>(a);
+        dec_act<NS><<<resident_grid(dec_act<NS>), 256, 0, s>>>(a);
         prof_end(s, "dec_act");
     } else {
         dec_act_direct<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
@@ -1074,7 +1150,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 bool decode_lds_ok(int T, int d, int h, int r, int rL, int gq, int S1) {
     const int ns = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
     const int nsd = decode_ns_down(T);
-    return gq % KC == 0 && r == KC && rL % 8 == 0 && rL <= ACT_RL && h % (CB_L * ACT_CPB) == 0 &&
+    return gq % KC == 0 && r == KC && rL % 8 == 0 && rL <= ACT_RL && h % CB_L == 0 &&
            (d / S1) % (512 / ns) == 0 && h % (512 / nsd) == 0;
 }
 
