@@ -76,19 +76,23 @@ def dequant(packed: np.ndarray, scale_bits: np.ndarray, K: int) -> np.ndarray:
 def rn_bf16(v: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bf16 value, ties to even.
 
-    bf16 keeps 8 significant bits.  With v = m * 2**e, m in [0.5, 1), the
-    rounded value is rint(m * 256) / 256 * 2**e (rint is half-to-even).  The
-    layer's values never reach the bf16 subnormal or overflow range; that is
-    asserted rather than handled.
+    bf16 keeps 8 significant bits and fp32's exponent range, subnormals
+    included.  With v = m * 2**e, m in [0.5, 1), a normal result is
+    rint(m * 256) / 256 * 2**e (rint is half-to-even); below 2**-126 the grid
+    is the fixed spacing 2**-133, so the result is rint(v * 2**133) * 2**-133.
+    Deep stacks of layers reach that range (SiLU of a large negative
+    pre-activation).  Overflow is asserted rather than handled.
     """
     v = np.asarray(v, dtype=np.float64)
     if not np.all(np.isfinite(v)):
         raise ValueError("non-finite value at a bf16 rounding point")
     a = np.abs(v)
-    if np.any((a != 0) & (a < F32_MIN_NORMAL)) or np.any(a >= BF16_MAX):
-        raise ValueError("value outside the bf16 normal range")
+    if np.any(a >= BF16_MAX):
+        raise ValueError("value outside the bf16 range")
     m, e = np.frexp(v)
-    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+    normal = np.ldexp(np.rint(m * 256.0) / 256.0, e)
+    sub = np.ldexp(np.rint(np.ldexp(v, 133)), -133)
+    return np.where(a < F32_MIN_NORMAL, sub, normal)
 
 
 def rn_f32(v: np.ndarray) -> np.ndarray:

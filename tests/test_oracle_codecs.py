@@ -69,6 +69,23 @@ def test_rn_bf16_matches_torch_on_fp32_inputs():
     assert np.array_equal(got, ref)
 
 
+def test_rn_bf16_subnormal_range_matches_torch():
+    """Below 2**-126 bf16 has a fixed spacing of 2**-133 (subnormals), like fp32's
+    own subnormal range; torch's float32 -> bfloat16 conversion is the reference."""
+    rng = np.random.default_rng(6)
+    k = rng.integers(1, 2 ** 23, size=20000)
+    v32 = (np.ldexp(k.astype(np.float64), -149) * rng.choice([-1.0, 1.0], size=k.size)).astype(np.float32)
+    ties = np.array([np.ldexp(2 * j + 1, -134) for j in range(0, 200, 7)], dtype=np.float32)  # midpoints
+    near = np.array([np.float32(2.0 ** -126), np.nextafter(np.float32(2.0 ** -126), np.float32(0))],
+                    dtype=np.float32)
+    v32 = np.concatenate([v32, ties, -ties, near])
+    ref = torch.from_numpy(v32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(codecs.rn_bf16(v32.astype(np.float64)), ref)
+    # float64 inputs below fp32's range round to zero or to the smallest step
+    assert codecs.rn_bf16(np.array([2.0 ** -140]))[0] == 0.0
+    assert codecs.rn_bf16(np.array([0.75 * 2.0 ** -133]))[0] == 2.0 ** -133
+
+
 def test_rn_bf16_special_cases():
     one = 1.0
     assert codecs.rn_bf16(np.array([one + 2.0 ** -8]))[0] == 1.0             # tie -> even
