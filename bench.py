@@ -89,6 +89,10 @@ def kernel_bytes(D, idx: np.ndarray):
         "lora_in_down": G * per["ld_u"] + R * h * 2,
         "gemm_down": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2 + R * d * 4,
         "combine": R * d * 4 + T * d * 4,
+        "pf_gather_x": 2 * U * d * 2,
+        "pf_shared_up": G * (per["s_up"] + per["lu_v"]) + U * d * 2 + U * h * 4,
+        "pf_delta_up_act": X * per["b_up"] + R * r * 2 + R * h * 4 + R * h * 2,
+        "pf_down": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2 + R * d * 4,
     }, {"groups": G, "experts": X, "rows": R, "unique": U, "gw_up": gw_up, "gw_dn": gw_dn}
 
 
@@ -117,6 +121,9 @@ def kernel_flops(D, idx):
         "gemm_z2": 2 * R * r * h,
         "lora_in_down": 2 * R * rL * h,
         "gemm_down": 2 * R * d * h + 2 * R * d * r + 2 * R * d * rL,
+        "pf_shared_up": 2 * U * h * d + 2 * U * h * rL,
+        "pf_delta_up_act": 2 * R * h * r,
+        "pf_down": 2 * R * d * h + 2 * R * d * r + 2 * R * d * rL,
     }
 
 
@@ -245,6 +252,61 @@ def roofline_mfma(D, idxs, ktimes):
                   "kernel": name, "avg_ms": round(avg_ms, 4), "flops_per_launch": int(fl[name])}
 
 
+class Stack:
+    """The 48-layer stack of full-size layers (T=8), every layer's weights and
+    router resident in HBM at once; one step is route + layer + residual through
+    all layers in sequence."""
+
+    def __init__(self, seed=0, host_init=False):
+        import torch
+        import shared_matrix_expert_amd as em
+        import synth
+        self.torch, self.em = torch, em
+        c = synth.config(4)
+        self.D = c.dims
+        self.n_layers = c.layers
+        self.x0 = torch.from_numpy(synth.make_activations(4, seed).view(np.int16)).cuda()
+        self.layers = []
+        for layer in range(self.n_layers):
+            wr, _ = synth.make_router(4, seed, layer)
+            self.layers.append({"wr": torch.from_numpy(wr.view(np.int16)).cuda(),
+                                "W": Workload._weights(synth, 4, seed, layer, host_init)})
+        D = self.D
+        self.ws = torch.empty(em.edge_moe_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+        self.idx = torch.empty(D.T, D.top_k, dtype=torch.int32, device="cuda")
+        self.w = torch.empty(D.T, D.top_k, dtype=torch.float32, device="cuda")
+        self.y = torch.empty(D.T, D.d, dtype=torch.float32, device="cuda")
+        self.xa = torch.empty_like(self.x0)
+        self.xb = torch.empty_like(self.x0)
+        self.stream = torch.cuda.current_stream()
+        self.idxs = []
+
+    def step(self, record=False):
+        em, D = self.em, self.D
+        x = self.x0
+        for li, L in enumerate(self.layers):
+            em.edge_moe_route(D, x, L["wr"], None, self.idx, self.w, None, self.ws, self.stream)
+            em.edge_moe_forward(D, x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
+            if record:
+                self.torch.cuda.synchronize()
+                self.idxs.append(self.idx.cpu().numpy().copy())
+            out = self.xa if li % 2 == 0 else self.xb
+            em.edge_moe_residual(x, self.y, out, self.stream)
+            x = out
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        self.step(record=True)
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+
 # ---------------------------------------------------------------- CPU baseline -------
 
 def cpu_baseline(wl: Workload, budget_s: float = 30.0):
@@ -303,6 +365,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--stack-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -369,6 +433,23 @@ def main():
         line["cpu_baseline"] = cpu_baseline(wl)
     del wl
     torch.cuda.empty_cache()
+
+    if not args.no_stack:
+        log("building the 48-layer stack ...")
+        st = Stack(host_init=args.host_init)
+        ssec = st.time_steps(args.stack_steps, 2)
+        sb = float(sum(step_bytes(st.D, ix) + 2 * st.D.T * st.D.d * 2 for ix in st.idxs))
+        line["stack_48"] = {
+            "value": round(st.D.T / ssec, 1), "unit": "tokens/s", "steps": args.stack_steps,
+            "ms_per_step": round(ssec * 1e3, 4),
+            "workload": "T=8 batch through 48 full-size layers in sequence (independent routers, "
+                        "residual between layers), all weights resident",
+            "hbm": {"bytes_per_step": int(sb), "achieved_GBs": round(sb / ssec / 1e9, 1),
+                    "frac": round(sb / ssec / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        log(f"  stack: {ssec * 1e3:.3f} ms per pass, {st.D.T / ssec:.1f} tokens/s")
+        del st
+        torch.cuda.empty_cache()
 
     if not args.no_prefill:
         log("building prefill workload ...")
