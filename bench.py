@@ -366,6 +366,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--stack-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=4)
@@ -433,6 +434,27 @@ def main():
         line["cpu_baseline"] = cpu_baseline(wl)
     del wl
     torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        log("building decode workload (T=1) ...")
+        wd = Workload(1, args.layers, host_init=args.host_init)
+        didx = wd.routed_indices()
+        dsec = wd.time_steps(args.steps, args.warmup)
+        dkt = wd.kernel_times(max(20, args.steps // 4))
+        dname, droof = roofline_hbm(wd.D, didx, dkt)
+        droof["traffic"] = stored_traffic(dname, "decode_t1")
+        dsb = float(np.mean([step_bytes(wd.D, ix) for ix in didx]))
+        line["decode_t1"] = {
+            "value": round(wd.D.T / dsec, 1), "unit": "tokens/s", "steps": args.steps,
+            "ms_per_step": round(dsec * 1e3, 5),
+            "workload": "decode T=1, one layer, %d rotating layer instances" % args.layers,
+            "roofline": droof, "kernels": kernel_table(wd.D, didx, dkt),
+            "step_hbm": {"bytes_per_step": int(dsb), "achieved_GBs": round(dsb / dsec / 1e9, 1),
+                         "frac": round(dsb / dsec / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        log(f"  decode: {dsec * 1e6:.1f} us per step")
+        del wd
+        torch.cuda.empty_cache()
 
     if not args.no_stack:
         log("building the 48-layer stack ...")
