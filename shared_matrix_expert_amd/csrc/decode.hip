@@ -906,6 +906,12 @@ dec_act(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ kernel 3 -------
+// Delta-down weights of four experts (this lane's 16 bytes and scale each).
+struct DnRing {
+    uint4 w[4];
+    uint32_t s[4];
+};
+
 template <int NS, bool LDSP>
 __global__ void __launch_bounds__(256)
 dec_down(DecodeArgs a) {
@@ -915,6 +921,7 @@ dec_down(DecodeArgs a) {
     __shared__ RouteView v;
     __shared__ StreamLds<LNS, LKB> L;
     __shared__ int arow_l[16 * NS];
+    __shared__ int dexp_l[16 * NS];
     rv_load(v, a.idx, a.R);
     const int nbd = a.d / 64;
     const int pass = blockIdx.x / (a.G * nbd);
@@ -990,7 +997,63 @@ dec_down(DecodeArgs a) {
         if (lane < prow) my_e = v.idx[v.rows[m0 + lane]];
         if (lane >= 1 && lane - 1 < prow) prev_e = v.idx[v.rows[m0 + lane - 1]];
         uint64_t starts = __ballot(lane < prow && (lane == 0 || my_e != prev_e));
-        if (fast) {
+        if (LDSP && fast) {
+            // Expert u of the pass (in row order) owns the rows whose rank, the
+            // number of expert starts at or before the row less one, is u.  The
+            // A rows (R4 outputs) are the same for every expert, only the row mask
+            // changes.  Each expert needs one 16-byte weight load and one scale
+            // per lane; two sets of four experts alternate, so that one set is
+            // in flight while the other is consumed, with every load
+            // unconditional (indices past the last expert repeat it).
+            const int nexp = __popcll(starts);
+            if (wv == 0 && ((starts >> lane) & 1ull))
+                dexp_l[__popcll(starts & ((2ull << lane) - 1ull)) - 1] = my_e;
+            int rk[NS];
+            uint4 af[NS][4];
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) {
+                const int i = ms * 16 + li;
+                rk[ms] = i < prow ? __popcll(starts & ((2ull << i) - 1ull)) - 1 : -1;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) af[ms][s] = ld16(a.z2 + (size_t)slot_i[ms] * KC + 32 * c + 8 * s);
+            }
+            __syncthreads();
+            auto fetch = [&](DnRing& r, int u0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int e = dexp_l[min(u0 + q, nexp - 1)];
+                    r.w[q] = ld16(a.b_dn + ((size_t)e * a.d + ncol) * (KC / 2) + 16 * c);
+                    r.s[q] = a.b_dn_s[(size_t)e * a.d + ncol];
+                }
+            };
+            auto consume = [&](const DnRing& r, int u0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int u = u0 + q;
+                    if (u >= nexp) break;
+                    uint4 am[NS][4];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) am[ms][s] = rk[ms] == u ? af[ms][s] : zero_u4();
+                    mac_fast<NS>(acc, am, r.w[q], r.s[q]);
+                }
+            };
+            DnRing d0, d1;
+            fetch(d0, 0);
+            int u0 = 0;
+            for (; u0 + 8 <= nexp; u0 += 8) {
+                fetch(d1, u0 + 4);
+                consume(d0, u0);
+                fetch(d0, u0 + 8);
+                consume(d1, u0 + 4);
+            }
+            if (u0 < nexp) {
+                fetch(d1, u0 + 4);
+                consume(d0, u0);
+                consume(d1, u0 + 4);
+            }
+        } else if (fast) {
             // the A rows (R4 outputs of this pass) are the same for every expert;
             // only the row mask changes.  Each expert needs one 16-byte weight
             // load and one scale, kept DEPTH experts ahead in a ring.

@@ -38,18 +38,31 @@ router_logits_small(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     const int t0 = tg * RS_TOK;
     const int nt = min(RS_TOK, T - t0);
     const int hd = d / 2;                          // elements per half (a multiple of 64)
-    for (int i = threadIdx.x * 8; i < RS_TOK * d; i += 256 * 8) {
-        const int t = i / d, kk = i % d;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (t < nt) v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * d + kk);
-        *reinterpret_cast<uint4*>(&xs[t][kk]) = v;
+    // every load is issued before the first LDS store (clamped addresses, zero
+    // for rows past the batch), so the loads overlap
+    constexpr int XV = RS_TOK * RS_D / (256 * 8);
+    uint4 xv[XV];
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+        const int i = (threadIdx.x + 256 * u) * 8;
+        const int t = min(i / d, nt - 1), kk = i % d;
+        xv[u] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * d + kk);
     }
     const uint16_t* wrow = wr + (size_t)(e < E ? e : 0) * d + half * hd;
     uint4 wv8[RS_D / 2 / 512];
 #pragma unroll
     for (int i = 0; i < RS_D / 2 / 512; ++i) {
         const int kk = (i * kWave + lane) * 8;
-        wv8[i] = (e < E && kk < hd) ? *reinterpret_cast<const uint4*>(wrow + kk) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 w = *reinterpret_cast<const uint4*>(wrow + min(kk, hd - 8));
+        wv8[i] = (e < E && kk < hd) ? w : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+        const int i = (threadIdx.x + 256 * u) * 8;
+        if (i < RS_TOK * d) {
+            const int t = i / d, kk = i % d;
+            *reinterpret_cast<uint4*>(&xs[t][kk]) = t < nt ? xv[u] : make_uint4(0u, 0u, 0u, 0u);
+        }
     }
     __syncthreads();
     double acc[RS_TOK];
@@ -182,10 +195,10 @@ router_logits_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 // -------------------------------------------------------------- top-k -----------
 // One wave per token.  A candidate is the 64-bit key (order-preserving bits of
 // the logit, ~index): the larger key is the larger logit, or the equal logit
-// with the lower index.  Each lane keeps the best key among its own logits; a
-// round takes the wave-wide maximum with DPP row operations (no LDS), then
-// only the winning lane rescans its logits.  Then the softmax over the
-// selected logits in float64.
+// with the lower index; 0 marks no candidate.  Each lane sorts its own keys
+// (descending) once; a round takes the wave-wide maximum of the lanes' first
+// keys with DPP row operations (no LDS), and the lane that held it shifts its
+// list by one.  Then the softmax over the selected logits in float64.
 EM_DEV uint64_t topk_key(float v, int i) {
     uint32_t u = __float_as_uint(v);
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);     // order-preserving for non-NaN floats
@@ -215,40 +228,68 @@ EM_DEV uint64_t wave_max_key(uint64_t x) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Descending sort of N keys (N a power of two) with Batcher's odd-even merge
+// network; every index is a compile-time constant, so the keys stay in registers.
+template <int N>
+EM_DEV void sort_desc(uint64_t (&k)[N]) {
+#pragma unroll
+    for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+        for (int q = p; q >= 1; q >>= 1)
+#pragma unroll
+            for (int j = q % p; j + q < N; j += 2 * q)
+#pragma unroll
+                for (int i = 0; i < q; ++i)
+                    if (i + j + q < N && (i + j) / (2 * p) == (i + j + q) / (2 * p)) {
+                        const uint64_t a = k[i + j], b = k[i + j + q];
+                        k[i + j] = a > b ? a : b;
+                        k[i + j + q] = a > b ? b : a;
+                    }
+}
+
+// b in the lanes set in `lanes`, a in the others: one v_cndmask per 32-bit
+// half.  Written out so that the shift below stays a fixed set of selects
+// (the compiler otherwise turns a select between neighbours into an indexed
+// read, a compare chain per element).
+EM_DEV uint64_t select_lanes(uint64_t a, uint64_t b, uint64_t lanes) {
+    uint32_t lo, hi;
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(lo) : "v"((uint32_t)a), "v"((uint32_t)b), "s"(lanes));
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3"
+                 : "=v"(hi) : "v"((uint32_t)(a >> 32)), "v"((uint32_t)(b >> 32)), "s"(lanes));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int MAXPER>
 __global__ void __launch_bounds__(256)
 router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
             float* __restrict__ topk_w, int T, int E, int k) {
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
-    constexpr int MAXPER = 16;            // E <= 1024
     uint64_t key[MAXPER];
     const float* row = logits + (size_t)t * E;
+    float lv[MAXPER];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) lv[i] = row[min(lane + kWave * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
         const int e = lane + kWave * i;
-        key[i] = e < E ? topk_key(row[e], e) : 0ull;
+        key[i] = e < E ? topk_key(lv[i], e) : 0ull;
     }
-    auto local_best = [&]() {
-        uint64_t b = 0ull;
-#pragma unroll
-        for (int i = 0; i < MAXPER; ++i) b = key[i] > b ? key[i] : b;
-        return b;
-    };
-    uint64_t best = local_best();
+    sort_desc<MAXPER>(key);
     float my_sel = 0.f, sel0 = 0.f;
     int my_idx = 0;
     for (int j = 0; j < k; ++j) {
-        const uint64_t w = wave_max_key(best);
+        const uint64_t w = wave_max_key(key[0]);
         const int bi = (int)(~(uint32_t)w);
         const uint32_t hb = (uint32_t)(w >> 32);
         const float bv = __uint_as_float((hb & 0x80000000u) ? (hb & 0x7FFFFFFFu) : ~hb);
         if (j == 0) sel0 = bv;
         if (lane == j) { my_sel = bv; my_idx = bi; }
-        if ((bi & (kWave - 1)) == lane) {
-            key[bi / kWave] = 0ull;       // taken
-            best = local_best();
-        }
+        const uint64_t won = __ballot(key[0] == w);      // keys are distinct: one lane
+#pragma unroll
+        for (int i = 0; i + 1 < MAXPER; ++i) key[i] = select_lanes(key[i], key[i + 1], won);
+        key[MAXPER - 1] = select_lanes(key[MAXPER - 1], 0ull, won);
     }
     double u = (lane < k) ? exp((double)my_sel - (double)sel0) : 0.0;
     double s = u;
@@ -279,7 +320,8 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     prof_begin(stream);
-    router_topk<<<(T + 3) / 4, 256, 0, stream>>>(logits, idx, w, T, E, k);
+    if (E <= 8 * kWave) router_topk<8><<<(T + 3) / 4, 256, 0, stream>>>(logits, idx, w, T, E, k);
+    else router_topk<16><<<(T + 3) / 4, 256, 0, stream>>>(logits, idx, w, T, E, k);
     prof_end(stream, "router_topk");
     return hipGetLastError();
 }

@@ -179,6 +179,28 @@ def test_top1_routing():
     assert torch.all(w == 1.0)
 
 
+@pytest.mark.parametrize("E,T", [(64, 8), (512, 8), (1024, 8), (512, 40)])
+def test_route_ties(E, T):
+    """Many equal logits (experts share one of 5 weight rows, every 13th row is
+    zero): the order must be descending logit, equal logits by lower index.
+    Covers both top-k register layouts (E <= 512 and E <= 1024) and both logits
+    kernels (T <= 16 and larger batches)."""
+    say(f"case: route ties E={E} T={T}")
+    D = synth.Dims(T=T, d=256, h=256, n_experts=E, experts_per_group=max(E // 16, 4), top_k=10,
+                   delta_rank=8, lora_rank=2, quant_group=32)
+    rng = np.random.default_rng(E + T)
+    x = synth.bf16_bits_from_f32(rng.standard_normal((T, D.d), dtype=np.float32))
+    base = rng.standard_normal((5, D.d), dtype=np.float32) * np.float32(0.05)
+    w = base[(np.arange(E) * 7919) % 5].copy()
+    w[::13] = 0.0
+    wr = synth.bf16_bits_from_f32(w)
+    lay = Layer(D, {})
+    _check_route(D, x, wr, None, lay)
+    bias = np.zeros(E, dtype=np.float32)
+    bias[::3] = np.float32(0.25)
+    _check_route(D, x, wr, bias, lay)
+
+
 def test_residual_bit_exact():
     say("case: residual")
     rng = np.random.default_rng(4)
