@@ -656,10 +656,11 @@ dec_act_direct(DecodeArgs a) {
 }
 
 // Activation kernel with every weight block staged through LDS (r = 128,
-// quant groups a multiple of 128).  The work items are (distinct expert, block
-// of 256 columns), expert-major, and a fixed grid of workgroups (all resident
-// at once) splits them into equal contiguous ranges, so a range spans at most
-// a few experts.  Per block the expert's B_up rows of those columns (256 x 64
+// quant groups a multiple of 128).  The work is (distinct expert, block of 256
+// columns); a fixed grid of workgroups (all resident at once) cuts each
+// expert's blocks into the same number of near-equal ranges (as many as the
+// grid holds for every expert), so that no range spans two experts and each
+// pays the expert's set-up once.  Per block the expert's B_up rows of those columns (256 x 64
 // B, contiguous), its A_dn columns (128 rows x 128 B) and the group's U_dn
 // columns are loaded coalesced, each phase's next-block loads issued before
 // the other phase's arithmetic.  A range keeps its R4 / R5 partial sums in
@@ -675,8 +676,10 @@ struct ActUp {
     uint4 rb[4];
     uint32_t bs;
 };
+constexpr int ACT_UI = ACT_RL * 32 / 256;   // U_dn 16-byte pieces per thread
+
 struct ActDn {
-    uint4 ra[4], ru[4];
+    uint4 ra[4], ru[ACT_UI];
     uint32_t as2;
 };
 
@@ -696,6 +699,10 @@ EM_DEV void act_fetch_dn(ActDn& r, const DecodeArgs& a, int e, int g, int cb) {
         const int q = tid + 256 * i;
         const int row = q >> 3, seg = q & 7;
         r.ra[i] = ld16(a.a_dn + ((size_t)e * KC + row) * (a.h / 2) + cb * (CB_L / 2) + 16 * seg);
+    }
+#pragma unroll
+    for (int i = 0; i < ACT_UI; ++i) {
+        const int q = tid + 256 * i;
         const int urow = q >> 5, useg = q & 31;
         r.ru[i] = ld16(a.ld_u + ((size_t)g * a.rL + min(urow, a.rL - 1)) * a.h + cb * CB_L + 8 * useg);
     }
@@ -718,23 +725,19 @@ dec_act(DecodeArgs a) {
     // workgroup takes one contiguous range of them (at most a few experts).
     const int X = rv_count_experts(v, a.R, a.E);
     const int NB = a.ncb2;
-    const int items = X * NB;
-    const int per = (items + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int iend = min((int)blockIdx.x * per + per, items);
+    const int G0 = (int)gridDim.x;
+    const int rpe = max(1, min(NB, G0 / X));          // ranges per expert
     const int tid = threadIdx.x;
     const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
     const int N2 = KC + ((a.rL + 15) & ~15);
-    for (int i0 = blockIdx.x * per; i0 < iend;) {
-        const int xi = i0 / NB, j0 = i0 % NB;
-        const int j1 = min(NB, j0 + (iend - i0));
+    for (int w = blockIdx.x; w < X * rpe; w += G0) {
+        // range r of expert xi: blocks [r NB / rpe, (r + 1) NB / rpe)
+        const int xi = w / rpe, r = w % rpe;
+        const int j0 = (r * NB) / rpe, j1 = ((r + 1) * NB) / rpe;
         const int e = rv_nth_expert(v, a.E, xi);
         const int nrows = rv_expert_rows(v, e, a.T, a.k);
         const int g = e / a.P;
 
-        ActUp ru_;
-        ActDn rd_;
-        act_fetch_up(ru_, a, e, j0);
-        act_fetch_dn(rd_, a, e, g, j0);
         int tq[NS][4];
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms)
@@ -743,25 +746,64 @@ dec_act(DecodeArgs a) {
                 const int i = ms * 16 + 4 * c + q;
                 tq[ms][q] = v.rtok[i < nrows ? i : 0];
             }
+        // per-block shared-up values and V_up rows, loaded one block ahead
+        uint4 vb[4];
+        float hv[4][NS][4];
+        auto fetch_hv = [&](int cb) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int ncol = cb * CB_L + wv * 64 + nt * 16 + li;
+                const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
+                vb[nt] = 8 * c < a.rL ? t : zero_u4();
+#pragma unroll
+                for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
+            }
+        };
 
-        // ---- R1, R2: finish the split-K sums in slice order and round to bf16
-        for (int i = tid; i < 16 * NS * (KC + 8); i += 256) {
-            const int row = i / (KC + 8), col = i % (KC + 8);
-            if (row >= nrows || col >= KC) zs[row][col] = 0;
+        // ---- R1, R2: finish the split-K sums in slice order and round to bf16.
+        // Every partial is loaded before the first is added (S1 <= 2 slices for
+        // R1, 4 S1 <= 8 for R2; addresses past the count are clamped, unused).
+        constexpr int ZI = 16 * NS * KC / 256;
+        constexpr int ZLI = 16 * NS * 32 / 256;
+        float zp[ZI][2], lp[ZLI][8];
+        const int s1b = min(1, a.S1 - 1), nl = 4 * a.S1;
+#pragma unroll
+        for (int u = 0; u < ZI; ++u) {
+            const int i = tid + 256 * u, row = min(i / KC, nrows - 1), col = i % KC;
+            const float* p = a.z1p + (size_t)v.rows[row] * KC + col;
+            zp[u][0] = p[0];
+            zp[u][1] = p[(size_t)s1b * a.R * KC];
         }
-        for (int i = tid; i < 16 * NS * ZL_W; i += 256) {
-            const int row = i / ZL_W, col = i % ZL_W;
-            if (row >= nrows || col >= a.rL) zls[row][col] = 0;
+#pragma unroll
+        for (int u = 0; u < ZLI; ++u) {
+            const int i = tid + 256 * u, row = min(i / 32, nrows - 1), col = min(i % 32, a.rL - 1);
+            const float* p = a.zlp + ((size_t)v.rtok[row] * a.G + g) * a.rLp + col;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) lp[u][s] = p[(size_t)min(s, nl - 1) * a.T * a.G * a.rLp];
         }
-        for (int i = tid; i < nrows * KC; i += 256) {
-            const int row = i / KC, col = i % KC;
-            zs[row][col] = (uint16_t)f32_to_bf16_rne(
-                ordered_sum(a.z1p + (size_t)v.rows[row] * KC + col, a.S1, (size_t)a.R * KC));
+        // then the first block's operands, so that the sums above wait for no weight
+        fetch_hv(j0);
+        ActUp ru_;
+        ActDn rd_;
+        act_fetch_up(ru_, a, e, j0);
+        act_fetch_dn(rd_, a, e, g, j0);
+#pragma unroll
+        for (int u = 0; u < ZI; ++u) {
+            const int i = tid + 256 * u, row = i / KC, col = i % KC;
+            float sum = 0.f + zp[u][0];
+            if (a.S1 > 1) sum += zp[u][1];
+            zs[row][col] = row < nrows ? (uint16_t)f32_to_bf16_rne(sum) : (uint16_t)0;
         }
-        for (int i = tid; i < nrows * a.rL; i += 256) {
-            const int row = i / a.rL, col = i % a.rL;
-            zls[row][col] = (uint16_t)f32_to_bf16_rne(ordered_sum(
-                a.zlp + ((size_t)v.rtok[row] * a.G + g) * a.rLp + col, 4 * a.S1, (size_t)a.T * a.G * a.rLp));
+#pragma unroll
+        for (int u = 0; u < ZLI; ++u) {
+            const int i = tid + 256 * u, row = i / 32, col = i % 32;
+            float sum = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                if (s < nl) sum += lp[u][s];
+            zls[row][col] = (row < nrows && col < a.rL) ? (uint16_t)f32_to_bf16_rne(sum) : (uint16_t)0;
         }
 
         floatx4 z2acc[3][NS];                                 // this wave's R4 / R5 tiles nt2 = wv + 4 t
@@ -771,20 +813,6 @@ dec_act(DecodeArgs a) {
             for (int ms = 0; ms < NS; ++ms) z2acc[t][ms] = zero4();
 
         for (int cb = j0; cb < j1; ++cb) {
-            const bool more = cb + 1 < j1;
-            const int col0 = cb * CB_L + wv * 64;
-            uint4 vb[4];
-            float hv[4][NS][4];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int ncol = col0 + nt * 16 + li;
-                const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
-                vb[nt] = 8 * c < a.rL ? t : zero_u4();
-#pragma unroll
-                for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
-            }
             // this block's B_up into LDS; the next block's B_up loads go out at once
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -793,7 +821,9 @@ dec_act(DecodeArgs a) {
             }
             bsc[tid] = (uint16_t)ru_.bs;
             __syncthreads();
-            if (more) act_fetch_up(ru_, a, e, cb + 1);
+            // unconditional (the last block re-reads itself): the compiler's waits
+            // for later loads would otherwise count these as possibly absent
+            act_fetch_up(ru_, a, e, min(cb + 1, j1 - 1));
 
             // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h))
 #pragma unroll
@@ -826,16 +856,21 @@ dec_act(DecodeArgs a) {
                         as_[i][lrow] = ab;
                     }
             }
+            fetch_hv(min(cb + 1, j1 - 1));
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int q = tid + 256 * i;
                 wb[(q >> 3) * 9 + (q & 7)] = rd_.ra[i];
+            }
+#pragma unroll
+            for (int i = 0; i < ACT_UI; ++i) {
+                const int q = tid + 256 * i;
                 if ((q >> 5) < a.rL) ub[(q >> 5) * 33 + (q & 31)] = rd_.ru[i];
             }
             asc[tid >> 1][tid & 1] = (uint16_t)rd_.as2;
             __syncthreads();
-            if (more) act_fetch_dn(rd_, a, e, g, cb + 1);
+            act_fetch_dn(rd_, a, e, g, min(cb + 1, j1 - 1));
 
             // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows
 #pragma unroll
@@ -885,14 +920,13 @@ dec_act(DecodeArgs a) {
                     if (i < nrows) st_agent(&a.z2p[((size_t)j0 * a.R + v.rows[i]) * N2 + n2], z2acc[t][ms][q]);
                 }
         }
-        const int s_first = (xi * NB) / per, s_last = ((xi + 1) * NB - 1) / per;
-        if (arrive_last(v, &a.cnt_e[e], (uint32_t)(s_last - s_first + 1))) {
+        if (arrive_last(v, &a.cnt_e[e], (uint32_t)rpe)) {
             for (int i = tid; i < nrows * N2; i += 256) {
                 const int row = i / N2, n2 = i % N2;
                 const int slot = v.rows[row];
                 float sum = 0.f;
-                for (int sg = s_first; sg <= s_last; ++sg) {
-                    const int j = max(xi * NB, sg * per) - xi * NB;
+                for (int rr = 0; rr < rpe; ++rr) {
+                    const int j = (rr * NB) / rpe;
                     sum += ld_agent(a.z2p + ((size_t)j * a.R + slot) * N2 + n2);
                 }
                 const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum);
@@ -901,7 +935,6 @@ dec_act(DecodeArgs a) {
             }
         }
         __syncthreads();
-        i0 += j1 - j0;
     }
 }
 
