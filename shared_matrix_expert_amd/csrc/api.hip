@@ -297,7 +297,6 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.S1 = L.S1; a.cb2 = L.cb2; a.ncb2 = L.ncb2; a.lds = L.lds ? 1 : 0;
     const int rows_per_pass = 16 * em::decode_ns_down(d.T);
     a.npass = (a.R + rows_per_pass - 1) / rows_per_pass;
-    a.nsplit = (a.npass + 3) / 4;               // a workgroup takes at most 4 passes of its group
     a.nxmax = a.R < a.E ? a.R : a.E;
     a.x = x; a.idx = topk_idx; a.topk_w = topk_w;
     a.s_up = wt->s_up_q; a.s_up_s = wt->s_up_scale; a.s_dn = wt->s_dn_q; a.s_dn_s = wt->s_dn_scale;

@@ -67,7 +67,6 @@ struct DecodeArgs {
     int cb2;     // columns per workgroup of the activation kernel (128, 256 or 512)
     int ncb2;    // h / cb2
     int npass;   // row passes of the down kernel (bound: every slot in one group)
-    int nsplit;  // down-kernel workgroups per (group, column block); each takes every nsplit-th pass
     int nxmax;   // upper bound on distinct experts: min(E, R)
     int lds;     // LDS-streaming kernels (see decode_lds_ok)
     const uint16_t* x; const int32_t* idx; const float* topk_w;

@@ -89,7 +89,8 @@ def stats(out_dir: str, cmd: str, title: str, match: str = "") -> str:
 
 
 def _per_dispatch(out_dir: str, counter: str) -> dict:
-    """{short kernel name: [value per dispatch]} for one counter."""
+    """{kernel name: [value per dispatch]} for one counter, keyed both by the
+    name without template arguments (all instances) and with them (one)."""
     path = _find(out_dir, "counter_collection.csv")
     acc = defaultdict(float)
     names = {}
@@ -98,10 +99,13 @@ def _per_dispatch(out_dir: str, counter: str) -> dict:
             continue
         did = _col(r, "Dispatch_Id", "Dispatch_ID")
         acc[did] += float(_col(r, "Counter_Value"))
-        names[did] = _base(_col(r, "Kernel_Name"))
+        names[did] = (_base(_col(r, "Kernel_Name")), _short(_col(r, "Kernel_Name")))
     out = defaultdict(list)
     for did, v in acc.items():
-        out[names[did]].append(v)
+        base, short = names[did]
+        out[base].append(v)
+        if short != base:
+            out[short].append(v)
     return out
 
 
