@@ -24,6 +24,7 @@
 #include "kernels.h"
 #include "mfma_ops.h"
 #include "tile_stream.h"
+#include "wave_stream.h"
 
 namespace em {
 
@@ -244,8 +245,14 @@ dec_up(DecodeArgs a) {
     constexpr int KB = KBlock<NS>::value;
     constexpr int LNS = LDSP ? NS : 1;                 // no LDS tiles in the fallback instance
     constexpr int LKB = LDSP ? KB : 128;
+    // the LDS streams of the R1 / R2 tasks and the staged x of the wave-streamed
+    // shared up share one buffer (a workgroup runs one task)
+    constexpr size_t HS_XS = 32768;                    // bytes of x per stage
+    constexpr size_t HS_SM = HS_XS + 4 * WS_TILE * 16;
+    constexpr size_t SM = sizeof(StreamLds<LNS, LKB>) > HS_SM ? sizeof(StreamLds<LNS, LKB>) : HS_SM;
     __shared__ RouteView v;
-    __shared__ StreamLds<LNS, LKB> L;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SM];
+    StreamLds<LNS, LKB>& L = *reinterpret_cast<StreamLds<LNS, LKB>*>(smem);
     __shared__ int arow_l[16 * NS];
     if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < a.E; i += blockDim.x) a.cnt_e[i] = 0u;
@@ -268,7 +275,57 @@ dec_up(DecodeArgs a) {
         const int g = b / (nbh / HS_RB), nb0 = (b % (nbh / HS_RB)) * HS_RB;
         const int nrows = rv_group_tokens(v, g, a.T, a.k, a.P);
         if (nrows == 0) return;
-        if constexpr (lds) {
+        if (LDSP && NS == 1 && a.gq == KC && a.d % 2048 == 0) {
+            // Wave-streamed: x rows of the group's tokens staged in LDS, 32 KB
+            // per stage (8 rows x 2048 or 16 rows x 1024 elements), then every
+            // wave streams its 16 weight rows of each 64-column block with no
+            // workgroup barrier until the next stage.
+            const int rp = nrows <= 8 ? 8 : 16;
+            const int KX = (int)(HS_XS / 2) / rp;
+            uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+            ws_u4* T = reinterpret_cast<ws_u4*>(smem + HS_XS) + wv * WS_TILE;
+            WsAct ar;
+            const int arw = min(li, rp - 1);
+            ar.row[0] = xs + (size_t)arw * KX;
+            ar.sw[0] = arw & 15;
+            WsSrc src[HS_RB];
+            floatx4 acc[HS_RB][1];
+#pragma unroll
+            for (int rb = 0; rb < HS_RB; ++rb) {
+                const size_t r0 = (size_t)g * a.h + (nb0 + rb) * 64 + wv * 16;
+                ws_src(src[rb], a.s_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.s_up_s + r0 * (a.d / KC),
+                       (size_t)(a.d / KC));
+                acc[rb][0] = zero4();
+            }
+            constexpr int XU = HS_XS / 16 / 256;          // 16-byte pieces per thread and stage
+            const int spr = KX / 8;                        // 16-byte segments per staged row
+            for (int ks = 0; ks < a.d; ks += KX) {
+                __syncthreads();                           // the previous stage is read
+                uint4 xv[XU];
+#pragma unroll
+                for (int u = 0; u < XU; ++u) {
+                    const int q = (int)threadIdx.x + 256 * u, r = q / spr, sg = q % spr;
+                    xv[u] = ld16(a.x + (size_t)v.rtok[min(r, nrows - 1)] * a.d + ks + 8 * sg);
+                }
+#pragma unroll
+                for (int u = 0; u < XU; ++u) {
+                    const int q = (int)threadIdx.x + 256 * u, r = q / spr, sg = q % spr;
+                    *reinterpret_cast<uint4*>(xs + (size_t)r * KX + 8 * ((sg & ~15) | ((sg & 15) ^ (r & 15)))) = xv[u];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int rb = 0; rb < HS_RB; ++rb) ws_gemm<1>(acc[rb], src[rb], ks, T, ar, KX);
+            }
+#pragma unroll
+            for (int rb = 0; rb < HS_RB; ++rb) {
+                const int ncol = (nb0 + rb) * 64 + wv * 16 + li;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = 4 * c + q;
+                    if (i < nrows) a.hs[((size_t)v.rtok[i] * a.G + g) * a.h + ncol] = acc[rb][0][q];
+                }
+            }
+        } else if constexpr (lds) {
             if ((int)threadIdx.x < 16 * NS)
                 arow_l[threadIdx.x] = v.rtok[(int)threadIdx.x < nrows ? threadIdx.x : 0];
             __syncthreads();
