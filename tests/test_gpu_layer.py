@@ -136,9 +136,11 @@ def test_prefill_layer_sampled():
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("T", [2, 37, 200])
+@pytest.mark.parametrize("T", [2, 13, 16, 37, 200])
 def test_ragged_batches(T):
-    """Token counts that leave partial tiles and cross the router's small/large paths."""
+    """Token counts that leave partial tiles and cross the router's small/large
+    paths; 13 and 16 put more than 8 tokens into a group, so the shared up
+    stages x as 16 rows x 1024 elements instead of 8 x 2048."""
     say(f"case: ragged T={T}")
     D = synth.config(1).dims.with_T(T)
     x = synth.make_activations(1, 5, T=T)
