@@ -1012,7 +1012,17 @@ dec_down(DecodeArgs a) {
     __shared__ StreamLds<LNS, LKB> L;
     __shared__ int arow_l[16 * NS];
     __shared__ int dexp_l[16 * NS];
+    __shared__ int gcnt[64];
     rv_load(v, a.idx, a.R);
+    // rows per group, hence the passes that carry rows: only those workgroups
+    // arrive at the column block's counter, so the empty passes of the grid
+    // (npass is a bound for the worst routing) never delay the final sum
+    if ((int)threadIdx.x < 64) gcnt[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.R; i += blockDim.x) atomicAdd(&gcnt[v.idx[i] / a.P], 1);
+    __syncthreads();
+    int live_passes = 0;
+    for (int gg = 0; gg < a.G; ++gg) live_passes += (gcnt[gg] + 16 * NS - 1) / (16 * NS);
     const int nbd = a.d / 64;
     const int pass = blockIdx.x / (a.G * nbd);
     const int g = (blockIdx.x / nbd) % a.G;
@@ -1228,7 +1238,8 @@ dec_down(DecodeArgs a) {
     }
 
     // ---- the last workgroup of this column block forms y = sum_j w_j o_j in slot order
-    if (!arrive_last(v, &a.cnt_c[nb], (uint32_t)(a.npass * a.G))) return;
+    if (prow <= 0) return;
+    if (!arrive_last(v, &a.cnt_c[nb], (uint32_t)live_passes)) return;
     for (int i = threadIdx.x; i < a.T * 64; i += blockDim.x) {
         const int t = i / 64, col = nb * 64 + (i % 64);
         float acc = 0.f;
