@@ -8,9 +8,10 @@
 // times S_up (up), the group's rows times S_dn (down).  At 16K tokens these
 // two GEMMs are ~95 % of the layer's flops.
 //
-// Tile: 128 rows x 256 columns per workgroup of 4 waves (each wave all 128
-// rows x its own 64 columns = 8 x 4 MFMA 16x16 subtiles), K in steps of 128 =
-// one quant group.  The activation tile (128 x 128 bf16 = 32 KB) and the
+// Tile: 128 rows x 256 columns per workgroup of 8 waves (each wave 64 rows x
+// 64 columns = 4 x 4 MFMA 16x16 subtiles; two waves per SIMD, so one wave's
+// dequantisation and scaling overlap the other's matrix work), K in steps of
+// 128 = one quant group.  The activation tile (128 x 128 bf16 = 32 KB) and the
 // weight tile (256 columns x 128 int4 = 16 KB) move from global memory
 // straight into LDS (global_load_lds_dwordx4, no registers), three buffer sets
 // deep so that every step's loads have two steps of math to arrive in; the
@@ -32,8 +33,10 @@ namespace em {
 namespace {
 
 constexpr int BM = 128, BN = 256, BK = 128;
+constexpr int PF_WAVES = 8, PF_TH = 64 * PF_WAVES;
 constexpr int SLOTS = BK / 8;                    // 16-byte slots per activation row
-constexpr int WN = BN / 4;                       // columns per wave
+constexpr int WN = BN / 4;                       // columns per wave (wave w: columns WN (w % 4))
+constexpr int WM = BM / 2;                       // rows per wave (wave w: rows WM (w / 4))
 static_assert(BM <= kPfSpareRows, "the last row tile reads up to BM - 1 rows past the end");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -70,26 +73,26 @@ EM_DEV bool pf_tile(const LayerArgs& a, int b, int ntn, PfTile& t) {
 }
 
 // Per-thread sources, fixed for the whole K range: round i of the activation
-// DMA reads row r0 + 16 i + (4 w + l / 16) and round i of the weight DMA column
-// 64 i + 16 w + l / 4, so one base pointer per operand and a uniform stride
+// DMA reads row r0 + 32 i + (4 w + l / 16) and round i of the weight DMA column
+// 128 i + 16 w + l / 4, so one base pointer per operand and a uniform stride
 // give every round.  Activation rows past r1 read the next rows of the buffer
 // (the workspace holds BM spare rows past the last one); they only reach
 // output rows that are never stored.
 struct PfSrc {
     const uint16_t* a;              // round 0's activation row, at this lane's 16-byte segment
-    size_t a_step;                  // elements between rounds (16 rows)
+    size_t a_step;                  // elements between rounds (32 rows)
     const uint8_t* b;               // round 0's weight column, at this lane's 16-byte segment
-    size_t b_step;                  // bytes between rounds (64 columns)
+    size_t b_step;                  // bytes between rounds (128 columns)
     const uint16_t* s;              // scale row of this lane's first column
     size_t sstride;                 // elements between the scale rows of 16 columns
 };
 
-// Activation tile: 128 rows x 16 slots; wave w, round i covers rows 16 i + 4 w
+// Activation tile: 128 rows x 16 slots; wave w, round i covers rows 32 i + 4 w
 // .. + 3 (1 KB, lane-contiguous); lane l writes slot l % 16 of its row and
 // fetches the row's global segment (l % 16) ^ (row % 16), so that a fragment
 // read (16 rows, one segment) hits 16 distinct bank groups.  Weight tile: 256
 // columns x 4 slots of 16 bytes, slot = c ^ ((col / 4) % 4) holding the
-// column's bytes [16c, 16c + 16); wave w, round i covers columns 64 i + 16 w
+// column's bytes [16c, 16c + 16); wave w, round i covers columns 128 i + 16 w
 // .. + 15.
 EM_DEV void pf_src(PfSrc& p, const uint16_t* A, size_t lda, const uint8_t* Wt, size_t wstride,
                    const uint16_t* srow0, size_t sstride, int r0) {
@@ -97,45 +100,46 @@ EM_DEV void pf_src(PfSrc& p, const uint16_t* A, size_t lda, const uint8_t* Wt, s
     const int rsub = 4 * w + (l >> 4);
     const int seg = (l & 15) ^ (rsub & 15);
     p.a = A + (size_t)(r0 + rsub) * lda + 8 * seg;
-    p.a_step = 16 * lda;
+    p.a_step = 32 * lda;
     const int col = 16 * w + (l >> 2);
     p.b = Wt + (size_t)col * wstride + 16 * ((l & 3) ^ ((col >> 2) & 3));
-    p.b_step = 64 * wstride;
+    p.b_step = 128 * wstride;
     p.s = srow0;
     p.sstride = sstride;
 }
 
 // Step k0's loads: the 4 scales of this lane's columns first, then the weight
-// and activation tiles (12 DMA instructions per thread).
+// and activation tiles (6 DMA instructions per thread).
 EM_DEV void pf_fetch(uint4* As, uint4* Bs, uint32_t (&sb)[4], const PfSrc& p, int gq, int k0) {
     const int w = wave_id();
 #pragma unroll
     for (int j = 0; j < 4; ++j) sb[j] = p.s[(size_t)(16 * j) * p.sstride + k0 / gq];
 #pragma unroll
-    for (int i = 0; i < BN / 64; ++i)
+    for (int i = 0; i < BN / 128; ++i)
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.b + i * p.b_step + (k0 >> 1)),
-                                         (lds_ptr_t)(Bs + (64 * i + 16 * w) * 4), 16, 0, 0);
+                                         (lds_ptr_t)(Bs + (128 * i + 16 * w) * 4), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BM / 16; ++i)
+    for (int i = 0; i < BM / 32; ++i)
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.a + i * p.a_step + k0),
-                                         (lds_ptr_t)(As + (16 * i + 4 * w) * SLOTS), 16, 0, 0);
+                                         (lds_ptr_t)(As + (32 * i + 4 * w) * SLOTS), 16, 0, 0);
 }
-constexpr int PF_STEP_VM = 4 + BN / 64 + BM / 16;      // vector-memory instructions per step and thread
+constexpr int PF_STEP_VM = 4 + BN / 128 + BM / 32;     // vector-memory instructions per step and thread
 
 // acc[i][j] += (A rows of subtile i) x (16 x scale_j x dequant(B_j)) over one chunk.
-EM_DEV void pf_compute(floatx4 (&acc)[8][4], const uint4* As, const uint4* Bs, const uint32_t (&sbits)[4]) {
+EM_DEV void pf_compute(floatx4 (&acc)[4][4], const uint4* As, const uint4* Bs, const uint32_t (&sbits)[4]) {
     const int l = lane_id(), c = l >> 4, li = l & 15;
+    const int wm = wave_id() >> 2, wn = wave_id() & 3;
     uint4 bq[4][4];
     float sc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int col = WN * wave_id() + 16 * j + li;
+        const int col = WN * wn + 16 * j + li;
         dequant_b(Bs[col * 4 + (c ^ ((col >> 2) & 3))], bq[j]);
         sc[j] = 16.0f * fp16_bits_to_f32((uint16_t)sbits[j]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 16 * i + li;
+    for (int i = 0; i < 4; ++i) {
+        const int row = WM * wm + 16 * i + li;
         uint4 af[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) af[s] = As[row * SLOTS + ((4 * c + s) ^ li)];
@@ -167,7 +171,7 @@ EM_DEV void pf_compute(floatx4 (&acc)[8][4], const uint4* As, const uint4* Bs, c
     if ((K0) + BK >= K) break;
 
 template <int MODE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(PF_TH)
 pf_gemm(LayerArgs a) {
     __shared__ uint4 As0[BM * SLOTS];
     __shared__ uint4 As1[BM * SLOTS];
@@ -189,15 +193,15 @@ pf_gemm(LayerArgs a) {
     const uint8_t* W = MODE == PF_HS ? a.s_up : a.s_dn;
     const uint16_t* S = MODE == PF_HS ? a.s_up_s : a.s_dn_s;
     const int l = lane_id(), wv = wave_id(), c = l >> 4, li = l & 15;
-    const int wm = 0, wn = wv;
+    const int wm = wv >> 2, wn = wv & 3;
 
     PfSrc src;
     pf_src(src, A, (size_t)K, W + ((size_t)t.g * N + t.n0) * (K / 2), (size_t)(K / 2),
-           S + ((size_t)t.g * N + t.n0 + WN * wv + li) * (K / gq), (size_t)(K / gq), t.r0);
+           S + ((size_t)t.g * N + t.n0 + WN * wn + li) * (K / gq), (size_t)(K / gq), t.r0);
 
-    floatx4 acc[8][4];
+    floatx4 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
 
@@ -227,8 +231,8 @@ pf_gemm(LayerArgs a) {
                 bv[j] = kv ? ld16(V + (size_t)n * a.rL + kb + 8 * c) : zero_u4();
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = min(t.r0 + 16 * i + li, t.r1 - 1);
+            for (int i = 0; i < 4; ++i) {
+                const int row = min(t.r0 + WM * wm + 16 * i + li, t.r1 - 1);
                 const uint4 av = kv ? ld16(Z + (size_t)row * rLp + kb + 8 * c) : zero_u4();
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(av, bv[j], acc[i][j]);
@@ -254,8 +258,8 @@ pf_gemm(LayerArgs a) {
                     sc[j] = 16.0f * fp16_bits_to_f32(a.b_dn_s[n * (a.r / gq_r) + k0 / gq_r]);
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int rl = 16 * i;                  // subtile rows [rl, rl + 16)
+                for (int i = 0; i < 4; ++i) {
+                    const int rl = WM * wm + 16 * i;        // subtile rows [rl, rl + 16)
                     if (rl + 16 <= p || rl >= q) continue;             // wave-uniform
                     const int row = rl + li;
                     const bool mine = row >= p && row < q;
@@ -276,13 +280,13 @@ pf_gemm(LayerArgs a) {
         }
     }
 
-    // ---- store: lane holds rows 16 i + 4 c + v, column 16 j + li of its wave's block
+    // ---- store: lane holds rows WM wm + 16 i + 4 c + v, column 16 j + li of its wave's block
     float* out = MODE == PF_HS ? a.hs : a.o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int row = t.r0 + 16 * i + 4 * c + v;
+            const int row = t.r0 + WM * wm + 16 * i + 4 * c + v;
             if (row >= t.r1) continue;
             float* orow = out + (size_t)row * N + t.n0 + WN * wn + li;
 #pragma unroll
@@ -396,10 +400,10 @@ hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, h
     blocks = (blocks + 7) & ~7ll;
     prof_begin(s);
     if (mode == PF_HS) {
-        pf_gemm<PF_HS><<<(unsigned)blocks, 256, 0, s>>>(a);
+        pf_gemm<PF_HS><<<(unsigned)blocks, PF_TH, 0, s>>>(a);
         prof_end(s, "pf_shared_up");
     } else {
-        pf_gemm<PF_OUT><<<(unsigned)blocks, 256, 0, s>>>(a);
+        pf_gemm<PF_OUT><<<(unsigned)blocks, PF_TH, 0, s>>>(a);
         prof_end(s, "pf_down");
     }
     return hipGetLastError();
