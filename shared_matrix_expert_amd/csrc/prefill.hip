@@ -8,10 +8,11 @@
 // times S_up (up), the group's rows times S_dn (down).  At 16K tokens these
 // two GEMMs are ~95 % of the layer's flops.
 //
-// Tile: 128 rows x 256 columns per workgroup of 8 waves (each wave 64 rows x
-// 64 columns = 4 x 4 MFMA 16x16 subtiles; two waves per SIMD, so one wave's
-// dequantisation and scaling overlap the other's matrix work), K in steps of
-// 128 = one quant group.  The activation tile (128 x 128 bf16 = 32 KB) and the
+// Tile: 128 rows x 256 columns per workgroup of 8 waves (each wave all 128
+// rows x its own 32 columns = 8 x 2 MFMA 16x16 subtiles; two waves per SIMD,
+// so one wave's dequantisation and scaling overlap the other's matrix work,
+// and every column is dequantised once per workgroup), K in steps of 128 = one
+// quant group.  The activation tile (128 x 128 bf16 = 32 KB) and the
 // weight tile (256 columns x 128 int4 = 16 KB) move from global memory
 // straight into LDS (global_load_lds_dwordx4, no registers), three buffer sets
 // deep so that every step's loads have two steps of math to arrive in; the
@@ -35,8 +36,8 @@ namespace {
 constexpr int BM = 128, BN = 256, BK = 128;
 constexpr int PF_WAVES = 8, PF_TH = 64 * PF_WAVES;
 constexpr int SLOTS = BK / 8;                    // 16-byte slots per activation row
-constexpr int WN = BN / 4;                       // columns per wave (wave w: columns WN (w % 4))
-constexpr int WM = BM / 2;                       // rows per wave (wave w: rows WM (w / 4))
+constexpr int WN = BN / PF_WAVES;                // columns per wave (wave w: columns WN w)
+constexpr int NJ = WN / 16, NI = BM / 16;        // 16x16 subtiles per wave (all BM rows)
 static_assert(BM <= kPfSpareRows, "the last row tile reads up to BM - 1 rows past the end");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -108,12 +109,12 @@ EM_DEV void pf_src(PfSrc& p, const uint16_t* A, size_t lda, const uint8_t* Wt, s
     p.sstride = sstride;
 }
 
-// Step k0's loads: the 4 scales of this lane's columns first, then the weight
+// Step k0's loads: the scales of this lane's NJ columns first, then the weight
 // and activation tiles (6 DMA instructions per thread).
-EM_DEV void pf_fetch(uint4* As, uint4* Bs, uint32_t (&sb)[4], const PfSrc& p, int gq, int k0) {
+EM_DEV void pf_fetch(uint4* As, uint4* Bs, uint32_t (&sb)[NJ], const PfSrc& p, int gq, int k0) {
     const int w = wave_id();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sb[j] = p.s[(size_t)(16 * j) * p.sstride + k0 / gq];
+    for (int j = 0; j < NJ; ++j) sb[j] = p.s[(size_t)(16 * j) * p.sstride + k0 / gq];
 #pragma unroll
     for (int i = 0; i < BN / 128; ++i)
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.b + i * p.b_step + (k0 >> 1)),
@@ -123,28 +124,28 @@ EM_DEV void pf_fetch(uint4* As, uint4* Bs, uint32_t (&sb)[4], const PfSrc& p, in
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.a + i * p.a_step + k0),
                                          (lds_ptr_t)(As + (32 * i + 4 * w) * SLOTS), 16, 0, 0);
 }
-constexpr int PF_STEP_VM = 4 + BN / 128 + BM / 32;     // vector-memory instructions per step and thread
+constexpr int PF_STEP_VM = NJ + BN / 128 + BM / 32;    // vector-memory instructions per step and thread
 
 // acc[i][j] += (A rows of subtile i) x (16 x scale_j x dequant(B_j)) over one chunk.
-EM_DEV void pf_compute(floatx4 (&acc)[4][4], const uint4* As, const uint4* Bs, const uint32_t (&sbits)[4]) {
+EM_DEV void pf_compute(floatx4 (&acc)[NI][NJ], const uint4* As, const uint4* Bs, const uint32_t (&sbits)[NJ]) {
     const int l = lane_id(), c = l >> 4, li = l & 15;
-    const int wm = wave_id() >> 2, wn = wave_id() & 3;
-    uint4 bq[4][4];
-    float sc[4];
+    const int wn = wave_id();
+    uint4 bq[NJ][4];
+    float sc[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int col = WN * wn + 16 * j + li;
         dequant_b(Bs[col * 4 + (c ^ ((col >> 2) & 3))], bq[j]);
         sc[j] = 16.0f * fp16_bits_to_f32((uint16_t)sbits[j]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = WM * wm + 16 * i + li;
+    for (int i = 0; i < NI; ++i) {
+        const int row = 16 * i + li;
         uint4 af[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) af[s] = As[row * SLOTS + ((4 * c + s) ^ li)];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             floatx4 t = mfma_bf16(af[0], bq[j][0], zero4());
             t = mfma_bf16(af[1], bq[j][1], t);
             t = mfma_bf16(af[2], bq[j][2], t);
@@ -193,20 +194,20 @@ pf_gemm(LayerArgs a) {
     const uint8_t* W = MODE == PF_HS ? a.s_up : a.s_dn;
     const uint16_t* S = MODE == PF_HS ? a.s_up_s : a.s_dn_s;
     const int l = lane_id(), wv = wave_id(), c = l >> 4, li = l & 15;
-    const int wm = wv >> 2, wn = wv & 3;
+    const int wn = wv;
 
     PfSrc src;
     pf_src(src, A, (size_t)K, W + ((size_t)t.g * N + t.n0) * (K / 2), (size_t)(K / 2),
            S + ((size_t)t.g * N + t.n0 + WN * wn + li) * (K / gq), (size_t)(K / gq), t.r0);
 
-    floatx4 acc[4][4];
+    floatx4 acc[NI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+        for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
 
     // ---- main loop: three buffer sets, loads two steps ahead of the math (K >= 3 BK)
-    uint32_t s0[4], s1[4], s2[4];
+    uint32_t s0[NJ], s1[NJ], s2[NJ];
     pf_fetch(As0, Bs0, s0, src, gq, 0);
     pf_fetch(As1, Bs1, s1, src, gq, BK);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF_STEP_VM));
@@ -224,18 +225,18 @@ pf_gemm(LayerArgs a) {
         const uint16_t* Z = MODE == PF_HS ? a.zl : a.zl2;
         for (int kb = 0; kb < a.rL; kb += 32) {
             const bool kv = kb + 8 * c < a.rL;
-            uint4 bv[4];
+            uint4 bv[NJ];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int n = t.n0 + WN * wn + 16 * j + li;
                 bv[j] = kv ? ld16(V + (size_t)n * a.rL + kb + 8 * c) : zero_u4();
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = min(t.r0 + WM * wm + 16 * i + li, t.r1 - 1);
+            for (int i = 0; i < NI; ++i) {
+                const int row = min(t.r0 + 16 * i + li, t.r1 - 1);
                 const uint4 av = kv ? ld16(Z + (size_t)row * rLp + kb + 8 * c) : zero_u4();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(av, bv[j], acc[i][j]);
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_bf16(av, bv[j], acc[i][j]);
             }
         }
     }
@@ -249,17 +250,17 @@ pf_gemm(LayerArgs a) {
             const int q = min(a.db.eoff[e + 1], t.r1) - t.r0;
             if (p >= q) continue;
             for (int k0 = 0; k0 < a.r; k0 += KC) {
-                uint4 bq[4][4];
-                float sc[4];
+                uint4 bq[NJ][4];
+                float sc[NJ];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     const size_t n = (size_t)e * a.d + t.n0 + WN * wn + 16 * j + li;
                     dequant_b(ld16(a.b_dn + n * (a.r / 2) + (k0 >> 1) + 16 * c), bq[j]);
                     sc[j] = 16.0f * fp16_bits_to_f32(a.b_dn_s[n * (a.r / gq_r) + k0 / gq_r]);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rl = WM * wm + 16 * i;        // subtile rows [rl, rl + 16)
+                for (int i = 0; i < NI; ++i) {
+                    const int rl = 16 * i;        // subtile rows [rl, rl + 16)
                     if (rl + 16 <= p || rl >= q) continue;             // wave-uniform
                     const int row = rl + li;
                     const bool mine = row >= p && row < q;
@@ -268,7 +269,7 @@ pf_gemm(LayerArgs a) {
 #pragma unroll
                     for (int s = 0; s < 4; ++s) af[s] = mine ? ld16(zr + 8 * s) : zero_u4();
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int j = 0; j < NJ; ++j) {
                         floatx4 tt = mfma_bf16(af[0], bq[j][0], zero4());
                         tt = mfma_bf16(af[1], bq[j][1], tt);
                         tt = mfma_bf16(af[2], bq[j][2], tt);
@@ -280,17 +281,17 @@ pf_gemm(LayerArgs a) {
         }
     }
 
-    // ---- store: lane holds rows WM wm + 16 i + 4 c + v, column 16 j + li of its wave's block
+    // ---- store: lane holds rows 16 i + 4 c + v, column 16 j + li of its wave's block
     float* out = MODE == PF_HS ? a.hs : a.o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int row = t.r0 + WM * wm + 16 * i + 4 * c + v;
+            const int row = t.r0 + 16 * i + 4 * c + v;
             if (row >= t.r1) continue;
             float* orow = out + (size_t)row * N + t.n0 + WN * wn + li;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) orow[16 * j] = acc[i][j][v];
+            for (int j = 0; j < NJ; ++j) orow[16 * j] = acc[i][j][v];
         }
 }
 
