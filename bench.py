@@ -127,6 +127,8 @@ def kernel_flops(D, idx):
         "gemm_z2": 2 * R * r * h,
         "lora_in_down": 2 * R * rL * h,
         "gemm_down": 2 * R * d * h + 2 * R * d * r + 2 * R * d * rL,
+        "pf_z1": 2 * R * r * d,
+        "pf_z2": 2 * R * r * h,
         "pf_shared_up": 2 * U * h * d + 2 * U * h * rL,
         "pf_delta_up_act": 2 * R * h * r,
         "pf_down": 2 * R * d * h + 2 * R * d * r + 2 * R * d * rL,

@@ -44,7 +44,7 @@ int check_dims(const edge_moe_dims* p) {
 }
 
 struct Layout {
-    size_t bm, pre, total, eoff, uoff, etile, gtile_u, gtile_r;
+    size_t bm, pre, total, eoff, uoff, etile, etile_pf, gtile_u, gtile_r;
     size_t row_tok, row_slot, row_exp, row_u, slot_row, ut_tok;
     size_t xg, z1, zl, hs, act, z2, zl2, o;
     size_t logits;
@@ -70,6 +70,7 @@ Layout make_layout(const edge_moe_dims& d) {
     L.eoff = take((E + 1) * 4);
     L.uoff = take((L.G + 1) * 4);
     L.etile = take((E + 1) * 4);
+    L.etile_pf = take((E + 1) * 4);
     L.gtile_u = take((L.G + 1) * 4);
     L.gtile_r = take((L.G + 1) * 4);
     L.row_tok = take(L.R * 4);
@@ -262,6 +263,7 @@ static em::DispatchBufs dispatch_bufs(const Layout& L, char* base) {
     db.eoff = reinterpret_cast<int32_t*>(base + L.eoff);
     db.uoff = reinterpret_cast<int32_t*>(base + L.uoff);
     db.etile = reinterpret_cast<int32_t*>(base + L.etile);
+    db.etile_pf = reinterpret_cast<int32_t*>(base + L.etile_pf);
     db.gtile_u = reinterpret_cast<int32_t*>(base + L.gtile_u);
     db.gtile_r = reinterpret_cast<int32_t*>(base + L.gtile_r);
     db.row_tok = reinterpret_cast<int32_t*>(base + L.row_tok);

@@ -64,51 +64,61 @@ perm_rank(const uint32_t* __restrict__ bm, uint32_t* __restrict__ pre,
 }
 
 // Single workgroup: offsets of experts and groups and the per-segment m-tile
-// prefixes used to map workgroups of the GEMM kernels onto segments.
+// prefixes used to map workgroups of the GEMM kernels onto segments (mt-row
+// tiles for the general kernels, kPfTileRows-row tiles per expert for the
+// tiled prefill GEMMs).
 __global__ void __launch_bounds__(256)
 perm_offsets(const int32_t* __restrict__ total, int E, int G, int P, int mt,
              int32_t* __restrict__ eoff, int32_t* __restrict__ uoff,
-             int32_t* __restrict__ etile, int32_t* __restrict__ gtile_u,
+             int32_t* __restrict__ etile, int32_t* __restrict__ etile_pf, int32_t* __restrict__ gtile_u,
              int32_t* __restrict__ gtile_r) {
-    __shared__ int srow[256], stile[256];
+    __shared__ int srow[256], stile[256], stile2[256];
     __shared__ int s_eoff[1025];
     const int tid = threadIdx.x;
     const int per = (E + 255) / 256;         // <= 4
-    int cr[4], ct[4], sr = 0, st = 0;
+    int cr[4], ct[4], ct2[4], sr = 0, st = 0, st2 = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = tid * per + i;
         cr[i] = (i < per && e < E) ? total[e] : 0;
         ct[i] = (cr[i] + mt - 1) / mt;
+        ct2[i] = (cr[i] + kPfTileRows - 1) / kPfTileRows;
         sr += cr[i];
         st += ct[i];
+        st2 += ct2[i];
     }
     srow[tid] = sr;
     stile[tid] = st;
+    stile2[tid] = st2;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
         const int a = tid >= off ? srow[tid - off] : 0;
         const int b = tid >= off ? stile[tid - off] : 0;
+        const int b2 = tid >= off ? stile2[tid - off] : 0;
         __syncthreads();
         srow[tid] += a;
         stile[tid] += b;
+        stile2[tid] += b2;
         __syncthreads();
     }
-    int ra = tid ? srow[tid - 1] : 0, ta = tid ? stile[tid - 1] : 0;
+    int ra = tid ? srow[tid - 1] : 0, ta = tid ? stile[tid - 1] : 0, ta2 = tid ? stile2[tid - 1] : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = tid * per + i;
         if (i < per && e < E) {
             eoff[e] = ra;
             etile[e] = ta;
+            etile_pf[e] = ta2;
             s_eoff[e] = ra;
             ra += cr[i];
             ta += ct[i];
+            ta2 += ct2[i];
         }
     }
     if (tid == 255) {
         eoff[E] = srow[255];
         etile[E] = stile[255];
+        etile_pf[E] = stile2[255];
         s_eoff[E] = srow[255];
     }
     __syncthreads();
@@ -188,7 +198,7 @@ hipError_t launch_dispatch(const int32_t* idx, const DispatchBufs& db, int T, in
     perm_rank<<<E + G, 256, 0, stream>>>(db.bm, db.pre, db.total, W);
     prof_end(stream, "perm_rank");
     prof_begin(stream);
-    perm_offsets<<<1, 256, 0, stream>>>(db.total, E, G, P, mt, db.eoff, db.uoff, db.etile,
+    perm_offsets<<<1, 256, 0, stream>>>(db.total, E, G, P, mt, db.eoff, db.uoff, db.etile, db.etile_pf,
                                        db.gtile_u, db.gtile_r);
     prof_end(stream, "perm_offsets");
     prof_begin(stream);

@@ -414,7 +414,13 @@ static void launch_gemm(const LayerArgs& a, int tiles, int N, hipStream_t s, con
 
 hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
     // a4-a6 inputs: R1 (per row) and R2 (per distinct token of a group)
-    launch_gemm<M_Z1>(a, a.max_etiles, a.r, s, "gemm_z1");
+    const bool pf_z = a.pf && a.r == KC;                 // rank-128 inputs on the tiled GEMM
+    if (pf_z) {
+        const hipError_t e = launch_prefill_gemm(a, PF_Z1, a.rmax, s);
+        if (e != hipSuccess) return e;
+    } else {
+        launch_gemm<M_Z1>(a, a.max_etiles, a.r, s, "gemm_z1");
+    }
     prof_begin(s);
     lora_in<0><<<a.max_gtiles_u, 256, 0, s>>>(a);
     prof_end(s, "lora_in_up");
@@ -434,7 +440,12 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
         launch_gemm<M_ACT>(a, a.max_etiles, a.h, s, "gemm_delta_up_act");
     }
     // a9 / a10 inputs: R4 (per row), R5 (per row)
-    launch_gemm<M_Z2>(a, a.max_etiles, a.r, s, "gemm_z2");
+    if (pf_z) {
+        const hipError_t e = launch_prefill_gemm(a, PF_Z2, a.rmax, s);
+        if (e != hipSuccess) return e;
+    } else {
+        launch_gemm<M_Z2>(a, a.max_etiles, a.r, s, "gemm_z2");
+    }
     prof_begin(s);
     lora_in<1><<<a.max_gtiles_r, 256, 0, s>>>(a);
     prof_end(s, "lora_in_down");

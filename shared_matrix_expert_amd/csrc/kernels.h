@@ -18,6 +18,7 @@ struct DispatchBufs {
     int32_t* eoff;      // [E+1] first row of each expert
     int32_t* uoff;      // [G+1] first unique-token slot of each group
     int32_t* etile;     // [E+1] m-tile prefix over experts
+    int32_t* etile_pf;  // [E+1] prefix of 128-row tiles over experts (tiled prefill GEMMs)
     int32_t* gtile_u;   // [G+1] m-tile prefix over groups' unique tokens
     int32_t* gtile_r;   // [G+1] m-tile prefix over groups' rows
     int32_t* row_tok;   // [R] token of each row
@@ -108,8 +109,9 @@ hipError_t launch_gather_rows(const void* src, const int32_t* index, void* dst, 
                               int64_t row_bytes, hipStream_t stream);
 
 // LDS-tiled shared-matrix GEMMs of large batches (prefill.hip)
-enum PfMode { PF_HS = 0, PF_OUT = 1 };
+enum PfMode { PF_HS = 0, PF_OUT = 1, PF_Z1 = 2, PF_Z2 = 3 };
 constexpr int kPfSpareRows = 128;    // readable rows past the end of xg and act (one row tile)
+constexpr int kPfTileRows = 128;     // rows per tile of the tiled prefill GEMMs
 bool prefill_gemm_ok(int d, int h, int r, int rL, int gq);
 hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, hipStream_t s);
 hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);

@@ -33,12 +33,23 @@ namespace em {
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 128;
+constexpr int BM = kPfTileRows, BK = 128;
 constexpr int PF_WAVES = 8, PF_TH = 64 * PF_WAVES;
 constexpr int SLOTS = BK / 8;                    // 16-byte slots per activation row
-constexpr int WN = BN / PF_WAVES;                // columns per wave (wave w: columns WN w)
-constexpr int NJ = WN / 16, NI = BM / 16;        // 16x16 subtiles per wave (all BM rows)
+constexpr int NI = BM / 16;                      // 16-row subtiles per wave (all BM rows)
 static_assert(BM <= kPfSpareRows, "the last row tile reads up to BM - 1 rows past the end");
+
+// Per mode: the shared products (HS, OUT) tile 256 columns, the rank-128
+// inputs of the deltas (Z1 = A_up x, Z2 = A_dn a) their 128; each wave takes
+// WN = BN / 8 columns of all BM rows.
+template <int MODE>
+struct PfCfg {
+    static constexpr bool Z = MODE == PF_Z1 || MODE == PF_Z2;
+    static constexpr int BN = Z ? 128 : 256;
+    static constexpr int WN = BN / PF_WAVES;     // columns per wave (wave w: columns WN w)
+    static constexpr int NJ = WN / 16;           // 16-column subtiles per wave
+    static constexpr int STEP_VM = NJ + BN / 128 + BM / 32;   // vector-memory instructions per step
+};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -48,16 +59,33 @@ typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 struct PfTile {
-    int g;          // group
+    int g;          // group (HS, OUT) or expert (Z1, Z2)
     int r0, r1;     // rows [r0, r1) of the tile (r1 - r0 <= BM)
     int n0;         // first output column
 };
 
-// Tile b of the launch: row tiles of the groups in group order, columns fastest.
+// Tile b of the launch.  HS, OUT: row tiles of the groups in group order,
+// columns fastest.  Z1, Z2: the experts' row tiles in expert order (one column
+// tile), found by bisecting the per-expert tile prefix.
 template <int MODE>
 EM_DEV bool pf_tile(const LayerArgs& a, int b, int ntn, PfTile& t) {
+    if constexpr (PfCfg<MODE>::Z) {
+        const int32_t* tp = a.db.etile_pf;
+        if (b >= tp[a.E]) return false;
+        int lo = 0, hi = a.E;                    // tp[lo] <= b < tp[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tp[mid] <= b) lo = mid;
+            else hi = mid;
+        }
+        t.g = lo;
+        t.r0 = a.db.eoff[lo] + (b - tp[lo]) * BM;
+        t.r1 = min(a.db.eoff[lo + 1], t.r0 + BM);
+        t.n0 = 0;
+        return true;
+    }
     int m = b / ntn;
-    t.n0 = (b % ntn) * BN;
+    t.n0 = (b % ntn) * PfCfg<MODE>::BN;
     for (int g = 0; g < a.G; ++g) {
         const int r0 = MODE == PF_HS ? a.db.uoff[g] : a.db.eoff[g * a.P];
         const int r1 = MODE == PF_HS ? a.db.uoff[g + 1] : a.db.eoff[(g + 1) * a.P];
@@ -82,6 +110,7 @@ EM_DEV bool pf_tile(const LayerArgs& a, int b, int ntn, PfTile& t) {
 struct PfSrc {
     const uint16_t* a;              // round 0's activation row, at this lane's 16-byte segment
     size_t a_step;                  // elements between rounds (32 rows)
+    const uint16_t* ag[BM / 32];    // Z1: each round's gathered x row (at the lane's segment)
     const uint8_t* b;               // round 0's weight column, at this lane's 16-byte segment
     size_t b_step;                  // bytes between rounds (128 columns)
     const uint16_t* s;              // scale row of this lane's first column
@@ -110,24 +139,28 @@ EM_DEV void pf_src(PfSrc& p, const uint16_t* A, size_t lda, const uint8_t* Wt, s
 }
 
 // Step k0's loads: the scales of this lane's NJ columns first, then the weight
-// and activation tiles (6 DMA instructions per thread).
-EM_DEV void pf_fetch(uint4* As, uint4* Bs, uint32_t (&sb)[NJ], const PfSrc& p, int gq, int k0) {
+// and activation tiles (BN / 128 + 4 DMA instructions per thread).
+template <int MODE>
+EM_DEV void pf_fetch(uint4* As, uint4* Bs, uint32_t (&sb)[PfCfg<MODE>::NJ], const PfSrc& p, int gq, int k0) {
     const int w = wave_id();
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) sb[j] = p.s[(size_t)(16 * j) * p.sstride + k0 / gq];
+    for (int j = 0; j < PfCfg<MODE>::NJ; ++j) sb[j] = p.s[(size_t)(16 * j) * p.sstride + k0 / gq];
 #pragma unroll
-    for (int i = 0; i < BN / 128; ++i)
+    for (int i = 0; i < PfCfg<MODE>::BN / 128; ++i)
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.b + i * p.b_step + (k0 >> 1)),
                                          (lds_ptr_t)(Bs + (128 * i + 16 * w) * 4), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BM / 32; ++i)
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.a + i * p.a_step + k0),
-                                         (lds_ptr_t)(As + (32 * i + 4 * w) * SLOTS), 16, 0, 0);
+    for (int i = 0; i < BM / 32; ++i) {
+        const uint16_t* src = MODE == PF_Z1 ? p.ag[i] + k0 : p.a + i * p.a_step + k0;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(As + (32 * i + 4 * w) * SLOTS), 16, 0, 0);
+    }
 }
-constexpr int PF_STEP_VM = NJ + BN / 128 + BM / 32;    // vector-memory instructions per step and thread
 
 // acc[i][j] += (A rows of subtile i) x (16 x scale_j x dequant(B_j)) over one chunk.
-EM_DEV void pf_compute(floatx4 (&acc)[NI][NJ], const uint4* As, const uint4* Bs, const uint32_t (&sbits)[NJ]) {
+template <int MODE>
+EM_DEV void pf_compute(floatx4 (&acc)[NI][PfCfg<MODE>::NJ], const uint4* As, const uint4* Bs,
+                       const uint32_t (&sbits)[PfCfg<MODE>::NJ]) {
+    constexpr int NJ = PfCfg<MODE>::NJ, WN = PfCfg<MODE>::WN;
     const int l = lane_id(), c = l >> 4, li = l & 15;
     const int wn = wave_id();
     uint4 bq[NJ][4];
@@ -161,11 +194,11 @@ EM_DEV void pf_compute(floatx4 (&acc)[NI][NJ], const uint4* As, const uint4* Bs,
 // into X's predecessor, then wait until only step k + 2's loads are in flight.
 #define PF_STEP(X, XN, K0)                                                        \
     if ((K0) + 2 * BK < K) {                                                      \
-        pf_fetch(As##XN, Bs##XN, s##XN, src, gq, (K0) + 2 * BK);                  \
-        pf_compute(acc, As##X, Bs##X, s##X);                                      \
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF_STEP_VM));                       \
+        pf_fetch<MODE>(As##XN, Bs##XN, s##XN, src, gq, (K0) + 2 * BK);            \
+        pf_compute<MODE>(acc, As##X, Bs##X, s##X);                                \
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(Cfg::STEP_VM));                     \
     } else {                                                                      \
-        pf_compute(acc, As##X, Bs##X, s##X);                                      \
+        pf_compute<MODE>(acc, As##X, Bs##X, s##X);                                \
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                \
     }                                                                             \
     __syncthreads();                                                              \
@@ -174,31 +207,42 @@ EM_DEV void pf_compute(floatx4 (&acc)[NI][NJ], const uint4* As, const uint4* Bs,
 template <int MODE>
 __global__ void __launch_bounds__(PF_TH)
 pf_gemm(LayerArgs a) {
+    using Cfg = PfCfg<MODE>;
+    constexpr int BN = Cfg::BN, WN = Cfg::WN, NJ = Cfg::NJ;
+    constexpr bool Z = Cfg::Z;
     __shared__ uint4 As0[BM * SLOTS];
     __shared__ uint4 As1[BM * SLOTS];
     __shared__ uint4 As2[BM * SLOTS];
     __shared__ uint4 Bs0[BN * 4];
     __shared__ uint4 Bs1[BN * 4];
     __shared__ uint4 Bs2[BN * 4];
-    const int ntn = (MODE == PF_HS ? a.h : a.d) / BN;
+    const int ntn = Z ? 1 : (MODE == PF_HS ? a.h : a.d) / BN;
     // XCD-aware order: XCD x = blockIdx % 8 takes tiles [x * per, (x + 1) * per)
     const int per = gridDim.x >> 3;
     const int b = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     PfTile t;
     if (!pf_tile<MODE>(a, b, ntn, t)) return;
 
-    const int K = MODE == PF_HS ? a.d : a.h;
-    const int N = MODE == PF_HS ? a.h : a.d;
+    const int K = (MODE == PF_HS || MODE == PF_Z1) ? a.d : a.h;
+    const int N = Z ? a.r : (MODE == PF_HS ? a.h : a.d);
     const int gq = min(a.gq, K);
     const uint16_t* A = MODE == PF_HS ? a.xg : a.act;
-    const uint8_t* W = MODE == PF_HS ? a.s_up : a.s_dn;
-    const uint16_t* S = MODE == PF_HS ? a.s_up_s : a.s_dn_s;
+    const uint8_t* W = MODE == PF_HS ? a.s_up : (MODE == PF_OUT ? a.s_dn : (MODE == PF_Z1 ? a.a_up : a.a_dn));
+    const uint16_t* S = MODE == PF_HS ? a.s_up_s : (MODE == PF_OUT ? a.s_dn_s : (MODE == PF_Z1 ? a.a_up_s : a.a_dn_s));
     const int l = lane_id(), wv = wave_id(), c = l >> 4, li = l & 15;
     const int wn = wv;
 
     PfSrc src;
     pf_src(src, A, (size_t)K, W + ((size_t)t.g * N + t.n0) * (K / 2), (size_t)(K / 2),
            S + ((size_t)t.g * N + t.n0 + WN * wn + li) * (K / gq), (size_t)(K / gq), t.r0);
+    if constexpr (MODE == PF_Z1) {
+        // x rows of the tile's tokens (rows past r1 repeat the last row)
+        const int rsub = 4 * wv + (l >> 4);
+        const int seg = (l & 15) ^ (rsub & 15);
+#pragma unroll
+        for (int i = 0; i < BM / 32; ++i)
+            src.ag[i] = a.x + (size_t)a.db.row_tok[min(t.r0 + 32 * i + rsub, t.r1 - 1)] * a.d + 8 * seg;
+    }
 
     floatx4 acc[NI][NJ];
 #pragma unroll
@@ -208,14 +252,30 @@ pf_gemm(LayerArgs a) {
 
     // ---- main loop: three buffer sets, loads two steps ahead of the math (K >= 3 BK)
     uint32_t s0[NJ], s1[NJ], s2[NJ];
-    pf_fetch(As0, Bs0, s0, src, gq, 0);
-    pf_fetch(As1, Bs1, s1, src, gq, BK);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF_STEP_VM));
+    pf_fetch<MODE>(As0, Bs0, s0, src, gq, 0);
+    pf_fetch<MODE>(As1, Bs1, s1, src, gq, BK);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(Cfg::STEP_VM));
     __syncthreads();
     for (int k0 = 0; k0 < K; k0 += 3 * BK) {
         PF_STEP(0, 2, k0)
         PF_STEP(1, 0, k0 + BK)
         PF_STEP(2, 1, k0 + 2 * BK)
+    }
+
+    // ---- R1 / R4 inputs: rounded to bf16, no further terms
+    if constexpr (Z) {
+        uint16_t* out = MODE == PF_Z1 ? a.z1 : a.z2;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = t.r0 + 16 * i + 4 * c + v;
+                if (row >= t.r1) continue;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    out[(size_t)row * a.r + WN * wn + 16 * j + li] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+            }
+        return;
     }
 
     // ---- LoRA branch: V[g] (bf16 [N][rL]) x the rounded LoRA input rows (bf16 [rows][rLp])
@@ -390,12 +450,27 @@ pf_gather_x(const uint16_t* __restrict__ x, const int32_t* __restrict__ ut_tok, 
 }
 
 bool prefill_gemm_ok(int d, int h, int r, int rL, int gq) {
+    constexpr int BN = PfCfg<PF_HS>::BN;
     return gq % KC == 0 && r % KC == 0 && rL % 8 == 0 && rL <= 32 && d % BN == 0 && h % BN == 0 &&
            d >= 3 * BK && h >= 3 * BK;
 }
 
 hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, hipStream_t s) {
-    const int ntn = (mode == PF_HS ? a.h : a.d) / BN;
+    if (mode == PF_Z1 || mode == PF_Z2) {
+        // >= sum over experts of ceil(rows_e / BM)
+        int64_t blocks = max_rows / BM + (a.E < max_rows ? a.E : max_rows) + 1;
+        blocks = (blocks + 7) & ~7ll;
+        prof_begin(s);
+        if (mode == PF_Z1) {
+            pf_gemm<PF_Z1><<<(unsigned)blocks, PF_TH, 0, s>>>(a);
+            prof_end(s, "pf_z1");
+        } else {
+            pf_gemm<PF_Z2><<<(unsigned)blocks, PF_TH, 0, s>>>(a);
+            prof_end(s, "pf_z2");
+        }
+        return hipGetLastError();
+    }
+    const int ntn = (mode == PF_HS ? a.h : a.d) / PfCfg<PF_HS>::BN;
     const int64_t mt = max_rows / BM + a.G + 1;          // >= sum over groups of ceil(rows_g / BM)
     int64_t blocks = mt * ntn;
     blocks = (blocks + 7) & ~7ll;
