@@ -1002,6 +1002,111 @@ struct DnRing {
     uint32_t s[4];
 };
 
+// Reorders the 8 bf16 of an A fragment to the K order (0,4,1,5,2,6,3,7) that
+// dq_offset produces for the B side.
+EM_DEV uint4 k_interleave(uint4 v) {
+    return make_uint4((v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
+                      (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u));
+}
+
+// Eight two's-complement int4 codes q of one 32-bit word to four bf16 pairs
+// holding 136 + q exactly: flipping each nibble's sign bit gives q + 8 in
+// 0..15, which becomes the low mantissa bits below the exponent of 128.  The
+// pairs come out in the K order (0,4,1,5,2,6,3,7).
+EM_DEV uint4 dq_offset(uint32_t w) {
+    constexpr uint32_t M = 0x000F000Fu, C = 0x43004300u;
+    w ^= 0x88888888u;
+    return make_uint4((w & M) | C, ((w >> 4) & M) | C, ((w >> 8) & M) | C, ((w >> 12) & M) | C);
+}
+
+// Delta down for the rows of one pass (sorted by expert): acc[ms] (output rows
+// ms*16 + 4c + q, this lane's column ncol) += B_dn[e(row)][ncol] . z2[row].
+// Expert u of the pass (dexp[u], rows [dstart[u], dstart[u + 1])) owns the rows
+// whose rank (expert starts at or before the row, less one) is u.  Each
+// expert's product runs over the z2 rows of the 16-row subtiles that hold its
+// rows, and only its own rows' outputs are kept.  The codes enter the MFMA as
+// 136 + q (exact in bf16), so the product is corrected by 136 times the row
+// sums of z2 (one product against a ones operand); both operands take the K
+// order of dq_offset.  The B_dn rows of four experts are in flight while four are used.
+template <int NS>
+EM_DEV void delta_down_pass(floatx4 (&acc)[NS], const DecodeArgs& a, const int* dexp, const int* dstart,
+                            uint64_t starts, int prow, const int (&slot_i)[NS], int ncol) {
+    const int nexp = __popcll(starts);
+    const int lane = lane_id(), c = lane >> 4;
+    uint4 af[NS][4];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) af[ms][s] = k_interleave(ld16(a.z2 + (size_t)slot_i[ms] * KC + 32 * c + 8 * s));
+    // expert rank of each output row (-1 past the pass's rows)
+    int rko[NS][4];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = ms * 16 + 4 * c + q;
+            rko[ms][q] = i < prow ? __popcll(starts & ((2ull << i) - 1ull)) - 1 : -1;
+        }
+    floatx4 zc[NS];
+    {
+        const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) {
+            floatx4 t = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) t = mfma_bf16(af[ms][s], ones, t);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) zc[ms][q] = 136.0f * t[q];
+        }
+    }
+    auto fetch = [&](DnRing& r, int u0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = dexp[min(u0 + q, nexp - 1)];
+            r.w[q] = ld16(a.b_dn + ((size_t)e * a.d + ncol) * (KC / 2) + 16 * c);
+            r.s[q] = a.b_dn_s[(size_t)e * a.d + ncol];
+        }
+    };
+    auto consume = [&](const DnRing& r, int u0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int u = u0 + q;
+            if (u >= nexp) break;
+            const int r0 = dstart[u], r1 = u + 1 < nexp ? dstart[u + 1] : prow;
+            uint4 b[4];
+            b[0] = dq_offset(r.w[q].x);
+            b[1] = dq_offset(r.w[q].y);
+            b[2] = dq_offset(r.w[q].z);
+            b[3] = dq_offset(r.w[q].w);
+            const float sc = fp16_bits_to_f32((uint16_t)r.s[q]);
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) {
+                if (r1 <= 16 * ms || r0 >= 16 * ms + 16) continue;
+                floatx4 t = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) t = mfma_bf16(af[ms][s], b[s], t);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    acc[ms][qq] = fmaf(rko[ms][qq] == u ? sc : 0.0f, t[qq] - zc[ms][qq], acc[ms][qq]);
+            }
+        }
+    };
+    DnRing d0, d1;
+    fetch(d0, 0);
+    int u0 = 0;
+    for (; u0 + 8 <= nexp; u0 += 8) {
+        fetch(d1, u0 + 4);
+        consume(d0, u0);
+        fetch(d0, u0 + 8);
+        consume(d1, u0 + 4);
+    }
+    if (u0 < nexp) {
+        fetch(d1, u0 + 4);
+        consume(d0, u0);
+        consume(d1, u0 + 4);
+    }
+}
+
 template <int NS, bool LDSP>
 __global__ void __launch_bounds__(256)
 dec_down(DecodeArgs a) {
@@ -1012,6 +1117,7 @@ dec_down(DecodeArgs a) {
     __shared__ StreamLds<LNS, LKB> L;
     __shared__ int arow_l[16 * NS];
     __shared__ int dexp_l[16 * NS];
+    __shared__ int dstart_l[16 * NS];
     __shared__ int gcnt[64];
     rv_load(v, a.idx, a.R);
     // rows per group, hence the passes that carry rows: only those workgroups
@@ -1098,61 +1204,14 @@ dec_down(DecodeArgs a) {
         if (lane >= 1 && lane - 1 < prow) prev_e = v.idx[v.rows[m0 + lane - 1]];
         uint64_t starts = __ballot(lane < prow && (lane == 0 || my_e != prev_e));
         if (LDSP && fast) {
-            // Expert u of the pass (in row order) owns the rows whose rank, the
-            // number of expert starts at or before the row less one, is u.  The
-            // A rows (R4 outputs) are the same for every expert, only the row mask
-            // changes.  Each expert needs one 16-byte weight load and one scale
-            // per lane; two sets of four experts alternate, so that one set is
-            // in flight while the other is consumed, with every load
-            // unconditional (indices past the last expert repeat it).
-            const int nexp = __popcll(starts);
-            if (wv == 0 && ((starts >> lane) & 1ull))
-                dexp_l[__popcll(starts & ((2ull << lane) - 1ull)) - 1] = my_e;
-            int rk[NS];
-            uint4 af[NS][4];
-#pragma unroll
-            for (int ms = 0; ms < NS; ++ms) {
-                const int i = ms * 16 + li;
-                rk[ms] = i < prow ? __popcll(starts & ((2ull << i) - 1ull)) - 1 : -1;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) af[ms][s] = ld16(a.z2 + (size_t)slot_i[ms] * KC + 32 * c + 8 * s);
+            // distinct experts of the pass in row order, and their first rows
+            if (wv == 0 && ((starts >> lane) & 1ull)) {
+                const int u = __popcll(starts & ((2ull << lane) - 1ull)) - 1;
+                dexp_l[u] = my_e;
+                dstart_l[u] = lane;
             }
             __syncthreads();
-            auto fetch = [&](DnRing& r, int u0) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int e = dexp_l[min(u0 + q, nexp - 1)];
-                    r.w[q] = ld16(a.b_dn + ((size_t)e * a.d + ncol) * (KC / 2) + 16 * c);
-                    r.s[q] = a.b_dn_s[(size_t)e * a.d + ncol];
-                }
-            };
-            auto consume = [&](const DnRing& r, int u0) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int u = u0 + q;
-                    if (u >= nexp) break;
-                    uint4 am[NS][4];
-#pragma unroll
-                    for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) am[ms][s] = rk[ms] == u ? af[ms][s] : zero_u4();
-                    mac_fast<NS>(acc, am, r.w[q], r.s[q]);
-                }
-            };
-            DnRing d0, d1;
-            fetch(d0, 0);
-            int u0 = 0;
-            for (; u0 + 8 <= nexp; u0 += 8) {
-                fetch(d1, u0 + 4);
-                consume(d0, u0);
-                fetch(d0, u0 + 8);
-                consume(d1, u0 + 4);
-            }
-            if (u0 < nexp) {
-                fetch(d1, u0 + 4);
-                consume(d0, u0);
-                consume(d1, u0 + 4);
-            }
+            delta_down_pass<NS>(acc, a, dexp_l, dstart_l, starts, prow, slot_i, ncol);
         } else if (fast) {
             // the A rows (R4 outputs of this pass) are the same for every expert;
             // only the row mask changes.  Each expert needs one 16-byte weight
@@ -1259,6 +1318,135 @@ dec_down(DecodeArgs a) {
     }
 }
 
+// ---- shared down, wave-streamed ----------------------------------------------------
+// Batches of at most 16 slots (every group's rows fit one 16-row subtile), r =
+// 128, quant groups of 128.  A workgroup of 8 waves takes (group, 128 output
+// columns); each wave streams the int4 S_dn rows of its 16 columns (full-line
+// loads, four blocks ahead) against the group's activation rows staged
+// through LDS in pieces of 1024 elements per row (8 or 16 rows, chosen by the
+// row count), then adds the LoRA down V_dn zl2 and the delta down of each
+// distinct expert.  The per-slot outputs go to the workspace, and the column
+// block's last arriving workgroup forms y.  With every group's rows in one
+// workgroup, each light group of a decode step fills 32 compute units with
+// one full-rate stream.
+constexpr int DNW_WAVES = 8;
+constexpr int DNW_COLS = 16 * DNW_WAVES;
+constexpr int DNW_THREADS = 64 * DNW_WAVES;
+
+struct DnwLds {
+    __attribute__((aligned(16))) uint16_t xs[2 * WS_PIECE];   // two staged activation pieces (128 KB)
+    ws_u4 tile[DNW_WAVES * WS_TILE];                           // one transposition tile per wave
+    int arow[32];                                              // staged row -> slot
+    int dexp[32];                                              // distinct experts of the pass, in row order
+    int dstart[32];                                            // first row of each
+};
+
+template <int RP>
+EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb, int m0, int prow) {
+    constexpr int NS = WsPiece<RP, DNW_THREADS>::NS;
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    const int ncol = nb * DNW_COLS + wv * 16 + li;
+    if ((int)threadIdx.x < RP) L.arow[threadIdx.x] = v.rows[m0 + min((int)threadIdx.x, prow - 1)];
+    // distinct experts of the pass and their first rows: rows are sorted by
+    // expert, so an expert starts where the row's expert differs from the
+    // previous row's
+    int my_e = -1, prev_e = -1;
+    if (lane < prow) my_e = v.idx[v.rows[m0 + lane]];
+    if (lane >= 1 && lane - 1 < prow) prev_e = v.idx[v.rows[m0 + lane - 1]];
+    const uint64_t starts = __ballot(lane < prow && (lane == 0 || my_e != prev_e));
+    if (wv == 0 && ((starts >> lane) & 1ull)) {
+        const int u = __popcll(starts & ((2ull << lane) - 1ull)) - 1;
+        L.dexp[u] = my_e;
+        L.dstart[u] = lane;
+    }
+    __syncthreads();
+    int slot_i[NS];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) slot_i[ms] = L.arow[min(ms * 16 + li, RP - 1)];
+    // LoRA down operands, in flight during the stream
+    const uint16_t* vrow = a.ld_v + ((size_t)g * a.d + ncol) * a.rL;
+    const uint4 lvt = ld16(vrow + min(8 * c, a.rL - 8));
+    uint4 lzt[NS];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) lzt[ms] = ld16(a.zl2 + (size_t)slot_i[ms] * a.rLp + min(8 * c, a.rLp - 8));
+
+    // shared down
+    floatx4 acc[NS];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+    {
+        WsSrc src;
+        const size_t r0 = (size_t)g * a.d + nb * DNW_COLS + wv * 16;
+        ws_src(src, a.s_dn + r0 * (a.h / 2), (size_t)(a.h / 2), a.s_dn_s + r0 * (a.h / KC), (size_t)(a.h / KC));
+        WsPieceSrc<RP, DNW_THREADS> q;
+        ws_piece_src<RP, DNW_THREADS>(q, a.act, (size_t)a.h, L.arow);
+        ws_gemm_pieces<RP, DNW_THREADS, NS>(acc, src, a.h, q, L.xs, L.tile + wv * WS_TILE);
+    }
+    // LoRA down: K = rL <= 32 in one product
+    {
+        const uint4 lv = 8 * c < a.rL ? lvt : zero_u4();
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(8 * c < a.rL ? lzt[ms] : zero_u4(), lv, acc[ms]);
+    }
+    delta_down_pass<NS>(acc, a, L.dexp, L.dstart, starts, prow, slot_i, ncol);
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int i = ms * 16 + 4 * c + qq;
+            if (i < prow) st_agent(&a.o[(size_t)v.rows[m0 + i] * a.d + ncol], acc[ms][qq]);
+        }
+}
+
+__global__ void __launch_bounds__(DNW_THREADS)
+dec_down_ws(DecodeArgs a) {
+    __shared__ RouteView v;
+    __shared__ DnwLds L;
+    __shared__ int gcnt[64];
+    rv_load(v, a.idx, a.R);
+    if ((int)threadIdx.x < 64) gcnt[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.R; i += blockDim.x) atomicAdd(&gcnt[v.idx[i] / a.P], 1);
+    __syncthreads();
+    // passes that carry rows: only they arrive at the column block's counter
+    int live_passes = 0;
+    for (int gg = 0; gg < a.G; ++gg) live_passes += (gcnt[gg] + 31) / 32;
+    const int nbd = a.d / DNW_COLS;
+    const int per_pass = a.G * nbd;
+    const int pass = blockIdx.x / per_pass;
+    const int loc = blockIdx.x % per_pass;
+    // a group's column blocks on one XCD (workgroups go to the XCDs in turn),
+    // so that its activation rows are read into one L2
+    const int bx = per_pass % 8 == 0 ? (loc & 7) * (per_pass / 8) + (loc >> 3) : loc;
+    const int g = bx / nbd, nb = bx % nbd;
+    const int m0 = pass * 32;
+    const int prow = min(gcnt[g] - m0, 32);
+    if (prow <= 0) return;
+    rv_group_rows(v, g, a.T, a.k, a.P, a.R);
+    if (prow > 8) dnw_pass<16>(a, v, L, g, nb, m0, prow);
+    else dnw_pass<8>(a, v, L, g, nb, m0, prow);
+
+    // ---- the last workgroup of this column block forms y = sum_j w_j o_j in slot order
+    if (!arrive_last(v, &a.cnt_c[nb], (uint32_t)live_passes)) return;
+    for (int i = threadIdx.x; i < a.T * DNW_COLS; i += blockDim.x) {
+        const int t = i / DNW_COLS, col = nb * DNW_COLS + (i % DNW_COLS);
+        float acc = 0.f;
+        for (int j0 = 0; j0 < a.k; j0 += 8) {
+            float wv8[8], ov8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = min(j0 + u, a.k - 1);
+                wv8[u] = a.topk_w[t * a.k + j];
+                ov8[u] = ld_agent(&a.o[(size_t)(t * a.k + j) * a.d + col]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (j0 + u < a.k) acc = fmaf(wv8[u], ov8[u], acc);
+        }
+        a.y[(size_t)t * a.d + col] = acc;
+    }
+}
+
 // ------------------------------------------------------------------ launcher -------
 // Workgroups of `kernel` (256 threads) that fit on the current device at once:
 // compute units x resident workgroups per unit, cached per kernel and device.
@@ -1276,6 +1464,14 @@ static int resident_grid(K kernel) {
     }
     return cached[dev];
 }
+// Shapes the wave-streamed shared down takes: at most 16 slots, quant groups
+// of 128, r = 128, LoRA rank a multiple of 8 up to 32, h a multiple of one
+// staged piece (1024 elements) and whole 128-column blocks.
+static bool down_ws_ok(const DecodeArgs& a) {
+    return a.R <= 16 && a.gq == KC && a.r == KC && a.rL % 8 == 0 && a.rL <= 32 && a.rL > 0 && a.h % 1024 == 0 &&
+           a.d % DNW_COLS == 0 && a.P <= 64 && a.T <= 64 && a.G <= 64;
+}
+
 template <int NS, bool LDSP>
 static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
     const int nbh = a.h / 64, nbr = (a.r + 63) / 64;
@@ -1291,11 +1487,16 @@ static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
         dec_act_direct<NS><<<a.nxmax * a.ncb2, 256, 0, s>>>(a);
         prof_end(s, "dec_act_direct");
     }
-    const int g3 = a.npass * a.G * (a.d / 64);
     prof_begin(s);
-    if (ns_down == 2) dec_down<2, LDSP><<<g3, 256, 0, s>>>(a);
-    else dec_down<4, LDSP><<<g3, 256, 0, s>>>(a);
-    prof_end(s, "dec_down");
+    if (LDSP && ns_down == 2 && down_ws_ok(a)) {
+        dec_down_ws<<<a.npass * a.G * (a.d / DNW_COLS), DNW_THREADS, 0, s>>>(a);
+        prof_end(s, "dec_down_ws");
+    } else {
+        const int g3 = a.npass * a.G * (a.d / 64);
+        if (ns_down == 2) dec_down<2, LDSP><<<g3, 256, 0, s>>>(a);
+        else dec_down<4, LDSP><<<g3, 256, 0, s>>>(a);
+        prof_end(s, "dec_down");
+    }
     return hipGetLastError();
 }
 

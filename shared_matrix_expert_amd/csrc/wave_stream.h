@@ -57,9 +57,11 @@ struct WsAct {
 };
 
 // Consume one block: transpose through the wave tile T, then the two chunks'
-// MFMAs against the activation rows at stage offset k0.
+// MFMAs against the activation rows at stage offset k0 (rows displaced by boff
+// elements: the second of two stage buffers).
 template <int NS>
-EM_DEV void ws_block(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t spair, ws_u4* T, const WsAct& ar, int k0) {
+EM_DEV void ws_block(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t spair, ws_u4* T, const WsAct& ar, int k0,
+                     int boff = 0) {
     const int l = lane_id(), c = l >> 4, li = l & 15;
     T[(l >> 3) * WS_TP + (l & 7)] = w0;
     T[(8 + (l >> 3)) * WS_TP + (l & 7)] = w1;
@@ -73,7 +75,7 @@ EM_DEV void ws_block(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t spair, ws_
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int seg = (k0 >> 3) + (((16 * ch + 4 * c + s) ^ ar.sw[ms]) & 15) + ((16 * ch + 4 * c + s) & ~15);
-                af[ms][s] = *reinterpret_cast<const uint4*>(ar.row[ms] + 8 * seg);
+                af[ms][s] = *reinterpret_cast<const uint4*>(ar.row[ms] + boff + 8 * seg);
             }
         mac_fast<NS>(acc, af, raw, ch ? (spair >> 16) : (spair & 0xFFFFu));
     }
@@ -105,6 +107,114 @@ EM_DEV void ws_gemm(floatx4 (&acc)[NS], const WsSrc& p0, int kw, ws_u4* T, const
     if (b < nb) {                       // two blocks left
         ws_block<NS>(acc, a0, a1, as0, T, ar, b * WS_KB);
         ws_block<NS>(acc, a2, a3, as1, T, ar, (b + 1) * WS_KB);
+    }
+}
+
+// ---- activation rows staged in pieces ------------------------------------------
+// When the activation rows of a K range do not fit in LDS, the workgroup stages
+// them in pieces (RP rows x SK elements, at most 32 KB, XOR-swizzled as above),
+// two pieces resident: the one being read and the next, which is loaded into
+// registers one piece ahead and written at the piece boundary.  The waves'
+// weight streams run on across the boundary (a barrier with no memory fence:
+// only this wave's LDS accesses are waited for), so a piece boundary costs one
+// barrier, not a refill of the weight pipeline.
+constexpr int WS_PIECE = 16384;          // elements per piece buffer (32 KB)
+
+template <int RP, int NT>
+struct WsPiece {
+    static constexpr int SK = WS_PIECE / RP < 1024 ? WS_PIECE / RP : 1024;   // elements per row and piece
+    static constexpr int BPS = SK / WS_KB;              // weight blocks per piece
+    static constexpr int NS = RP > 16 ? 2 : 1;          // 16-row MFMA subtiles
+    static constexpr int U = RP * SK / 8 / NT;          // 16-byte loads per thread and piece
+};
+
+// This thread's share of a piece: global source at K = 0 and LDS offset.
+template <int RP, int NT>
+struct WsPieceSrc {
+    const uint16_t* g[WsPiece<RP, NT>::U];
+    int l[WsPiece<RP, NT>::U];
+};
+
+// rows[r] (r < RP): the activation row that staged row r holds.
+template <int RP, int NT>
+EM_DEV void ws_piece_src(WsPieceSrc<RP, NT>& q, const uint16_t* act, size_t stride, const int* rows) {
+    using P = WsPiece<RP, NT>;
+    constexpr int SPR = P::SK / 8;                      // 16-byte segments per staged row
+#pragma unroll
+    for (int u = 0; u < P::U; ++u) {
+        const int i = (int)threadIdx.x + NT * u, r = i / SPR, sg = i % SPR;
+        q.g[u] = act + (size_t)rows[r] * stride + 8 * sg;
+        q.l[u] = r * P::SK + 8 * ((sg & ~15) | ((sg & 15) ^ (r & 15)));
+    }
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses only; the empty
+// asm statements keep the compiler from moving memory accesses across it.
+EM_DEV void ws_lds_barrier() {
+    asm volatile("" ::: "memory");
+    // vmcnt and expcnt left free, lgkmcnt = 0 (gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// acc += (this wave's 16 weight rows) . A over K (a multiple of SK and of
+// WS_RING blocks), with A's RP rows staged through xs (2 x WS_PIECE elements).  The
+// weight loads run WS_RING blocks ahead in a ring of single-block register
+// slots: a slot is refilled right after its block is consumed, and the loop
+// body covers the whole ring, so no value moves between slots.  All NT
+// threads of the workgroup call this with the same K.
+constexpr int WS_RING = 4;
+
+template <int RP, int NT, int NS>
+EM_DEV void ws_gemm_pieces(floatx4 (&acc)[NS], const WsSrc& p, int K, const WsPieceSrc<RP, NT>& q, uint16_t* xs,
+                           ws_u4* T) {
+    using P = WsPiece<RP, NT>;
+    static_assert(NS == P::NS, "subtiles of the staged rows");
+    static_assert(WS_RING % P::BPS == 0, "piece boundaries fall on ring boundaries");
+    const int li = lane_id() & 15;
+    WsAct ar;
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) {
+        const int r = min(ms * 16 + li, RP - 1);
+        ar.row[ms] = xs + r * P::SK;
+        ar.sw[ms] = r & 15;
+    }
+    const int nb = K / WS_KB, npc = K / P::SK;
+    uint4 xa[P::U];
+    auto piece_fetch = [&](int pc) {
+        const int k = min(pc, npc - 1) * P::SK;         // past the end: the last piece again
+#pragma unroll
+        for (int u = 0; u < P::U; ++u) xa[u] = ld16(q.g[u] + k);
+    };
+    auto piece_store = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < P::U; ++u) *reinterpret_cast<uint4*>(xs + buf * WS_PIECE + q.l[u]) = xa[u];
+    };
+    piece_fetch(0);
+    ws_u4 w0[WS_RING], w1[WS_RING];
+    uint32_t sp[WS_RING];
+#pragma unroll
+    for (int j = 0; j < WS_RING; ++j) ws_fetch(w0[j], w1[j], sp[j], p, j, nb);
+    piece_store(0);
+    piece_fetch(1);
+    ws_lds_barrier();
+    for (int b = 0; b < nb; b += WS_RING) {
+#pragma unroll
+        for (int j = 0; j < WS_RING; ++j) {
+            const int blk = b + j;
+            const int buf = (blk / P::BPS) & 1;
+            ws_block<NS>(acc, w0[j], w1[j], sp[j], T, ar, (j % P::BPS) * WS_KB, buf * WS_PIECE);
+            ws_fetch(w0[j], w1[j], sp[j], p, blk + WS_RING, nb);
+            if ((j + 1) % P::BPS == 0) {
+                // piece boundary: the next piece goes into the other buffer
+                // (read last in the piece before this one, which every wave has
+                // left), then the one after it is fetched
+                piece_store(buf ^ 1);
+                ws_lds_barrier();
+                piece_fetch(blk / P::BPS + 2);
+            }
+        }
     }
 }
 
