@@ -80,6 +80,12 @@ def kernel_bytes(D, idx: np.ndarray):
                    + U * h * 4 + R * r * 4 + U * rL * 4 + R * h * 2 + R * (r + rL) * 2,
         "dec_down": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2
                     + R * (r + rL) * 2 + R * 4 + T * d * 4,
+        # the wave-streamed down kernels (row-major, decode-tiled shared matrix)
+        # move the same algorithmic bytes
+        "dec_down_ws": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2
+                       + R * (r + rL) * 2 + R * 4 + T * d * 4,
+        "dec_down_wst": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2
+                        + R * (r + rL) * 2 + R * 4 + T * d * 4,
         # general (prefill) path
         "gemm_z1": X * per["a_up"] + R * d * 2 + R * r * 2,
         "lora_in_up": G * per["lu_u"] + U * d * 2,
@@ -156,7 +162,7 @@ class Workload:
                 "wr_host": wr, "bias_host": bias,
                 "wr": torch.from_numpy(wr.view(np.int16)).cuda(),
                 "bias": None if bias is None else torch.from_numpy(bias).cuda(),
-                "W": self._weights(synth, cfg_id, seed, layer, host_init),
+                "W": self._weights(synth, cfg_id, seed, layer, host_init, em, self.D),
             })
         D = self.D
         self.ws = torch.empty(em.edge_moe_workspace_bytes(D), dtype=torch.uint8, device="cuda")
@@ -166,12 +172,18 @@ class Workload:
         self.stream = torch.cuda.current_stream()
 
     @staticmethod
-    def _weights(synth, cfg_id, seed, layer, host_init):
+    def _weights(synth, cfg_id, seed, layer, host_init, em, D):
         """Weights made on the device, or (host_init) on the host and copied over,
-        so that no kernel but the library's runs in the process (counter runs)."""
+        so that no kernel but the library's runs in the process (counter runs).
+        Decode batches also get the decode-tiled copies of the shared matrices,
+        written once here by the library (a stored format, outside any step)."""
         if not host_init:
-            return synth.make_weights(cfg_id, seed, layer, device="cuda")
-        return {k: v.cuda() for k, v in synth.make_weights(cfg_id, seed, layer, device="cpu").items()}
+            W = synth.make_weights(cfg_id, seed, layer, device="cuda")
+        else:
+            W = {k: v.cuda() for k, v in synth.make_weights(cfg_id, seed, layer, device="cpu").items()}
+        if D.T <= 16 and D.quant_group == 128 and D.d % 256 == 0 and D.h % 256 == 0:
+            W = em.tile_weights(D, W)
+        return W
 
     def step(self, i):
         L = self.layers[i % len(self.layers)]
@@ -278,7 +290,7 @@ class Stack:
         for layer in range(self.n_layers):
             wr, _ = synth.make_router(4, seed, layer)
             self.layers.append({"wr": torch.from_numpy(wr.view(np.int16)).cuda(),
-                                "W": Workload._weights(synth, 4, seed, layer, host_init)})
+                                "W": Workload._weights(synth, 4, seed, layer, host_init, em, self.D)})
         D = self.D
         self.ws = torch.empty(em.edge_moe_workspace_bytes(D), dtype=torch.uint8, device="cuda")
         self.idx = torch.empty(D.T, D.top_k, dtype=torch.int32, device="cuda")

@@ -27,7 +27,7 @@ EDGE_MOE_EHIP = -4
 
 EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_forward_traced", "edge_moe_residual", "edge_moe_status_string",
-            "edge_moe_abi_version", "edge_moe_copy",
+            "edge_moe_abi_version", "edge_moe_copy", "edge_moe_tile_shared",
             "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset")
 
 
@@ -39,11 +39,15 @@ class CDims(ctypes.Structure):
 
 _WEIGHT_FIELDS = ("s_up_q", "s_up_scale", "s_dn_q", "s_dn_scale", "a_up_q", "a_up_scale",
                   "b_up_q", "b_up_scale", "a_dn_q", "a_dn_scale", "b_dn_q", "b_dn_scale",
-                  "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v")
-# keys of the weight dicts made by the input generator -> struct fields
+                  "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v",
+                  "s_up_t", "s_up_tscale", "s_dn_t", "s_dn_tscale")
+# keys of the weight dicts made by the input generator -> struct fields (the
+# last four, the decode-tiled shared matrices, are optional)
 _WEIGHT_KEYS = ("s_up", "s_up_scale", "s_dn", "s_dn_scale", "a_up", "a_up_scale",
                 "b_up", "b_up_scale", "a_dn", "a_dn_scale", "b_dn", "b_dn_scale",
-                "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v")
+                "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v",
+                "s_up_t", "s_up_tscale", "s_dn_t", "s_dn_tscale")
+_OPTIONAL_KEYS = ("s_up_t", "s_up_tscale", "s_dn_t", "s_dn_tscale")
 
 
 class CWeights(ctypes.Structure):
@@ -92,6 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_moe_residual.restype = i32
     lib.edge_moe_copy.argtypes = [vp, vp, sz, vp]
     lib.edge_moe_copy.restype = i32
+    lib.edge_moe_tile_shared.argtypes = [ctypes.POINTER(CDims), ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.edge_moe_tile_shared.restype = i32
     lib.edge_moe_status_string.argtypes = [i32]
     lib.edge_moe_status_string.restype = ctypes.c_char_p
     lib.edge_moe_abi_version.argtypes = []
@@ -128,7 +134,29 @@ def _stream(stream) -> Optional[int]:
 
 
 def cweights(weights: dict) -> CWeights:
-    return CWeights(*(_ptr(weights[k]) for k in _WEIGHT_KEYS))
+    return CWeights(*(_ptr(weights.get(k) if k in _OPTIONAL_KEYS else weights[k]) for k in _WEIGHT_KEYS))
+
+
+def edge_moe_tile_shared(dims, which, src_q, src_scale, dst_q, dst_scale, stream=None) -> None:
+    """Decode-tiled copy of s_up (which=0) or s_dn (which=1) into dst_q / dst_scale."""
+    st = load().edge_moe_tile_shared(ctypes.byref(cdims(dims)), int(which), _ptr(src_q), _ptr(src_scale),
+                                     _ptr(dst_q), _ptr(dst_scale), _stream(stream))
+    if st != EDGE_MOE_OK:
+        raise EdgeMoeError("edge_moe_tile_shared", st)
+
+
+def tile_weights(dims, weights: dict, stream=None) -> dict:
+    """A copy of the weight dict with the decode-tiled shared matrices added
+    (new device tensors of the same sizes as s_up / s_dn and their scales)."""
+    import torch
+    out = dict(weights)
+    for which, key in ((0, "s_up"), (1, "s_dn")):
+        q = torch.empty_like(weights[key])
+        sc = torch.empty_like(weights[key + "_scale"])
+        edge_moe_tile_shared(dims, which, weights[key], weights[key + "_scale"], q, sc, stream)
+        out[key + "_t"] = q
+        out[key + "_tscale"] = sc
+    return out
 
 
 def status_string(status: int) -> str:

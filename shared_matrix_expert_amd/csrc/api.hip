@@ -146,6 +146,12 @@ DecLayout make_dec_layout(const edge_moe_dims& d) {
 
 bool aligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) == 0; }
 
+// Shapes the decode-tiled shared matrices take: quant groups of 128, d and h
+// multiples of 256 (whole tile groups of 128 rows and blocks of 256).
+bool tile_shape_ok(const edge_moe_dims& d) {
+    return d.quant_group == 128 && d.d % 256 == 0 && d.h % 256 == 0;
+}
+
 // gfx950 check, cached per device
 int check_device() {
     static std::mutex mu;
@@ -305,6 +311,9 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.a_up = wt->a_up_q; a.a_up_s = wt->a_up_scale; a.b_up = wt->b_up_q; a.b_up_s = wt->b_up_scale;
     a.a_dn = wt->a_dn_q; a.a_dn_s = wt->a_dn_scale; a.b_dn = wt->b_dn_q; a.b_dn_s = wt->b_dn_scale;
     a.lu_u = wt->lora_up_u; a.lu_v = wt->lora_up_v; a.ld_u = wt->lora_dn_u; a.ld_v = wt->lora_dn_v;
+    if (wt->s_up_t) {
+        a.s_up_t = wt->s_up_t; a.s_up_ts = wt->s_up_tscale; a.s_dn_t = wt->s_dn_t; a.s_dn_ts = wt->s_dn_tscale;
+    }
     a.hs = reinterpret_cast<float*>(base + L.hs);
     a.z1p = reinterpret_cast<float*>(base + L.z1p);
     a.zlp = reinterpret_cast<float*>(base + L.zlp);
@@ -352,6 +361,15 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
                              wt->lora_up_u, wt->lora_up_v, wt->lora_dn_u, wt->lora_dn_v};
     for (const void* p : wptrs)
         if (!aligned(p, 16)) return EDGE_MOE_EINVAL;
+    // the tiled copies: none or all four
+    const void* tptrs[4] = {wt->s_up_t, wt->s_up_tscale, wt->s_dn_t, wt->s_dn_tscale};
+    const int ntiled = (tptrs[0] != nullptr) + (tptrs[1] != nullptr) + (tptrs[2] != nullptr) + (tptrs[3] != nullptr);
+    if (ntiled != 0 && ntiled != 4) return EDGE_MOE_EINVAL;
+    if (ntiled == 4) {
+        if (!aligned(tptrs[0], 16) || !aligned(tptrs[2], 16) || !aligned(tptrs[1], 4) || !aligned(tptrs[3], 4))
+            return EDGE_MOE_EINVAL;
+        if (!tile_shape_ok(*dims)) return EDGE_MOE_EUNSUPPORTED;
+    }
     if (!ws) return EDGE_MOE_EWORKSPACE;
     if (!aligned(ws, kAlign)) return EDGE_MOE_EINVAL;
     const Layout L = make_layout(*dims);
@@ -433,6 +451,30 @@ int edge_moe_residual(int32_t T, int32_t d, const uint16_t* x, const float* y, u
     if (st != EDGE_MOE_OK) return st;
     return em::launch_residual(T, d, x, y, x_out, (hipStream_t)stream) == hipSuccess ? EDGE_MOE_OK
                                                                                      : EDGE_MOE_EHIP;
+}
+
+int edge_moe_tile_shared(const edge_moe_dims* dims, int32_t which, const uint8_t* src_q,
+                         const uint16_t* src_scale, uint8_t* dst_q, uint16_t* dst_scale, void* stream) {
+    const int st = check_dims(dims);
+    if (st != EDGE_MOE_OK) return st;
+    if (which != 0 && which != 1) return EDGE_MOE_EINVAL;
+    if (!aligned(src_q, 16) || !aligned(dst_q, 16) || !aligned(src_scale, 4) || !aligned(dst_scale, 4))
+        return EDGE_MOE_EINVAL;
+    if (!tile_shape_ok(*dims)) return EDGE_MOE_EUNSUPPORTED;
+    const int G = dims->n_experts / dims->experts_per_group;
+    const int N = which == 0 ? dims->h : dims->d, K = which == 0 ? dims->d : dims->h;
+    const size_t qb = (size_t)G * N * K / 2, sb = (size_t)G * N * (K / 128) * 2;
+    const char* s8 = reinterpret_cast<const char*>(src_q);
+    const char* d8 = reinterpret_cast<const char*>(dst_q);
+    if (d8 < s8 + qb && s8 < d8 + qb) return EDGE_MOE_EINVAL;
+    const char* ss = reinterpret_cast<const char*>(src_scale);
+    const char* ds = reinterpret_cast<const char*>(dst_scale);
+    if (ds < ss + sb && ss < ds + sb) return EDGE_MOE_EINVAL;
+    const int dst_st = check_device();
+    if (dst_st != EDGE_MOE_OK) return dst_st;
+    return em::launch_tile_shared(src_q, src_scale, dst_q, dst_scale, G, N, K, (hipStream_t)stream) == hipSuccess
+               ? EDGE_MOE_OK
+               : EDGE_MOE_EHIP;
 }
 
 int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream) {

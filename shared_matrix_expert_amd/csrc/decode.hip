@@ -248,7 +248,7 @@ dec_up(DecodeArgs a) {
     // the LDS streams of the R1 / R2 tasks and the staged x of the wave-streamed
     // shared up share one buffer (a workgroup runs one task)
     constexpr size_t HS_XS = 32768;                    // bytes of x per stage
-    constexpr size_t HS_SM = HS_XS + 4 * WS_TILE * 16;
+    constexpr size_t HS_SM = HS_XS + 4 * 2 * WS_TILE * 16;
     constexpr size_t SM = sizeof(StreamLds<LNS, LKB>) > HS_SM ? sizeof(StreamLds<LNS, LKB>) : HS_SM;
     __shared__ RouteView v;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SM];
@@ -283,18 +283,24 @@ dec_up(DecodeArgs a) {
             const int rp = nrows <= 8 ? 8 : 16;
             const int KX = (int)(HS_XS / 2) / rp;
             uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-            ws_u4* T = reinterpret_cast<ws_u4*>(smem + HS_XS) + wv * WS_TILE;
+            ws_u4* T = reinterpret_cast<ws_u4*>(smem + HS_XS) + wv * 2 * WS_TILE;
             WsAct ar;
             const int arw = min(li, rp - 1);
             ar.row[0] = xs + (size_t)arw * KX;
             ar.sw[0] = arw & 15;
+            // Row-major weights: tiles rb * 4 + wv of the 128 rows; decode-tiled
+            // weights: tiles 2 wv + rb (each wave reads 4 KB contiguous per block)
+            const bool tiled = a.s_up_t != nullptr;
             WsSrc src[HS_RB];
+            WsSrcT srct[HS_RB];
             floatx4 acc[HS_RB][1];
 #pragma unroll
             for (int rb = 0; rb < HS_RB; ++rb) {
                 const size_t r0 = (size_t)g * a.h + (nb0 + rb) * 64 + wv * 16;
                 ws_src(src[rb], a.s_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.s_up_s + r0 * (a.d / KC),
                        (size_t)(a.d / KC));
+                const size_t tg = (size_t)g * (a.h / 128) + nb0 / 2;     // tile group (128 rows)
+                ws_src_t(srct[rb], a.s_up_t + tg * 64 * a.d, a.s_up_ts + tg * a.d, 2 * wv + rb);
                 acc[rb][0] = zero4();
             }
             constexpr int XU = HS_XS / 16 / 256;          // 16-byte pieces per thread and stage
@@ -313,12 +319,12 @@ dec_up(DecodeArgs a) {
                     *reinterpret_cast<uint4*>(xs + (size_t)r * KX + 8 * ((sg & ~15) | ((sg & 15) ^ (r & 15)))) = xv[u];
                 }
                 __syncthreads();
-#pragma unroll
-                for (int rb = 0; rb < HS_RB; ++rb) ws_gemm<1>(acc[rb], src[rb], ks, T, ar, KX);
+                if (tiled) ws_gemm2_t<1>(acc[0], acc[1], srct[0], srct[1], ks, ar, KX);
+                else ws_gemm2<1>(acc[0], acc[1], src[0], src[1], ks, T, ar, KX);
             }
 #pragma unroll
             for (int rb = 0; rb < HS_RB; ++rb) {
-                const int ncol = (nb0 + rb) * 64 + wv * 16 + li;
+                const int ncol = tiled ? nb0 * 64 + (2 * wv + rb) * 16 + li : (nb0 + rb) * 64 + wv * 16 + li;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int i = 4 * c + q;
@@ -1341,7 +1347,7 @@ struct DnwLds {
     int dstart[32];                                            // first row of each
 };
 
-template <int RP>
+template <int RP, bool TILED>
 EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb, int m0, int prow) {
     constexpr int NS = WsPiece<RP, DNW_THREADS>::NS;
     const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
@@ -1375,12 +1381,21 @@ EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb
 #pragma unroll
     for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
     {
-        WsSrc src;
-        const size_t r0 = (size_t)g * a.d + nb * DNW_COLS + wv * 16;
-        ws_src(src, a.s_dn + r0 * (a.h / 2), (size_t)(a.h / 2), a.s_dn_s + r0 * (a.h / KC), (size_t)(a.h / KC));
         WsPieceSrc<RP, DNW_THREADS> q;
         ws_piece_src<RP, DNW_THREADS>(q, a.act, (size_t)a.h, L.arow);
-        ws_gemm_pieces<RP, DNW_THREADS, NS>(acc, src, a.h, q, L.xs, L.tile + wv * WS_TILE);
+        if constexpr (TILED) {
+            // the workgroup's 128 columns are tile group nb of S_dn[g]
+            const size_t tg = (size_t)g * (a.d / 128) + nb;
+            WsSrcT src;
+            ws_src_t(src, a.s_dn_t + tg * 64 * a.h, a.s_dn_ts + tg * a.h, wv);
+            ws_gemm_pieces<RP, DNW_THREADS, NS>(acc, src, a.h, q, L.xs, L.tile + wv * WS_TILE);
+        } else {
+            WsSrc src;
+            const size_t r0 = (size_t)g * a.d + nb * DNW_COLS + wv * 16;
+            ws_src(src, a.s_dn + r0 * (a.h / 2), (size_t)(a.h / 2), a.s_dn_s + r0 * (a.h / KC),
+                   (size_t)(a.h / KC));
+            ws_gemm_pieces<RP, DNW_THREADS, NS>(acc, src, a.h, q, L.xs, L.tile + wv * WS_TILE);
+        }
     }
     // LoRA down: K = rL <= 32 in one product
     {
@@ -1398,6 +1413,7 @@ EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb
         }
 }
 
+template <bool TILED>
 __global__ void __launch_bounds__(DNW_THREADS)
 dec_down_ws(DecodeArgs a) {
     __shared__ RouteView v;
@@ -1423,8 +1439,9 @@ dec_down_ws(DecodeArgs a) {
     const int prow = min(gcnt[g] - m0, 32);
     if (prow <= 0) return;
     rv_group_rows(v, g, a.T, a.k, a.P, a.R);
-    if (prow > 8) dnw_pass<16>(a, v, L, g, nb, m0, prow);
-    else dnw_pass<8>(a, v, L, g, nb, m0, prow);
+    if (prow > 16) dnw_pass<32, TILED>(a, v, L, g, nb, m0, prow);
+    else if (prow > 8) dnw_pass<16, TILED>(a, v, L, g, nb, m0, prow);
+    else dnw_pass<8, TILED>(a, v, L, g, nb, m0, prow);
 
     // ---- the last workgroup of this column block forms y = sum_j w_j o_j in slot order
     if (!arrive_last(v, &a.cnt_c[nb], (uint32_t)live_passes)) return;
@@ -1464,11 +1481,13 @@ static int resident_grid(K kernel) {
     }
     return cached[dev];
 }
-// Shapes the wave-streamed shared down takes: at most 16 slots, quant groups
-// of 128, r = 128, LoRA rank a multiple of 8 up to 32, h a multiple of one
-// staged piece (1024 elements) and whole 128-column blocks.
-static bool down_ws_ok(const DecodeArgs& a) {
-    return a.R <= 16 && a.gq == KC && a.r == KC && a.rL % 8 == 0 && a.rL <= 32 && a.rL > 0 && a.h % 1024 == 0 &&
+// Shapes the wave-streamed shared down takes: quant groups of 128, r = 128,
+// LoRA rank a multiple of 8 up to 32, h a multiple of one staged piece (1024
+// elements) and whole 128-column blocks; row-major weights only for at most 16
+// slots (there, the light groups of a decode step; the tiled weights stream
+// fast enough for the 32-row passes of larger batches too).
+static bool down_ws_ok(const DecodeArgs& a, bool tiled) {
+    return (tiled || a.R <= 16) && a.gq == KC && a.r == KC && a.rL % 8 == 0 && a.rL <= 32 && a.rL > 0 && a.h % 1024 == 0 &&
            a.d % DNW_COLS == 0 && a.P <= 64 && a.T <= 64 && a.G <= 64;
 }
 
@@ -1488,8 +1507,11 @@ static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
         prof_end(s, "dec_act_direct");
     }
     prof_begin(s);
-    if (LDSP && ns_down == 2 && down_ws_ok(a)) {
-        dec_down_ws<<<a.npass * a.G * (a.d / DNW_COLS), DNW_THREADS, 0, s>>>(a);
+    if (LDSP && ns_down == 2 && a.s_dn_t && down_ws_ok(a, true)) {
+        dec_down_ws<true><<<a.npass * a.G * (a.d / DNW_COLS), DNW_THREADS, 0, s>>>(a);
+        prof_end(s, "dec_down_wst");
+    } else if (LDSP && ns_down == 2 && down_ws_ok(a, false)) {
+        dec_down_ws<false><<<a.npass * a.G * (a.d / DNW_COLS), DNW_THREADS, 0, s>>>(a);
         prof_end(s, "dec_down_ws");
     } else {
         const int g3 = a.npass * a.G * (a.d / 64);

@@ -81,6 +81,60 @@ EM_DEV void ws_block(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t spair, ws_
     }
 }
 
+// Two 16-row tiles against the same activation fragments: one set of A reads
+// serves both, and the two tiles' dequantisation and MFMA chains are
+// independent work for the scheduler to interleave.
+template <int NS>
+EM_DEV void ws_block2(floatx4 (&acc0)[NS], floatx4 (&acc1)[NS], ws_u4 w00, ws_u4 w01, uint32_t sp0, ws_u4 w10,
+                      ws_u4 w11, uint32_t sp1, ws_u4* T, const WsAct& ar, int k0) {
+    const int l = lane_id(), c = l >> 4, li = l & 15;
+    T[(l >> 3) * WS_TP + (l & 7)] = w00;
+    T[(8 + (l >> 3)) * WS_TP + (l & 7)] = w01;
+    T[WS_TILE + (l >> 3) * WS_TP + (l & 7)] = w10;
+    T[WS_TILE + (8 + (l >> 3)) * WS_TP + (l & 7)] = w11;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const ws_u4 t0 = T[li * WS_TP + 4 * ch + c];
+        const ws_u4 t1 = T[WS_TILE + li * WS_TP + 4 * ch + c];
+        uint4 af[NS][4];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int seg = (k0 >> 3) + (((16 * ch + 4 * c + s) ^ ar.sw[ms]) & 15) + ((16 * ch + 4 * c + s) & ~15);
+                af[ms][s] = *reinterpret_cast<const uint4*>(ar.row[ms] + 8 * seg);
+            }
+        mac_fast<NS>(acc0, af, make_uint4(t0.x, t0.y, t0.z, t0.w), ch ? (sp0 >> 16) : (sp0 & 0xFFFFu));
+        mac_fast<NS>(acc1, af, make_uint4(t1.x, t1.y, t1.z, t1.w), ch ? (sp1 >> 16) : (sp1 & 0xFFFFu));
+    }
+}
+
+// ws_gemm for two weight tiles at once (T holds two wave tiles).
+template <int NS>
+EM_DEV void ws_gemm2(floatx4 (&acc0)[NS], floatx4 (&acc1)[NS], const WsSrc& p0, const WsSrc& p1, int kw, ws_u4* T,
+                     const WsAct& ar, int K) {
+    WsSrc q0 = p0, q1 = p1;
+    q0.w += kw / 2;
+    q0.s += kw / 128;
+    q1.w += kw / 2;
+    q1.s += kw / 128;
+    const int nb = K / WS_KB;
+    ws_u4 a00, a01, a10, a11, b00, b01, b10, b11;   // set a: block b, set b: block b + 1 (tiles 0, 1)
+    uint32_t as0, as1, bs0, bs1;
+    ws_fetch(a00, a01, as0, q0, 0, nb);
+    ws_fetch(a10, a11, as1, q1, 0, nb);
+    ws_fetch(b00, b01, bs0, q0, 1, nb);
+    ws_fetch(b10, b11, bs1, q1, 1, nb);
+    for (int b = 0; b < nb; b += 2) {
+        ws_block2<NS>(acc0, acc1, a00, a01, as0, a10, a11, as1, T, ar, b * WS_KB);
+        ws_fetch(a00, a01, as0, q0, b + 2, nb);
+        ws_fetch(a10, a11, as1, q1, b + 2, nb);
+        ws_block2<NS>(acc0, acc1, b00, b01, bs0, b10, b11, bs1, T, ar, (b + 1) * WS_KB);
+        ws_fetch(b00, b01, bs0, q0, b + 3, nb);
+        ws_fetch(b10, b11, bs1, q1, b + 3, nb);
+    }
+}
+
 // acc[ms] += (this wave's 16 rows) . A over K in [kw, kw + K) of the weights and
 // [0, K) of the staged activations; K a multiple of 512.
 template <int NS>
@@ -107,6 +161,97 @@ EM_DEV void ws_gemm(floatx4 (&acc)[NS], const WsSrc& p0, int kw, ws_u4* T, const
     if (b < nb) {                       // two blocks left
         ws_block<NS>(acc, a0, a1, as0, T, ar, b * WS_KB);
         ws_block<NS>(acc, a2, a3, as1, T, ar, (b + 1) * WS_KB);
+    }
+}
+
+// ---- decode-tiled weights --------------------------------------------------------
+// In the decode-tiled layout (defined in the public header) a 1 KB read of one
+// 16-row tile returns to each lane the 32 codes its MFMA operand needs, and the
+// tiles of a 128-row tile group follow each other block by block, so that the
+// waves of a workgroup streaming one tile group read one contiguous region and
+// no transposition through LDS is needed.  The loads are non-temporal: each
+// weight byte is read once per step.
+struct WsSrcT {
+    const uint8_t* w;                   // this wave's tile at block 0, plus 16 lane
+    const uint16_t* s;                  // its scale pairs at block 0, plus 2 (lane % 16)
+};
+
+// tg_q / tg_s: the tile group's codes and scales; t: the tile (0..7).
+EM_DEV void ws_src_t(WsSrcT& p, const uint8_t* tg_q, const uint16_t* tg_s, int t) {
+    const int l = lane_id();
+    p.w = tg_q + (size_t)t * 2048 + 16 * l;
+    p.s = tg_s + t * 32 + 2 * (l & 15);
+}
+
+EM_DEV void ws_fetch_t(ws_u4& w0, ws_u4& w1, uint32_t& sp, const WsSrcT& p, int b, int nb) {
+    const int bb = min(b, nb - 1);                      // past the end: the last block again
+    const uint8_t* q = p.w + (size_t)bb * 16384;
+    w0 = __builtin_nontemporal_load(reinterpret_cast<const ws_u4*>(q));
+    w1 = __builtin_nontemporal_load(reinterpret_cast<const ws_u4*>(q + 1024));
+    sp = *reinterpret_cast<const uint32_t*>(p.s + (size_t)bb * 256);
+}
+
+// One block of a tiled tile: w0 / w1 are the MFMA operands of its two chunks.
+template <int NS>
+EM_DEV void ws_block_t(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t spair, const WsAct& ar, int k0,
+                       int boff = 0) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const ws_u4 t = ch ? w1 : w0;
+        uint4 af[NS][4];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int seg = (k0 >> 3) + (((16 * ch + 4 * c + s) ^ ar.sw[ms]) & 15) + ((16 * ch + 4 * c + s) & ~15);
+                af[ms][s] = *reinterpret_cast<const uint4*>(ar.row[ms] + boff + 8 * seg);
+            }
+        mac_fast<NS>(acc, af, make_uint4(t.x, t.y, t.z, t.w), ch ? (spair >> 16) : (spair & 0xFFFFu));
+    }
+}
+
+// Two tiles of one wave against the same activation fragments (one set of A
+// reads for both), over blocks [kw / 256, + K / 256) of the tiles and [0, K) of
+// the staged activations; K a multiple of 512.
+template <int NS>
+EM_DEV void ws_block2_t(floatx4 (&acc0)[NS], floatx4 (&acc1)[NS], ws_u4 w00, ws_u4 w01, uint32_t sp0, ws_u4 w10,
+                        ws_u4 w11, uint32_t sp1, const WsAct& ar, int k0) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const ws_u4 t0 = ch ? w01 : w00;
+        const ws_u4 t1 = ch ? w11 : w10;
+        uint4 af[NS][4];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int seg = (k0 >> 3) + (((16 * ch + 4 * c + s) ^ ar.sw[ms]) & 15) + ((16 * ch + 4 * c + s) & ~15);
+                af[ms][s] = *reinterpret_cast<const uint4*>(ar.row[ms] + 8 * seg);
+            }
+        mac_fast<NS>(acc0, af, make_uint4(t0.x, t0.y, t0.z, t0.w), ch ? (sp0 >> 16) : (sp0 & 0xFFFFu));
+        mac_fast<NS>(acc1, af, make_uint4(t1.x, t1.y, t1.z, t1.w), ch ? (sp1 >> 16) : (sp1 & 0xFFFFu));
+    }
+}
+
+template <int NS>
+EM_DEV void ws_gemm2_t(floatx4 (&acc0)[NS], floatx4 (&acc1)[NS], const WsSrcT& p0, const WsSrcT& p1, int kw,
+                       const WsAct& ar, int K) {
+    const int b0 = kw / WS_KB, nb = b0 + K / WS_KB;
+    ws_u4 a00, a01, a10, a11, c00, c01, c10, c11;      // set a: block b, set c: block b + 1 (tiles 0, 1)
+    uint32_t as0, as1, cs0, cs1;
+    ws_fetch_t(a00, a01, as0, p0, b0, nb);
+    ws_fetch_t(a10, a11, as1, p1, b0, nb);
+    ws_fetch_t(c00, c01, cs0, p0, b0 + 1, nb);
+    ws_fetch_t(c10, c11, cs1, p1, b0 + 1, nb);
+    for (int b = b0; b < nb; b += 2) {
+        ws_block2_t<NS>(acc0, acc1, a00, a01, as0, a10, a11, as1, ar, (b - b0) * WS_KB);
+        ws_fetch_t(a00, a01, as0, p0, b + 2, nb);
+        ws_fetch_t(a10, a11, as1, p1, b + 2, nb);
+        ws_block2_t<NS>(acc0, acc1, c00, c01, cs0, c10, c11, cs1, ar, (b + 1 - b0) * WS_KB);
+        ws_fetch_t(c00, c01, cs0, p0, b + 3, nb);
+        ws_fetch_t(c10, c11, cs1, p1, b + 3, nb);
     }
 }
 
@@ -166,8 +311,25 @@ EM_DEV void ws_lds_barrier() {
 // threads of the workgroup call this with the same K.
 constexpr int WS_RING = 4;
 
-template <int RP, int NT, int NS>
-EM_DEV void ws_gemm_pieces(floatx4 (&acc)[NS], const WsSrc& p, int K, const WsPieceSrc<RP, NT>& q, uint16_t* xs,
+EM_DEV void ws_fetch_any(ws_u4& w0, ws_u4& w1, uint32_t& sp, const WsSrc& p, int b, int nb) {
+    ws_fetch(w0, w1, sp, p, b, nb);
+}
+EM_DEV void ws_fetch_any(ws_u4& w0, ws_u4& w1, uint32_t& sp, const WsSrcT& p, int b, int nb) {
+    ws_fetch_t(w0, w1, sp, p, b, nb);
+}
+template <int NS>
+EM_DEV void ws_block_any(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t sp, ws_u4* T, const WsAct& ar, int k0,
+                         int boff, const WsSrc&) {
+    ws_block<NS>(acc, w0, w1, sp, T, ar, k0, boff);
+}
+template <int NS>
+EM_DEV void ws_block_any(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t sp, ws_u4*, const WsAct& ar, int k0,
+                         int boff, const WsSrcT&) {
+    ws_block_t<NS>(acc, w0, w1, sp, ar, k0, boff);
+}
+
+template <int RP, int NT, int NS, class Src>
+EM_DEV void ws_gemm_pieces(floatx4 (&acc)[NS], const Src& p, int K, const WsPieceSrc<RP, NT>& q, uint16_t* xs,
                            ws_u4* T) {
     using P = WsPiece<RP, NT>;
     static_assert(NS == P::NS, "subtiles of the staged rows");
@@ -195,7 +357,7 @@ EM_DEV void ws_gemm_pieces(floatx4 (&acc)[NS], const WsSrc& p, int K, const WsPi
     ws_u4 w0[WS_RING], w1[WS_RING];
     uint32_t sp[WS_RING];
 #pragma unroll
-    for (int j = 0; j < WS_RING; ++j) ws_fetch(w0[j], w1[j], sp[j], p, j, nb);
+    for (int j = 0; j < WS_RING; ++j) ws_fetch_any(w0[j], w1[j], sp[j], p, j, nb);
     piece_store(0);
     piece_fetch(1);
     ws_lds_barrier();
@@ -204,8 +366,8 @@ EM_DEV void ws_gemm_pieces(floatx4 (&acc)[NS], const WsSrc& p, int K, const WsPi
         for (int j = 0; j < WS_RING; ++j) {
             const int blk = b + j;
             const int buf = (blk / P::BPS) & 1;
-            ws_block<NS>(acc, w0[j], w1[j], sp[j], T, ar, (j % P::BPS) * WS_KB, buf * WS_PIECE);
-            ws_fetch(w0[j], w1[j], sp[j], p, blk + WS_RING, nb);
+            ws_block_any<NS>(acc, w0[j], w1[j], sp[j], T, ar, (j % P::BPS) * WS_KB, buf * WS_PIECE, p);
+            ws_fetch_any(w0[j], w1[j], sp[j], p, blk + WS_RING, nb);
             if ((j + 1) % P::BPS == 0) {
                 // piece boundary: the next piece goes into the other buffer
                 // (read last in the piece before this one, which every wave has

@@ -22,12 +22,22 @@ def f32_to_dev(a) -> torch.Tensor:
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
-class Layer:
-    """Device buffers for one layer and the two library calls."""
+def tile_ok(D) -> bool:
+    """Shapes the decode-tiled shared matrices take (quant groups of 128, d and h
+    multiples of 256)."""
+    return D.quant_group == 128 and D.d % 256 == 0 and D.h % 256 == 0
 
-    def __init__(self, D, weights: dict):
+
+class Layer:
+    """Device buffers for one layer and the two library calls.  By default the
+    shared matrices also get their decode-tiled copies where the shape allows
+    (as in the benchmark); tiled=False keeps the row-major ones only."""
+
+    def __init__(self, D, weights: dict, tiled=None):
         self.D = D
-        self.W = weights
+        if tiled is None:
+            tiled = bool(weights) and tile_ok(D)
+        self.W = em.tile_weights(D, weights) if tiled else weights
         self.ws = torch.empty(em.edge_moe_workspace_bytes(D), dtype=torch.uint8, device=DEV)
 
     def route(self, x, wr, bias, want_logits=True):
