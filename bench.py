@@ -181,7 +181,7 @@ class Workload:
             W = synth.make_weights(cfg_id, seed, layer, device="cuda")
         else:
             W = {k: v.cuda() for k, v in synth.make_weights(cfg_id, seed, layer, device="cpu").items()}
-        if D.T <= 16 and D.quant_group == 128 and D.d % 256 == 0 and D.h % 256 == 0:
+        if D.T <= 16 and D.quant_group == 128 and D.d % 1024 == 0 and D.h % 1024 == 0:
             W = em.tile_weights(D, W)
         return W
 

@@ -92,11 +92,12 @@ typedef struct edge_moe_dims {
 } edge_moe_dims;
 
 /* Weights of one layer (device pointers, layouts above; 16-byte aligned).
- * The last four members are optional (NULL, or all four set): decode-tiled
- * copies of the shared matrices written by edge_moe_tile_shared.  When they are
- * set, batches of at most 16 tokens stream them instead of s_up_q / s_dn_q (the
- * row-major copies stay required: larger batches and the other paths read
- * them); the two copies must hold the same values. */
+ * The last three members are optional decode-tiled copies of the int4 codes
+ * written by edge_moe_tile_shared (the scales stay in the row-major arrays):
+ * s_up_t and s_dn_t NULL or both set, a_up_t NULL or set.  When they are set,
+ * batches of at most 16 tokens stream them instead of the row-major s_up_q /
+ * s_dn_q / a_up_q (the row-major copies stay required: larger batches and the
+ * other paths read them); both copies must hold the same values. */
 typedef struct edge_moe_weights {
     const uint8_t*  s_up_q;  const uint16_t* s_up_scale;
     const uint8_t*  s_dn_q;  const uint16_t* s_dn_scale;
@@ -106,8 +107,9 @@ typedef struct edge_moe_weights {
     const uint8_t*  b_dn_q;  const uint16_t* b_dn_scale;
     const uint16_t* lora_up_u; const uint16_t* lora_up_v;
     const uint16_t* lora_dn_u; const uint16_t* lora_dn_v;
-    const uint8_t*  s_up_t;  const uint16_t* s_up_tscale;   /* optional, tiled s_up  */
-    const uint8_t*  s_dn_t;  const uint16_t* s_dn_tscale;   /* optional, tiled s_dn  */
+    const uint8_t*  s_up_t;    /* optional, tiled s_up codes */
+    const uint8_t*  s_dn_t;    /* optional, tiled s_dn codes */
+    const uint8_t*  a_up_t;    /* optional, tiled a_up codes */
 } edge_moe_weights;
 
 /* Optional per-stage outputs of edge_moe_forward_traced (device pointers; any
@@ -179,14 +181,15 @@ int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream);
 /* Static description of a status code (never NULL). */
 const char* edge_moe_status_string(int status);
 
-/* Decode-tiled copy of one shared matrix (which = 0: s_up [G][h][d],
- * which = 1: s_dn [G][d][h]), written from the row-major packed int4 matrix
- * src_q and its scales src_scale into dst_q / dst_scale, which have the same
- * sizes (G*N*K/2 bytes and G*N*(K/128) fp16).  A stored-format conversion done
- * once per layer, outside any step: the layer's values are unchanged.
+/* Decode-tiled copy of the int4 codes of one matrix set (which = 0: s_up
+ * [G][h][d], which = 1: s_dn [G][d][h], which = 2: a_up [E][r][d]), written
+ * from the row-major packed codes src_q into dst_q of the same size (M*N*K/2
+ * bytes for M matrices of N x K).  A stored-format conversion done once per
+ * layer, outside any step: the layer's values are unchanged, and the scales
+ * keep their row-major arrays (each row's K/128 scales contiguous).
  *
- * Layout (N x K matrix of group g; requires quant_group == 128, N a multiple
- * of 128, K a multiple of 256): rows form tiles of 16 and tile groups of 8
+ * Layout (N x K matrix g of the set; requires quant_group == 128, N a multiple
+ * of 128, K a multiple of 1024): rows form tiles of 16 and tile groups of 8
  * tiles (128 rows); K forms blocks of 256 (two 128-element chunks).  For tile
  * group n, block b, tile t, chunk c and lane l = i + 16 j (i < 16, j < 4), the
  * 16 bytes at
@@ -194,15 +197,13 @@ const char* edge_moe_status_string(int status);
  * hold elements [(2b + c)*128 + 32 j, +32) of row 128 n + 16 t + i, packed as
  * in the row-major layout.  So one 1 KB read of 64 lanes returns, per lane,
  * the 32 codes of one row that a 16 x 16 x 32 matrix-core operand needs, and
- * a workgroup that streams one tile group reads one contiguous region.  The
- * scales of that row and block (chunks 2b, 2b + 1) are the fp16 pair at
- * element  g*N*K/128 + n*K + b*256 + t*32 + 2 i  of dst_scale.
+ * a workgroup that streams one tile group reads one contiguous region.
  *
- * Errors: EDGE_MOE_EINVAL for null / misaligned pointers (16 bytes for the
- * codes, 4 for the scales) or which not 0 / 1; EDGE_MOE_EUNSUPPORTED when the
- * shape is outside the layout above.  src and dst must not overlap. */
-int edge_moe_tile_shared(const edge_moe_dims* dims, int32_t which, const uint8_t* src_q,
-                         const uint16_t* src_scale, uint8_t* dst_q, uint16_t* dst_scale, void* stream);
+ * Errors: EDGE_MOE_EINVAL for null or not 16-byte aligned pointers, or which
+ * not 0, 1 or 2; EDGE_MOE_EUNSUPPORTED when the shape is outside the layout
+ * above.  src and dst must not overlap. */
+int edge_moe_tile_shared(const edge_moe_dims* dims, int32_t which, const uint8_t* src_q, uint8_t* dst_q,
+                         void* stream);
 
 /* EDGE_MOE_ABI_VERSION of the built library. */
 int edge_moe_abi_version(void);

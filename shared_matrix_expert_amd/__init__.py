@@ -40,14 +40,14 @@ class CDims(ctypes.Structure):
 _WEIGHT_FIELDS = ("s_up_q", "s_up_scale", "s_dn_q", "s_dn_scale", "a_up_q", "a_up_scale",
                   "b_up_q", "b_up_scale", "a_dn_q", "a_dn_scale", "b_dn_q", "b_dn_scale",
                   "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v",
-                  "s_up_t", "s_up_tscale", "s_dn_t", "s_dn_tscale")
+                  "s_up_t", "s_dn_t", "a_up_t")
 # keys of the weight dicts made by the input generator -> struct fields (the
-# last four, the decode-tiled shared matrices, are optional)
+# last three, the decode-tiled codes, are optional)
 _WEIGHT_KEYS = ("s_up", "s_up_scale", "s_dn", "s_dn_scale", "a_up", "a_up_scale",
                 "b_up", "b_up_scale", "a_dn", "a_dn_scale", "b_dn", "b_dn_scale",
                 "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v",
-                "s_up_t", "s_up_tscale", "s_dn_t", "s_dn_tscale")
-_OPTIONAL_KEYS = ("s_up_t", "s_up_tscale", "s_dn_t", "s_dn_tscale")
+                "s_up_t", "s_dn_t", "a_up_t")
+_OPTIONAL_KEYS = ("s_up_t", "s_dn_t", "a_up_t")
 
 
 class CWeights(ctypes.Structure):
@@ -96,7 +96,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_moe_residual.restype = i32
     lib.edge_moe_copy.argtypes = [vp, vp, sz, vp]
     lib.edge_moe_copy.restype = i32
-    lib.edge_moe_tile_shared.argtypes = [ctypes.POINTER(CDims), ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.edge_moe_tile_shared.argtypes = [ctypes.POINTER(CDims), ctypes.c_int32, vp, vp, vp]
     lib.edge_moe_tile_shared.restype = i32
     lib.edge_moe_status_string.argtypes = [i32]
     lib.edge_moe_status_string.restype = ctypes.c_char_p
@@ -137,25 +137,26 @@ def cweights(weights: dict) -> CWeights:
     return CWeights(*(_ptr(weights.get(k) if k in _OPTIONAL_KEYS else weights[k]) for k in _WEIGHT_KEYS))
 
 
-def edge_moe_tile_shared(dims, which, src_q, src_scale, dst_q, dst_scale, stream=None) -> None:
-    """Decode-tiled copy of s_up (which=0) or s_dn (which=1) into dst_q / dst_scale."""
-    st = load().edge_moe_tile_shared(ctypes.byref(cdims(dims)), int(which), _ptr(src_q), _ptr(src_scale),
-                                     _ptr(dst_q), _ptr(dst_scale), _stream(stream))
+def edge_moe_tile_shared(dims, which, src_q, dst_q, stream=None) -> None:
+    """Decode-tiled copy of the codes of s_up (which=0), s_dn (1) or a_up (2)."""
+    st = load().edge_moe_tile_shared(ctypes.byref(cdims(dims)), int(which), _ptr(src_q), _ptr(dst_q),
+                                     _stream(stream))
     if st != EDGE_MOE_OK:
         raise EdgeMoeError("edge_moe_tile_shared", st)
 
 
 def tile_weights(dims, weights: dict, stream=None) -> dict:
-    """A copy of the weight dict with the decode-tiled shared matrices added
-    (new device tensors of the same sizes as s_up / s_dn and their scales)."""
+    """A copy of the weight dict with the decode-tiled codes added (new device
+    tensors of the sizes of s_up / s_dn / a_up; a_up only when its rank is a
+    multiple of 128)."""
     import torch
     out = dict(weights)
-    for which, key in ((0, "s_up"), (1, "s_dn")):
+    for which, key in ((0, "s_up"), (1, "s_dn"), (2, "a_up")):
+        if which == 2 and dims.delta_rank % 128:
+            continue
         q = torch.empty_like(weights[key])
-        sc = torch.empty_like(weights[key + "_scale"])
-        edge_moe_tile_shared(dims, which, weights[key], weights[key + "_scale"], q, sc, stream)
+        edge_moe_tile_shared(dims, which, weights[key], q, stream)
         out[key + "_t"] = q
-        out[key + "_tscale"] = sc
     return out
 
 

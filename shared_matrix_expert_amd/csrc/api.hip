@@ -114,7 +114,7 @@ bool force_old_gemm() {
 }
 
 struct DecLayout {
-    size_t hs, z1p, zlp, act, z2p, z2, zl2, o, cnt_e, cnt_c, bytes;
+    size_t hs, z1p, zlp, act, z2p, z2, zl2, o, cnt_e, cnt_c, scratch, bytes;
     int S1, cb2, ncb2, N2;
     bool lds;
 };
@@ -140,16 +140,18 @@ DecLayout make_dec_layout(const edge_moe_dims& d) {
     L.o = take((size_t)R * d.d * 4);
     L.cnt_e = take((size_t)d.n_experts * 4);
     L.cnt_c = take((size_t)(d.d / 64) * 4);
+    L.scratch = take(64 * 4);
     L.bytes = off;
     return L;
 }
 
 bool aligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) == 0; }
 
-// Shapes the decode-tiled shared matrices take: quant groups of 128, d and h
-// multiples of 256 (whole tile groups of 128 rows and blocks of 256).
-bool tile_shape_ok(const edge_moe_dims& d) {
-    return d.quant_group == 128 && d.d % 256 == 0 && d.h % 256 == 0;
+// Shapes the decode-tiled codes take: quant groups of 128, d and h multiples
+// of 1024 (whole tile groups of 128 rows, blocks of 256, and each row's scales
+// a whole number of 16-byte pieces); for A_up also r a multiple of 128.
+bool tile_shape_ok(const edge_moe_dims& d, int which = 0) {
+    return d.quant_group == 128 && d.d % 1024 == 0 && d.h % 1024 == 0 && (which != 2 || d.delta_rank % 128 == 0);
 }
 
 // gfx950 check, cached per device
@@ -311,9 +313,7 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.a_up = wt->a_up_q; a.a_up_s = wt->a_up_scale; a.b_up = wt->b_up_q; a.b_up_s = wt->b_up_scale;
     a.a_dn = wt->a_dn_q; a.a_dn_s = wt->a_dn_scale; a.b_dn = wt->b_dn_q; a.b_dn_s = wt->b_dn_scale;
     a.lu_u = wt->lora_up_u; a.lu_v = wt->lora_up_v; a.ld_u = wt->lora_dn_u; a.ld_v = wt->lora_dn_v;
-    if (wt->s_up_t) {
-        a.s_up_t = wt->s_up_t; a.s_up_ts = wt->s_up_tscale; a.s_dn_t = wt->s_dn_t; a.s_dn_ts = wt->s_dn_tscale;
-    }
+    a.s_up_t = wt->s_up_t; a.s_dn_t = wt->s_dn_t; a.a_up_t = wt->a_up_t;
     a.hs = reinterpret_cast<float*>(base + L.hs);
     a.z1p = reinterpret_cast<float*>(base + L.z1p);
     a.zlp = reinterpret_cast<float*>(base + L.zlp);
@@ -325,6 +325,7 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.y = y;
     a.cnt_e = reinterpret_cast<uint32_t*>(base + L.cnt_e);
     a.cnt_c = reinterpret_cast<uint32_t*>(base + L.cnt_c);
+    a.scratch = reinterpret_cast<float*>(base + L.scratch);
     hipStream_t s = (hipStream_t)stream;
     hipError_t err = em::launch_decode(a, s);
     if (err != hipSuccess) return EDGE_MOE_EHIP;
@@ -361,14 +362,15 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
                              wt->lora_up_u, wt->lora_up_v, wt->lora_dn_u, wt->lora_dn_v};
     for (const void* p : wptrs)
         if (!aligned(p, 16)) return EDGE_MOE_EINVAL;
-    // the tiled copies: none or all four
-    const void* tptrs[4] = {wt->s_up_t, wt->s_up_tscale, wt->s_dn_t, wt->s_dn_tscale};
-    const int ntiled = (tptrs[0] != nullptr) + (tptrs[1] != nullptr) + (tptrs[2] != nullptr) + (tptrs[3] != nullptr);
-    if (ntiled != 0 && ntiled != 4) return EDGE_MOE_EINVAL;
-    if (ntiled == 4) {
-        if (!aligned(tptrs[0], 16) || !aligned(tptrs[2], 16) || !aligned(tptrs[1], 4) || !aligned(tptrs[3], 4))
-            return EDGE_MOE_EINVAL;
+    // the tiled copies: s_up / s_dn both or neither, a_up optional
+    if ((wt->s_up_t != nullptr) != (wt->s_dn_t != nullptr)) return EDGE_MOE_EINVAL;
+    if (wt->s_up_t) {
+        if (!aligned(wt->s_up_t, 16) || !aligned(wt->s_dn_t, 16)) return EDGE_MOE_EINVAL;
         if (!tile_shape_ok(*dims)) return EDGE_MOE_EUNSUPPORTED;
+    }
+    if (wt->a_up_t) {
+        if (!aligned(wt->a_up_t, 16)) return EDGE_MOE_EINVAL;
+        if (!tile_shape_ok(*dims, 2)) return EDGE_MOE_EUNSUPPORTED;
     }
     if (!ws) return EDGE_MOE_EWORKSPACE;
     if (!aligned(ws, kAlign)) return EDGE_MOE_EINVAL;
@@ -453,28 +455,24 @@ int edge_moe_residual(int32_t T, int32_t d, const uint16_t* x, const float* y, u
                                                                                      : EDGE_MOE_EHIP;
 }
 
-int edge_moe_tile_shared(const edge_moe_dims* dims, int32_t which, const uint8_t* src_q,
-                         const uint16_t* src_scale, uint8_t* dst_q, uint16_t* dst_scale, void* stream) {
+int edge_moe_tile_shared(const edge_moe_dims* dims, int32_t which, const uint8_t* src_q, uint8_t* dst_q,
+                         void* stream) {
     const int st = check_dims(dims);
     if (st != EDGE_MOE_OK) return st;
-    if (which != 0 && which != 1) return EDGE_MOE_EINVAL;
-    if (!aligned(src_q, 16) || !aligned(dst_q, 16) || !aligned(src_scale, 4) || !aligned(dst_scale, 4))
-        return EDGE_MOE_EINVAL;
-    if (!tile_shape_ok(*dims)) return EDGE_MOE_EUNSUPPORTED;
-    const int G = dims->n_experts / dims->experts_per_group;
-    const int N = which == 0 ? dims->h : dims->d, K = which == 0 ? dims->d : dims->h;
-    const size_t qb = (size_t)G * N * K / 2, sb = (size_t)G * N * (K / 128) * 2;
+    if (which < 0 || which > 2) return EDGE_MOE_EINVAL;
+    if (!aligned(src_q, 16) || !aligned(dst_q, 16)) return EDGE_MOE_EINVAL;
+    if (!tile_shape_ok(*dims, which)) return EDGE_MOE_EUNSUPPORTED;
+    const int G = which == 2 ? dims->n_experts : dims->n_experts / dims->experts_per_group;
+    const int N = which == 0 ? dims->h : (which == 1 ? dims->d : dims->delta_rank);
+    const int K = which == 1 ? dims->h : dims->d;
+    const size_t qb = (size_t)G * N * K / 2;
     const char* s8 = reinterpret_cast<const char*>(src_q);
     const char* d8 = reinterpret_cast<const char*>(dst_q);
     if (d8 < s8 + qb && s8 < d8 + qb) return EDGE_MOE_EINVAL;
-    const char* ss = reinterpret_cast<const char*>(src_scale);
-    const char* ds = reinterpret_cast<const char*>(dst_scale);
-    if (ds < ss + sb && ss < ds + sb) return EDGE_MOE_EINVAL;
     const int dst_st = check_device();
     if (dst_st != EDGE_MOE_OK) return dst_st;
-    return em::launch_tile_shared(src_q, src_scale, dst_q, dst_scale, G, N, K, (hipStream_t)stream) == hipSuccess
-               ? EDGE_MOE_OK
-               : EDGE_MOE_EHIP;
+    return em::launch_tile_shared(src_q, dst_q, G, N, K, (hipStream_t)stream) == hipSuccess ? EDGE_MOE_OK
+                                                                                            : EDGE_MOE_EHIP;
 }
 
 int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream) {

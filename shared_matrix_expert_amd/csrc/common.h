@@ -87,7 +87,10 @@ EM_DEV floatx4 fma4(float s, floatx4 t, floatx4 acc) {
 
 // ---------------------------------------------------------------- misc ----------
 EM_DEV int lane_id() { return threadIdx.x & (kWave - 1); }
-EM_DEV int wave_id() { return threadIdx.x >> 6; }
+// The wave's index in the workgroup, in a scalar register: the compiler cannot
+// see on its own that it is uniform across the wave, and loops bounded by it
+// would otherwise be compiled as divergent loops.
+EM_DEV int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // SiLU(v) = v / (1 + e^-v) from the hardware base-2 exponential and reciprocal
 // (v_exp_f32, v_rcp_f32, each within about 1 ulp): a few fp32 ulps from the

@@ -300,7 +300,7 @@ dec_up(DecodeArgs a) {
                 ws_src(src[rb], a.s_up + r0 * (a.d / 2), (size_t)(a.d / 2), a.s_up_s + r0 * (a.d / KC),
                        (size_t)(a.d / KC));
                 const size_t tg = (size_t)g * (a.h / 128) + nb0 / 2;     // tile group (128 rows)
-                ws_src_t(srct[rb], a.s_up_t + tg * 64 * a.d, a.s_up_ts + tg * a.d, 2 * wv + rb);
+                ws_src_t(srct[rb], a.s_up_t + tg * 64 * a.d, a.s_up_s + tg * a.d, a.d / KC, 2 * wv + rb);
                 acc[rb][0] = zero4();
             }
             constexpr int XU = HS_XS / 16 / 256;          // 16-byte pieces per thread and stage
@@ -475,6 +475,296 @@ dec_up(DecodeArgs a) {
                         a.zlp[(((size_t)(s * 4 + wv) * a.T + v.rtok[i]) * a.G + g) * a.rLp + n] = acc[ms][q];
                 }
         }
+    }
+}
+
+// ---- shared up and the R1 / R2 inputs from one work list --------------------------
+// Batches of at most 16 tokens with the decode-tiled S_up and A_up.  Every
+// token's x row is staged in LDS once per workgroup (8 or 16 rows of d), so any
+// wave can take any weight tile.  The work is a list of items: the 16-row tiles
+// of S_up of each group with slots (whole K, 32 KB at d = 4096; outputs for
+// every token, the next kernel reads only the group's tokens), then the K
+// halves of the 16-row tiles of A_up of each distinct expert (outputs kept for
+// the expert's slots, one z1 slice per half).  Wave w takes items w, w + W,
+// w + 2W, ... (W waves in the grid): the eight waves of a workgroup read the
+// eight tiles of one tile group, one contiguous region, and when every group
+// has slots each wave streams two S_up tiles and at most one A_up half.  A
+// wave streams its items as a sequence of K halves through one register ring
+// that runs across item boundaries; the half's source is worked out once per
+// half.  The U_up products (bf16, 16 KB per group and eighth of K) go to the
+// last waves, which carry fewer tiled items.
+constexpr int UPW_WAVES = 8;
+constexpr int UPW_THREADS = 64 * UPW_WAVES;
+constexpr int UPW_XS = 16 * 4096;          // staged x elements (RP rows x d)
+
+constexpr int UPW_XMAX = 256;              // distinct experts (the slots of a batch of <= 16 tokens)
+constexpr int UPW_MAXK = 8;                // work items per wave
+
+struct UpwLds {
+    __attribute__((aligned(16))) uint16_t xs[UPW_XS];
+    int16_t glist[64];                     // groups with slots, ascending
+    int16_t xlist[UPW_XMAX];               // distinct experts, ascending
+    int16_t xslot[UPW_XMAX][16];           // slot of each token for each distinct expert, or -1
+    int ng, nx;
+};
+
+// The route view, the lists of groups with slots and of distinct experts, and
+// each distinct expert's slot per token.
+EM_DEV void upw_lists(const DecodeArgs& a, RouteView& v, UpwLds& L) {
+    rv_load(v, a.idx, a.R);
+    rv_count_experts(v, a.R, a.E);                     // v.ebits: selected experts
+    // expert and group lists from the bitmap, built by wave 0: lane w expands
+    // word w (32 experts) at its prefix offset; lane g tests group g's bits
+    const int nwd = (a.E + 31) >> 5;                    // <= 32 words
+    if (wave_id() == 0) {
+        const int lane = lane_id();
+        const uint32_t word = lane < nwd ? v.ebits[lane] : 0u;
+        int pre = __popc(word);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(pre, off, 64);
+            if (lane >= off) pre += y;
+        }
+        int pos = pre - __popc(word);
+        for (uint32_t b = word; b; b &= b - 1u) L.xlist[pos++] = (int16_t)(lane * 32 + __ffs(b) - 1);
+        if (lane == 63) L.nx = pre;
+        bool live = false;
+        if (lane < a.G) {
+            const int e0 = lane * a.P, e1 = e0 + a.P;  // experts [e0, e1) of group lane
+            for (int w = e0 >> 5; w <= (e1 - 1) >> 5; ++w) {
+                const int lo = max(e0 - 32 * w, 0), hi = min(e1 - 32 * w, 32);
+                const uint32_t m = (hi >= 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
+                live = live || (v.ebits[w] & m) != 0u;
+            }
+        }
+        const uint64_t gl = __ballot(live);
+        if (live) L.glist[__popcll(gl & ((1ull << lane) - 1ull))] = (int16_t)lane;
+        if (lane == 0) L.ng = __popcll(gl);
+    }
+    __syncthreads();
+    // slot of token t for distinct expert xi (-1: the token did not choose it):
+    // every slot finds its expert's rank in the bitmap
+    for (int i = threadIdx.x; i < L.nx * 16; i += blockDim.x) L.xslot[i >> 4][i & 15] = -1;
+    __syncthreads();
+    for (int sl = threadIdx.x; sl < a.R; sl += blockDim.x) {
+        const int e = v.idx[sl], w = e >> 5;
+        int xi = __popc(v.ebits[w] & ((1u << (e & 31)) - 1u));
+        for (int u = 0; u < w; ++u) xi += __popc(v.ebits[u]);
+        L.xslot[xi][sl / a.k] = (int16_t)sl;
+    }
+    __syncthreads();
+}
+
+// One K half of a work item: its tile source, K half and where it ends.
+struct UpwHalf {
+    WsSrcT src;
+    int kh;          // K half (0, 1)
+    int item;        // global item index
+    bool last;       // the item's last half: store after it
+};
+
+template <int RP, int NBH>
+EM_DEV void upw_run(const DecodeArgs& a, RouteView& v, UpwLds& L) {
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    // stage x: RP rows (rows past T repeat row T - 1), 16-byte segments of each
+    // row XOR-swizzled by row % 16 in groups of 16.  The loads go out before
+    // the route view is built, so that their latency overlaps it.
+    constexpr int XU = RP * 4096 / 8 / UPW_THREADS;     // 16-byte pieces per thread at d = 4096
+    const int spr = a.d / 8;
+    uint4 xv[XU];
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+        const int i = (int)threadIdx.x + UPW_THREADS * u;
+        const int r = min(i / spr, RP - 1), sg = i % spr;
+        xv[u] = ld16(a.x + (size_t)min(r, a.T - 1) * a.d + 8 * sg);
+    }
+    upw_lists(a, v, L);
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+        const int i = (int)threadIdx.x + UPW_THREADS * u;
+        const int r = i / spr, sg = i % spr;
+        if (r < RP)
+            *reinterpret_cast<uint4*>(L.xs + (size_t)r * a.d + 8 * ((sg & ~15) | ((sg & 15) ^ (r & 15)))) = xv[u];
+    }
+    __syncthreads();
+    WsAct ar;
+    {
+        const int r = min(li, RP - 1);
+        ar.row[0] = L.xs + (size_t)r * a.d;
+        ar.sw[0] = r & 15;
+    }
+    const int tgh = a.h / 128;                          // S_up tile groups per group
+    const int n_hs = L.ng * tgh * 8;                    // S_up tiles (whole K)
+    const int n_z1 = L.nx * (a.r / 16) * 2;             // A_up tile halves
+    const int n_items = n_hs + n_z1;
+    const int nw = (int)gridDim.x * UPW_WAVES;
+    const int gw = (int)blockIdx.x * UPW_WAVES + wv;
+    const int nk_hs = gw < n_hs ? (n_hs - 1 - gw) / nw + 1 : 0;
+    const int nk = gw < n_items ? (n_items - 1 - gw) / nw + 1 : 0;
+    const int nhalf = 2 * nk_hs + (nk - nk_hs);         // K halves to stream
+    // half hk of this wave (clamped to the last one)
+    auto half_of = [&](int hk, UpwHalf& u) {
+        hk = min(hk, max(nhalf - 1, 0));
+        if (hk < 2 * nk_hs) {
+            const int i = gw + (hk >> 1) * nw;
+            const int t = i & 7, tg = i >> 3;           // tg over (group list, tile group)
+            const int gl = tg / tgh, tgl = tg - gl * tgh;
+            const size_t tgi = (size_t)L.glist[gl] * tgh + tgl;
+            ws_src_t(u.src, a.s_up_t + tgi * 64 * a.d, a.s_up_s + tgi * a.d, a.d / KC, t);
+            u.kh = hk & 1;
+            u.item = i;
+            u.last = (hk & 1) == 1;
+        } else {
+            const int i = gw + (nk_hs + hk - 2 * nk_hs) * nw;
+            const int j = i - n_hs;
+            const int t = j & 7, hh = (j >> 3) & 1, x2 = j >> 4;   // x2 over (expert list, tile group of r)
+            const int xi = x2 / (a.r / 128), tgr = x2 - xi * (a.r / 128);
+            const size_t tgi = (size_t)L.xlist[xi] * (a.r / 128) + tgr;
+            ws_src_t(u.src, a.a_up_t + tgi * 64 * a.d, a.a_up_s + tgi * a.d, a.d / KC, t);
+            u.kh = hh;
+            u.item = i;
+            u.last = true;
+        }
+    };
+    // Outputs are stored after the stream: a global store in the loop would
+    // leave stores and loads pending on the same counter, which the compiler
+    // then treats as completing out of order and answers with full waits.  The
+    // last UPW_MAXK items' results stay in registers, oldest first; rows
+    // without an output write a scratch word.
+    auto store = [&](int i, const floatx4& acc) {
+        float* dst[4];
+        if (i < n_hs) {
+            const int t = i & 7, tg = i >> 3;
+            const int gl = tg / tgh, tgl = tg - gl * tgh;
+            const int g = L.glist[gl];
+            const int col = tgl * 128 + t * 16 + li;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int tok = 4 * c + q;
+                dst[q] = tok < a.T ? a.hs + ((size_t)tok * a.G + g) * a.h + col : a.scratch + lane;
+            }
+        } else {
+            const int j = i - n_hs;
+            const int t = j & 7, hh = (j >> 3) & 1, x2 = j >> 4;
+            const int xi = x2 / (a.r / 128), tgr = x2 - xi * (a.r / 128);
+            const int col = tgr * 128 + t * 16 + li;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int slot = L.xslot[xi][4 * c + q];
+                dst[q] = slot >= 0 ? a.z1p + ((size_t)hh * a.R + slot) * a.r + col : a.scratch + lane;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *dst[q] = acc[q];
+    };
+    static_assert(WS_RING == 4 && NBH % WS_RING == 0, "a K half is a whole number of four-block turns");
+    if (nhalf > 0) {
+        // ring slot j holds the codes of block j (mod 4) of the wave's sequence
+        // of halves; the scale pairs of a turn of four blocks come in one load,
+        // one turn ahead
+        ws_u4 w0[WS_RING], w1[WS_RING];
+        UpwHalf cur, nxt;
+        half_of(0, cur);
+        half_of(1, nxt);
+        // the first turn's scales, then the codes in slot order, as the loop
+        // body issues them (the empty asm statements keep the compiler from
+        // reordering them): the waits at the loop head hold for the first
+        // iteration and every later one alike
+        ws_u4 scc = ws_scales4_t(cur.src, cur.kh * NBH);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < WS_RING; ++j) {
+            ws_fetch_tq(w0[j], w1[j], cur.src, cur.kh * NBH + j, 2 * NBH);
+            asm volatile("" ::: "memory");
+        }
+        floatx4 acc[1] = {zero4()};
+        floatx4 keep[UPW_MAXK];
+#pragma unroll
+        for (int i = 0; i < UPW_MAXK; ++i) keep[i] = zero4();
+        for (int hk = 0; hk < nhalf; ++hk) {
+#pragma unroll
+            for (int b0 = 0; b0 < NBH; b0 += WS_RING) {
+                // the next turn's scales: later in this half, or the next half's first
+                const ws_u4 scn = b0 + WS_RING < NBH ? ws_scales4_t(cur.src, cur.kh * NBH + b0 + WS_RING)
+                                                     : ws_scales4_t(nxt.src, nxt.kh * NBH);
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int j = 0; j < WS_RING; ++j) {
+                    const int b = b0 + j;
+                    const uint32_t spair = j == 0 ? scc.x : (j == 1 ? scc.y : (j == 2 ? scc.z : scc.w));
+                    ws_block_t<1>(acc, w0[j], w1[j], spair, ar, (cur.kh * NBH + b) * WS_KB);
+                    // the block four ahead: later in this half, or early in the next
+                    if (b + WS_RING < NBH)
+                        ws_fetch_tq(w0[j], w1[j], cur.src, cur.kh * NBH + b + WS_RING, 2 * NBH);
+                    else
+                        ws_fetch_tq(w0[j], w1[j], nxt.src, nxt.kh * NBH + b + WS_RING - NBH, 2 * NBH);
+                }
+                scc = scn;
+            }
+            if (cur.last) {
+#pragma unroll
+                for (int i = 0; i + 1 < UPW_MAXK; ++i) keep[i] = keep[i + 1];
+                keep[UPW_MAXK - 1] = acc[0];
+                acc[0] = zero4();
+            }
+            cur = nxt;
+            half_of(hk + 2, nxt);
+        }
+        // item k of the wave sits at keep[UPW_MAXK - nk + k]
+#pragma unroll
+        for (int i = 0; i < UPW_MAXK; ++i) {
+            const int k = i - (UPW_MAXK - nk);
+            if (k >= 0) store(gw + k * nw, keep[i]);
+        }
+    }
+    // U_up x for the last waves: item z = (group list index, eighth of K)
+    const int n_zl = L.ng * 8;
+    const int zi = nw - 1 - gw;
+    if (zi < n_zl) {
+        const int g = L.glist[zi >> 3], s8 = zi & 7;
+        const int kb = s8 * (a.d / 8);
+        for (int nt = 0; nt * 16 < a.rL; ++nt) {
+            const int n = nt * 16 + li;
+            const uint16_t* urow = a.lu_u + ((size_t)g * a.rL + min(n, a.rL - 1)) * a.d + kb + 8 * c;
+            floatx4 acc = zero4();
+            for (int st0 = 0; st0 < a.d / 8 / 32; st0 += 4) {
+                uint4 bv[4];
+#pragma unroll
+                for (int st = 0; st < 4; ++st) bv[st] = ld16(urow + (st0 + st) * 32);
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    // A fragment: x row li at K kb + (st0 + st) 32 + 8 c (swizzled segment)
+                    const int seg = ((kb + (st0 + st) * 32) >> 3) + c;
+                    const int sw = ((seg & 15) ^ ar.sw[0]) | (seg & ~15);
+                    const uint4 av = *reinterpret_cast<const uint4*>(ar.row[0] + 8 * sw);
+                    acc = mfma_bf16(av, bv[st], acc);
+                }
+            }
+            if (n < a.rL) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int tok = 4 * c + q;
+                    if (tok < a.T) a.zlp[(((size_t)s8 * a.T + tok) * a.G + g) * a.rLp + n] = acc[q];
+                }
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(UPW_THREADS)
+dec_up_ws(DecodeArgs a) {
+    __shared__ RouteView v;
+    __shared__ UpwLds L;
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < a.E; i += blockDim.x) a.cnt_e[i] = 0u;
+        for (int i = threadIdx.x; i < a.d / 64; i += blockDim.x) a.cnt_c[i] = 0u;
+    }
+    if (a.d == 4096) {
+        if (a.T <= 8) upw_run<8, 8>(a, v, L);
+        else upw_run<16, 8>(a, v, L);
+    } else {
+        if (a.T <= 8) upw_run<8, 4>(a, v, L);
+        else upw_run<16, 4>(a, v, L);
     }
 }
 
@@ -1387,7 +1677,7 @@ EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb
             // the workgroup's 128 columns are tile group nb of S_dn[g]
             const size_t tg = (size_t)g * (a.d / 128) + nb;
             WsSrcT src;
-            ws_src_t(src, a.s_dn_t + tg * 64 * a.h, a.s_dn_ts + tg * a.h, wv);
+            ws_src_t(src, a.s_dn_t + tg * 64 * a.h, a.s_dn_s + tg * a.h, a.h / KC, wv);
             ws_gemm_pieces<RP, DNW_THREADS, NS>(acc, src, a.h, q, L.xs, L.tile + wv * WS_TILE);
         } else {
             WsSrc src;
@@ -1491,15 +1781,51 @@ static bool down_ws_ok(const DecodeArgs& a, bool tiled) {
            a.d % DNW_COLS == 0 && a.P <= 64 && a.T <= 64 && a.G <= 64;
 }
 
+// Shapes the work-list shared up takes: at most 16 tokens, decode-tiled S_up
+// and A_up, quant groups of 128, d = 2048 or 4096 (every token's x row staged
+// whole; K halves a whole number of ring turns), r a multiple of 128, two K
+// slices of the R1 / R2 partial sums, and at most UPW_MAXK items per wave.
+static int device_cus();
+
+static bool up_ws_ok(const DecodeArgs& a) {
+    // at most UPW_MAXK items per wave whatever the routing
+    const long items = (long)a.G * (a.h / 16) + (long)a.nxmax * (a.r / 16) * 2;
+    if (items > (long)UPW_MAXK * device_cus() * UPW_WAVES) return false;
+    return a.s_up_t && a.a_up_t && a.T <= 16 && a.R <= UPW_XMAX && a.gq == KC && (a.d == 2048 || a.d == 4096) &&
+           a.r % 128 == 0 && a.h % 128 == 0 && a.S1 == 2 && a.rL <= 32 && a.G <= 64;
+}
+
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 template <int NS, bool LDSP>
 static hipError_t launch_ns(const DecodeArgs& a, hipStream_t s, int ns_down) {
     const int nbh = a.h / 64, nbr = (a.r + 63) / 64;
     const int g1 = a.G * (nbh / HS_RB) + a.nxmax * a.S1 * nbr + a.G * a.S1;
+    const bool upw = LDSP && NS == 1 && up_ws_ok(a);
     prof_begin(s);
-    dec_up<NS, LDSP><<<g1, 256, 0, s>>>(a);
-    prof_end(s, "dec_up");
+    if (upw) {
+        dec_up_ws<<<device_cus(), UPW_THREADS, 0, s>>>(a);
+        prof_end(s, "dec_up_ws");
+    } else {
+        dec_up<NS, LDSP><<<g1, 256, 0, s>>>(a);
+        prof_end(s, "dec_up");
+    }
     prof_begin(s);
-    if (LDSP) {
+    if (LDSP && upw) {
+        dec_act<NS><<<resident_grid(dec_act<NS>), 256, 0, s>>>(a);
+        prof_end(s, "dec_act");
+    } else if (LDSP) {
         dec_act<NS><<<resident_grid(dec_act<NS>), 256, 0, s>>>(a);
         prof_end(s, "dec_act");
     } else {

@@ -374,9 +374,9 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t str
     return hipGetLastError();
 }
 
-// Decode-tiled copy of G shared matrices of N x K (layout in the public
-// header): one thread per 16-byte unit of the destination, then one per fp16
-// scale pair.  Grid-stride, reads and writes in bounds by construction.
+// Decode-tiled copy of the codes of G matrices of N x K (layout in the public
+// header): one thread per 16-byte unit of the destination.  Grid-stride, reads
+// and writes in bounds by construction.
 __global__ void __launch_bounds__(256)
 tile_shared_q(uint4* __restrict__ dst, const uint8_t* __restrict__ src, int G, int N, int K) {
     const size_t units = (size_t)G * N * K / 32;          // 16-byte units
@@ -393,30 +393,11 @@ tile_shared_q(uint4* __restrict__ dst, const uint8_t* __restrict__ src, int G, i
     }
 }
 
-__global__ void __launch_bounds__(256)
-tile_shared_s(uint32_t* __restrict__ dst, const uint16_t* __restrict__ src, int G, int N, int K) {
-    const size_t pairs = (size_t)G * N * K / 256;
-    const size_t per_tg = (size_t)K / 2;                   // pairs per tile group
-    const size_t per_g = (size_t)N / 128 * per_tg;
-    for (size_t p = (size_t)blockIdx.x * 256 + threadIdx.x; p < pairs; p += (size_t)gridDim.x * 256) {
-        const size_t g = p / per_g, rg = p % per_g;
-        const size_t n = rg / per_tg, rt = rg % per_tg;
-        const size_t b = rt / 128, rb = rt % 128;          // 128 pairs per block
-        const size_t t = rb / 16, i = rb % 16;
-        const size_t row = 128 * n + 16 * t + i;
-        dst[p] = *reinterpret_cast<const uint32_t*>(src + (g * N + row) * (size_t)(K / 128) + 2 * b);
-    }
-}
-
-hipError_t launch_tile_shared(const uint8_t* src_q, const uint16_t* src_s, uint8_t* dst_q, uint16_t* dst_s,
-                              int G, int N, int K, hipStream_t stream) {
+hipError_t launch_tile_shared(const uint8_t* src_q, uint8_t* dst_q, int G, int N, int K, hipStream_t stream) {
     const size_t units = (size_t)G * N * K / 32;
     const size_t bq = (units + 255) / 256 < 8192 ? (units + 255) / 256 : 8192;
-    const size_t pairs = (size_t)G * N * K / 256;
-    const size_t bs = (pairs + 255) / 256 < 4096 ? (pairs + 255) / 256 : 4096;
     prof_begin(stream);
     tile_shared_q<<<(unsigned)bq, 256, 0, stream>>>(reinterpret_cast<uint4*>(dst_q), src_q, G, N, K);
-    tile_shared_s<<<(unsigned)bs, 256, 0, stream>>>(reinterpret_cast<uint32_t*>(dst_s), src_s, G, N, K);
     prof_end(stream, "tile_shared");
     return hipGetLastError();
 }

@@ -79,9 +79,10 @@ struct DecodeArgs {
     const uint8_t* b_dn; const uint16_t* b_dn_s;
     const uint16_t* lu_u; const uint16_t* lu_v;
     const uint16_t* ld_u; const uint16_t* ld_v;
-    const uint8_t* s_up_t; const uint16_t* s_up_ts;   // decode-tiled shared matrices (or null)
-    const uint8_t* s_dn_t; const uint16_t* s_dn_ts;
+    const uint8_t* s_up_t; const uint8_t* s_dn_t;     // decode-tiled codes of S_up, S_dn (or null)
+    const uint8_t* a_up_t;                             // and of A_up (or null)
     float* hs;          // [T][G][h]      shared up, per (token, group)
+    float* scratch;     // [64]           target of stores that have no output
     float* z1p;         // [S1][R][r]     partial sums of A_up x
     float* zlp;         // [4 S1][T][G][rLp] partial sums of U_up x
     uint16_t* act;      // [R][h]         bf16 activation per slot
@@ -119,8 +120,7 @@ hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, h
 hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);
 hipError_t launch_act(const LayerArgs& a, hipStream_t s);     // needs r == 128, h % 256 == 0
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
-hipError_t launch_tile_shared(const uint8_t* src_q, const uint16_t* src_s, uint8_t* dst_q, uint16_t* dst_s,
-                              int G, int N, int K, hipStream_t stream);
+hipError_t launch_tile_shared(const uint8_t* src_q, uint8_t* dst_q, int G, int N, int K, hipStream_t stream);
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
                            hipStream_t stream);
 

@@ -206,6 +206,20 @@ EM_DEV void mac_fast(floatx4 (&acc)[NS], const uint4 (&af)[NS][4], uint4 raw, ui
     }
 }
 
+// mac_fast with the chunk's scale already converted (16 s as a float).
+template <int NS>
+EM_DEV void mac_fast_f(floatx4 (&acc)[NS], const uint4 (&af)[NS][4], uint4 raw, float sc16) {
+    uint4 b[4];
+    dequant_b(raw, b);
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) {
+        floatx4 t = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) t = mfma_bf16(af[ms][s], b[s], t);
+        acc[ms] = fma4(sc16, t, acc[ms]);
+    }
+}
+
 template <int NS>
 EM_DEV void load_afrag_fast(uint4 (&af)[NS][4], const uint16_t* const (&arow)[NS], int kk, int c) {
 #pragma unroll

@@ -13,6 +13,8 @@
 // half-line MFMA-layout loads straight into registers.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_ops.h"
 
@@ -173,22 +175,35 @@ EM_DEV void ws_gemm(floatx4 (&acc)[NS], const WsSrc& p0, int kw, ws_u4* T, const
 // weight byte is read once per step.
 struct WsSrcT {
     const uint8_t* w;                   // this wave's tile at block 0, plus 16 lane
-    const uint16_t* s;                  // its scale pairs at block 0, plus 2 (lane % 16)
+    const uint16_t* s;                  // scales of row lane % 16 of the tile (row-major, K / 128 per row)
 };
 
-// tg_q / tg_s: the tile group's codes and scales; t: the tile (0..7).
-EM_DEV void ws_src_t(WsSrcT& p, const uint8_t* tg_q, const uint16_t* tg_s, int t) {
+// tg_q: the tile group's codes; tg_s: the scales of its row 0 (row-major, ks =
+// K / 128 per row); t: the tile (0..7).
+EM_DEV void ws_src_t(WsSrcT& p, const uint8_t* tg_q, const uint16_t* tg_s, int ks, int t) {
     const int l = lane_id();
     p.w = tg_q + (size_t)t * 2048 + 16 * l;
-    p.s = tg_s + t * 32 + 2 * (l & 15);
+    p.s = tg_s + (size_t)(16 * t + (l & 15)) * ks;
 }
 
-EM_DEV void ws_fetch_t(ws_u4& w0, ws_u4& w1, uint32_t& sp, const WsSrcT& p, int b, int nb) {
-    const int bb = min(b, nb - 1);                      // past the end: the last block again
-    const uint8_t* q = p.w + (size_t)bb * 16384;
+// The codes of block b (clamped to nb - 1).
+EM_DEV void ws_fetch_tq(ws_u4& w0, ws_u4& w1, const WsSrcT& p, int b, int nb) {
+    const uint8_t* q = p.w + (size_t)min(b, nb - 1) * 16384;
     w0 = __builtin_nontemporal_load(reinterpret_cast<const ws_u4*>(q));
     w1 = __builtin_nontemporal_load(reinterpret_cast<const ws_u4*>(q + 1024));
-    sp = *reinterpret_cast<const uint32_t*>(p.s + (size_t)bb * 256);
+}
+
+// The codes and the scale pair of block b (clamped to nb - 1).
+EM_DEV void ws_fetch_t(ws_u4& w0, ws_u4& w1, uint32_t& sp, const WsSrcT& p, int b, int nb) {
+    const int bb = min(b, nb - 1);
+    ws_fetch_tq(w0, w1, p, bb, nb);
+    sp = *reinterpret_cast<const uint32_t*>(p.s + 2 * bb);
+}
+
+// The scale pairs of blocks [b0, b0 + 4) in one 16-byte load (b0 a multiple
+// of 4; the row's scales 16-byte aligned).
+EM_DEV ws_u4 ws_scales4_t(const WsSrcT& p, int b0) {
+    return *reinterpret_cast<const ws_u4*>(p.s + 2 * b0);
 }
 
 // One block of a tiled tile: w0 / w1 are the MFMA operands of its two chunks.
@@ -196,6 +211,10 @@ template <int NS>
 EM_DEV void ws_block_t(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t spair, const WsAct& ar, int k0,
                        int boff = 0) {
     const int c = lane_id() >> 4;
+    // both chunks' scales first: the register that held them is then free for
+    // the load that refills this ring slot
+    const float sc[2] = {16.0f * fp16_bits_to_f32((uint16_t)(spair & 0xFFFFu)),
+                         16.0f * fp16_bits_to_f32((uint16_t)(spair >> 16))};
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const ws_u4 t = ch ? w1 : w0;
@@ -207,7 +226,7 @@ EM_DEV void ws_block_t(floatx4 (&acc)[NS], ws_u4 w0, ws_u4 w1, uint32_t spair, c
                 const int seg = (k0 >> 3) + (((16 * ch + 4 * c + s) ^ ar.sw[ms]) & 15) + ((16 * ch + 4 * c + s) & ~15);
                 af[ms][s] = *reinterpret_cast<const uint4*>(ar.row[ms] + boff + 8 * seg);
             }
-        mac_fast<NS>(acc, af, make_uint4(t.x, t.y, t.z, t.w), ch ? (spair >> 16) : (spair & 0xFFFFu));
+        mac_fast_f<NS>(acc, af, make_uint4(t.x, t.y, t.z, t.w), sc[ch]);
     }
 }
 
@@ -356,18 +375,46 @@ EM_DEV void ws_gemm_pieces(floatx4 (&acc)[NS], const Src& p, int K, const WsPiec
     piece_fetch(0);
     ws_u4 w0[WS_RING], w1[WS_RING];
     uint32_t sp[WS_RING];
+    // tiled codes: the scale pairs of a ring turn (four blocks) in one load, a
+    // turn ahead, issued before the turn's code refills (the same order in the
+    // prologue, so that the loop's waits hold from the first turn on)
+    constexpr bool TILED = std::is_same<Src, WsSrcT>::value;
+    ws_u4 scc = {0u, 0u, 0u, 0u};
+    if constexpr (TILED) {
+        static_assert(WS_RING == 4, "four-block turns");
+        scc = ws_scales4_t(p, 0);
+        asm volatile("" ::: "memory");
+    }
 #pragma unroll
-    for (int j = 0; j < WS_RING; ++j) ws_fetch_any(w0[j], w1[j], sp[j], p, j, nb);
+    for (int j = 0; j < WS_RING; ++j) {
+        if constexpr (TILED) {
+            ws_fetch_tq(w0[j], w1[j], p, j, nb);
+            asm volatile("" ::: "memory");
+        } else {
+            ws_fetch_any(w0[j], w1[j], sp[j], p, j, nb);
+        }
+    }
     piece_store(0);
     piece_fetch(1);
     ws_lds_barrier();
     for (int b = 0; b < nb; b += WS_RING) {
+        ws_u4 scn = scc;
+        if constexpr (TILED) {
+            scn = ws_scales4_t(p, min(b + WS_RING, nb - WS_RING));
+            asm volatile("" ::: "memory");
+        }
 #pragma unroll
         for (int j = 0; j < WS_RING; ++j) {
             const int blk = b + j;
             const int buf = (blk / P::BPS) & 1;
-            ws_block_any<NS>(acc, w0[j], w1[j], sp[j], T, ar, (j % P::BPS) * WS_KB, buf * WS_PIECE, p);
-            ws_fetch_any(w0[j], w1[j], sp[j], p, blk + WS_RING, nb);
+            if constexpr (TILED) {
+                const uint32_t spair = j == 0 ? scc.x : (j == 1 ? scc.y : (j == 2 ? scc.z : scc.w));
+                ws_block_t<NS>(acc, w0[j], w1[j], spair, ar, (j % P::BPS) * WS_KB, buf * WS_PIECE);
+                ws_fetch_tq(w0[j], w1[j], p, blk + WS_RING, nb);
+            } else {
+                ws_block_any<NS>(acc, w0[j], w1[j], sp[j], T, ar, (j % P::BPS) * WS_KB, buf * WS_PIECE, p);
+                ws_fetch_any(w0[j], w1[j], sp[j], p, blk + WS_RING, nb);
+            }
             if ((j + 1) % P::BPS == 0) {
                 // piece boundary: the next piece goes into the other buffer
                 // (read last in the piece before this one, which every wave has
@@ -377,6 +424,7 @@ EM_DEV void ws_gemm_pieces(floatx4 (&acc)[NS], const Src& p, int K, const WsPiec
                 piece_fetch(blk / P::BPS + 2);
             }
         }
+        scc = scn;
     }
 }
 

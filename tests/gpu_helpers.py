@@ -23,9 +23,9 @@ def f32_to_dev(a) -> torch.Tensor:
 
 
 def tile_ok(D) -> bool:
-    """Shapes the decode-tiled shared matrices take (quant groups of 128, d and h
-    multiples of 256)."""
-    return D.quant_group == 128 and D.d % 256 == 0 and D.h % 256 == 0
+    """Shapes the decode-tiled codes take (quant groups of 128, d and h multiples
+    of 1024)."""
+    return D.quant_group == 128 and D.d % 1024 == 0 and D.h % 1024 == 0
 
 
 class Layer:

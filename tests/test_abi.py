@@ -134,25 +134,20 @@ def test_copy_validation_before_any_device_call():
 
 
 def test_tiled_weights_all_or_none():
-    """The decode-tiled shared matrices are optional, but all four or none."""
+    """The decode-tiled codes are optional: s_up's and s_dn's both or neither,
+    a_up's on its own; aligned; only for shapes the layout takes."""
     lib = em.load()
     D = synth.config(2).dims
-    ptrs = [0x50000] * 16 + [0x60000, None, 0x70000, 0x80000]
-    cw = em.CWeights(*ptrs)
-    st = lib.edge_moe_forward(ctypes.byref(em.cdims(D)), 0x10000, 0x20000, 0x30000, ctypes.byref(cw),
-                              0x40000, 0x100000, em.edge_moe_workspace_bytes(D), None)
-    assert st == em.EDGE_MOE_EINVAL
-    ptrs = [0x50000] * 16 + [0x60008, 0x60000, 0x70000, 0x80000]      # codes not 16-byte aligned
-    cw = em.CWeights(*ptrs)
-    st = lib.edge_moe_forward(ctypes.byref(em.cdims(D)), 0x10000, 0x20000, 0x30000, ctypes.byref(cw),
-                              0x40000, 0x100000, em.edge_moe_workspace_bytes(D), None)
-    assert st == em.EDGE_MOE_EINVAL
-    # tiled copies for a shape the layout does not take (quant groups of 32)
-    T0 = synth.config(0).dims
-    cw = em.CWeights(*([0x50000] * 20))
-    st = lib.edge_moe_forward(ctypes.byref(em.cdims(T0)), 0x10000, 0x20000, 0x30000, ctypes.byref(cw),
-                              0x40000, 0x100000, em.edge_moe_workspace_bytes(T0), None)
-    assert st == em.EDGE_MOE_EUNSUPPORTED
+
+    def fwd(dims, ptrs):
+        cw = em.CWeights(*ptrs)
+        return lib.edge_moe_forward(ctypes.byref(em.cdims(dims)), 0x10000, 0x20000, 0x30000, ctypes.byref(cw),
+                                    0x40000, 0x100000, em.edge_moe_workspace_bytes(dims), None)
+    assert fwd(D, [0x50000] * 16 + [0x60000, None, None]) == em.EDGE_MOE_EINVAL      # s_up without s_dn
+    assert fwd(D, [0x50000] * 16 + [0x60008, 0x70000, None]) == em.EDGE_MOE_EINVAL   # not 16-byte aligned
+    assert fwd(D, [0x50000] * 16 + [None, None, 0x80008]) == em.EDGE_MOE_EINVAL      # a_up not aligned
+    T0 = synth.config(0).dims                                                        # quant groups of 32
+    assert fwd(T0, [0x50000] * 19) == em.EDGE_MOE_EUNSUPPORTED
 
 
 def test_tile_shared_validation_before_device():
@@ -161,18 +156,19 @@ def test_tile_shared_validation_before_device():
     cd = ctypes.byref(em.cdims(D))
     base = 1 << 40
     big = 1 << 34                                       # beyond any matrix of these dims
-    ok = dict(which=0, sq=base, ss=base + big, dq=base + 2 * big, ds=base + 3 * big)
+    ok = dict(which=0, sq=base, dq=base + big)
 
     def call(**kw):
         a = {**ok, **kw}
-        return lib.edge_moe_tile_shared(cd, a["which"], ctypes.c_void_p(a["sq"]), ctypes.c_void_p(a["ss"]),
-                                        ctypes.c_void_p(a["dq"]), ctypes.c_void_p(a["ds"]), None)
-    assert call(which=2) == em.EDGE_MOE_EINVAL
-    assert call(sq=base + 8) == em.EDGE_MOE_EINVAL                 # codes not 16-byte aligned
-    assert call(ds=base + 3 * big + 2) == em.EDGE_MOE_EINVAL       # scales not 4-byte aligned
+        return lib.edge_moe_tile_shared(cd, a["which"], ctypes.c_void_p(a["sq"]), ctypes.c_void_p(a["dq"]), None)
+    assert call(which=3) == em.EDGE_MOE_EINVAL
+    assert call(which=-1) == em.EDGE_MOE_EINVAL
+    assert call(sq=base + 8) == em.EDGE_MOE_EINVAL                 # not 16-byte aligned
     assert call(dq=base + 64) == em.EDGE_MOE_EINVAL                # overlaps the source
     assert call(sq=0) == em.EDGE_MOE_EINVAL
     T0 = synth.config(0).dims                                      # quant groups of 32
     assert lib.edge_moe_tile_shared(ctypes.byref(em.cdims(T0)), 0, ctypes.c_void_p(base),
-                                    ctypes.c_void_p(base + big), ctypes.c_void_p(base + 2 * big),
-                                    ctypes.c_void_p(base + 3 * big), None) == em.EDGE_MOE_EUNSUPPORTED
+                                    ctypes.c_void_p(base + big), None) == em.EDGE_MOE_EUNSUPPORTED
+    D8 = synth.Dims(**{**D.__dict__, "delta_rank": 64})            # a_up rank not a multiple of 128
+    assert lib.edge_moe_tile_shared(ctypes.byref(em.cdims(D8)), 2, ctypes.c_void_p(base),
+                                    ctypes.c_void_p(base + big), None) == em.EDGE_MOE_EUNSUPPORTED
