@@ -76,6 +76,9 @@ def kernel_bytes(D, idx: np.ndarray):
         # the kernel's inputs read once and its outputs written once
         "dec_up": G * (per["s_up"] + per["lu_u"]) + X * per["a_up"] + x_b
                   + U * h * 4 + R * r * 4 + U * rL * 4,
+        # the work-list shared up (decode-tiled codes) moves the same bytes
+        "dec_up_ws": G * (per["s_up"] + per["lu_u"]) + X * per["a_up"] + x_b
+                     + U * h * 4 + R * r * 4 + U * rL * 4,
         "dec_act": X * (per["b_up"] + per["a_dn"]) + G * (per["lu_v"] + per["ld_u"])
                    + U * h * 4 + R * r * 4 + U * rL * 4 + R * h * 2 + R * (r + rL) * 2,
         "dec_down": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2
