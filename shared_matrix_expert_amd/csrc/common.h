@@ -100,4 +100,14 @@ EM_DEV float silu(float v) {
     return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// An 8-byte global store that the compiler's wait insertion does not see.
+// Loads and stores share one counter on this target, and a counted store in
+// flight makes the compiler wait for zero before the next use of any load.
+// Loads complete in order among themselves, so a store it does not count can
+// only lengthen a vmcnt(N) wait, never end it early.  For results that
+// nothing in the same launch reads back; the launch's end makes them visible.
+EM_DEV void st8_uncounted(void* p, uint64_t v) {
+    asm volatile("global_store_dwordx2 %0, %1, off" : : "v"(p), "v"(v) : "memory");
+}
+
 }  // namespace em

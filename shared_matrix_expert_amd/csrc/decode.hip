@@ -1102,17 +1102,15 @@ dec_act(DecodeArgs a) {
         // per-block shared-up values and V_up rows, loaded one block ahead
         uint4 vb[4];
         float hv[4][NS][4];
-        auto fetch_hv = [&](int cb) {
+        auto fetch_hv = [&](int cb, int nt) {
+            const int ncol = cb * CB_L + wv * 64 + nt * 16 + li;
+            // lanes past the rank re-read the last 8 (finite weights that meet
+            // zeros: zl columns past the rank are zero in LDS)
+            vb[nt] = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int ncol = cb * CB_L + wv * 64 + nt * 16 + li;
-                const uint4 t = ld16(a.lu_v + ((size_t)g * a.h + ncol) * a.rL + min(8 * c, a.rL - 8));
-                vb[nt] = 8 * c < a.rL ? t : zero_u4();
+            for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
-                for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
-            }
+                for (int q = 0; q < 4; ++q) hv[nt][ms][q] = a.hs[((size_t)tq[ms][q] * a.G + g) * a.h + ncol];
         };
 
         // ---- R1, R2: finish the split-K sums in slice order and round to bf16.
@@ -1136,11 +1134,16 @@ dec_act(DecodeArgs a) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) lp[u][s] = p[(size_t)min(s, nl - 1) * a.T * a.G * a.rLp];
         }
-        // then the first block's operands, so that the sums above wait for no weight
-        fetch_hv(j0);
+        // then the first block's operands, so that the sums above wait for no
+        // weight, in the order the loop issues them (its waits hold for the
+        // first pass too only then)
         ActUp ru_;
         ActDn rd_;
         act_fetch_up(ru_, a, e, j0);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) fetch_hv(j0, nt);
+        asm volatile("" ::: "memory");
         act_fetch_dn(rd_, a, e, g, j0);
 #pragma unroll
         for (int u = 0; u < ZI; ++u) {
@@ -1202,15 +1205,22 @@ dec_act(DecodeArgs a) {
                     for (int q = 0; q < 4; ++q) {
                         const int i = ms * 16 + 4 * c + q;
                         uint16_t ab = 0;
-                        if (i < nrows) {
-                            ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
-                            a.act[(size_t)v.rows[i] * a.h + ncol] = ab;
-                        }
+                        if (i < nrows) ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
                         as_[i][lrow] = ab;
                     }
             }
-            fetch_hv(min(cb + 1, j1 - 1));
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) fetch_hv(min(cb + 1, j1 - 1), nt);
             __syncthreads();
+            // the block's activation rows, 8 bytes per lane, by stores the
+            // waits for the operand loads in flight do not count
+#pragma unroll
+            for (int u = 0; u < 4 * NS; ++u) {
+                const int q = tid + 256 * u, row = q >> 6, seg = q & 63;
+                if (row < nrows)
+                    st8_uncounted(a.act + (size_t)v.rows[row] * a.h + cb * CB_L + 4 * seg,
+                                  *reinterpret_cast<const uint64_t*>(&as_[row][4 * seg]));
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int q = tid + 256 * i;
