@@ -114,7 +114,7 @@ bool force_old_gemm() {
 }
 
 struct DecLayout {
-    size_t hs, z1p, zlp, act, z2p, z2, zl2, o, cnt_e, cnt_c, scratch, bytes;
+    size_t hs, z1p, zlp, act, z2p, z2, zl2, o, od, cnt_e, cnt_c, scratch, bytes;
     int S1, cb2, ncb2, N2;
     bool lds;
 };
@@ -138,6 +138,7 @@ DecLayout make_dec_layout(const edge_moe_dims& d) {
     L.z2 = take((size_t)R * d.delta_rank * 2);
     L.zl2 = take((size_t)R * rLp * 2);
     L.o = take((size_t)R * d.d * 4);
+    L.od = take((size_t)R * d.d * 4);
     L.cnt_e = take((size_t)d.n_experts * 4);
     L.cnt_c = take((size_t)(d.d / 64) * 4);
     L.scratch = take(64 * 4);
@@ -326,6 +327,7 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.cnt_e = reinterpret_cast<uint32_t*>(base + L.cnt_e);
     a.cnt_c = reinterpret_cast<uint32_t*>(base + L.cnt_c);
     a.scratch = reinterpret_cast<float*>(base + L.scratch);
+    a.od = reinterpret_cast<float*>(base + L.od);
     hipStream_t s = (hipStream_t)stream;
     hipError_t err = em::launch_decode(a, s);
     if (err != hipSuccess) return EDGE_MOE_EHIP;

@@ -1336,8 +1336,11 @@ EM_DEV uint4 dq_offset(uint32_t w) {
 // order of dq_offset.  The B_dn rows of four experts are in flight while four are used.
 template <int NS>
 EM_DEV void delta_down_pass(floatx4 (&acc)[NS], const DecodeArgs& a, const int* dexp, const int* dstart,
-                            uint64_t starts, int prow, const int (&slot_i)[NS], int ncol) {
+                            uint64_t starts, int prow, const int (&slot_i)[NS], int ncol, int ub = 0,
+                            int ue = DEC_RMAX) {
     const int nexp = __popcll(starts);
+    ue = min(ue, nexp);
+    if (ub >= ue) return;
     const int lane = lane_id(), c = lane >> 4;
     uint4 af[NS][4];
 #pragma unroll
@@ -1368,7 +1371,7 @@ EM_DEV void delta_down_pass(floatx4 (&acc)[NS], const DecodeArgs& a, const int* 
     auto fetch = [&](DnRing& r, int u0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int e = dexp[min(u0 + q, nexp - 1)];
+            const int e = dexp[min(u0 + q, ue - 1)];
             r.w[q] = ld16(a.b_dn + ((size_t)e * a.d + ncol) * (KC / 2) + 16 * c);
             r.s[q] = a.b_dn_s[(size_t)e * a.d + ncol];
         }
@@ -1377,7 +1380,7 @@ EM_DEV void delta_down_pass(floatx4 (&acc)[NS], const DecodeArgs& a, const int* 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int u = u0 + q;
-            if (u >= nexp) break;
+            if (u >= ue) break;
             const int r0 = dstart[u], r1 = u + 1 < nexp ? dstart[u + 1] : prow;
             uint4 b[4];
             b[0] = dq_offset(r.w[q].x);
@@ -1398,15 +1401,15 @@ EM_DEV void delta_down_pass(floatx4 (&acc)[NS], const DecodeArgs& a, const int* 
         }
     };
     DnRing d0, d1;
-    fetch(d0, 0);
-    int u0 = 0;
-    for (; u0 + 8 <= nexp; u0 += 8) {
+    fetch(d0, ub);
+    int u0 = ub;
+    for (; u0 + 8 <= ue; u0 += 8) {
         fetch(d1, u0 + 4);
         consume(d0, u0);
         fetch(d0, u0 + 8);
         consume(d1, u0 + 4);
     }
-    if (u0 < nexp) {
+    if (u0 < ue) {
         fetch(d1, u0 + 4);
         consume(d0, u0);
         consume(d1, u0 + 4);
@@ -1647,15 +1650,14 @@ struct DnwLds {
     int dstart[32];                                            // first row of each
 };
 
-template <int RP, bool TILED>
-EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb, int m0, int prow) {
-    constexpr int NS = WsPiece<RP, DNW_THREADS>::NS;
-    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
-    const int ncol = nb * DNW_COLS + wv * 16 + li;
+// The pass's staged rows (row -> slot) and its distinct experts with their
+// first rows: rows are sorted by expert, so an expert starts where the row's
+// expert differs from the previous row's.  Returns the bit mask of expert
+// starts.
+template <int RP>
+EM_DEV uint64_t dnw_experts(const RouteView& v, DnwLds& L, int m0, int prow) {
+    const int lane = lane_id(), wv = wave_id();
     if ((int)threadIdx.x < RP) L.arow[threadIdx.x] = v.rows[m0 + min((int)threadIdx.x, prow - 1)];
-    // distinct experts of the pass and their first rows: rows are sorted by
-    // expert, so an expert starts where the row's expert differs from the
-    // previous row's
     int my_e = -1, prev_e = -1;
     if (lane < prow) my_e = v.idx[v.rows[m0 + lane]];
     if (lane >= 1 && lane - 1 < prow) prev_e = v.idx[v.rows[m0 + lane - 1]];
@@ -1666,6 +1668,16 @@ EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb
         L.dstart[u] = lane;
     }
     __syncthreads();
+    return starts;
+}
+
+template <int RP, bool TILED>
+EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb, int m0, int prow,
+                     bool with_delta) {
+    constexpr int NS = WsPiece<RP, DNW_THREADS>::NS;
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    const int ncol = nb * DNW_COLS + wv * 16 + li;
+    const uint64_t starts = dnw_experts<RP>(v, L, m0, prow);
     int slot_i[NS];
 #pragma unroll
     for (int ms = 0; ms < NS; ++ms) slot_i[ms] = L.arow[min(ms * 16 + li, RP - 1)];
@@ -1703,7 +1715,7 @@ EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms) acc[ms] = mfma_bf16(8 * c < a.rL ? lzt[ms] : zero_u4(), lv, acc[ms]);
     }
-    delta_down_pass<NS>(acc, a, L.dexp, L.dstart, starts, prow, slot_i, ncol);
+    if (with_delta) delta_down_pass<NS>(acc, a, L.dexp, L.dstart, starts, prow, slot_i, ncol);
 #pragma unroll
     for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
@@ -1713,20 +1725,93 @@ EM_DEV void dnw_pass(const DecodeArgs& a, RouteView& v, DnwLds& L, int g, int nb
         }
 }
 
+// Share `part` of `nparts` of another group's delta down (the group's rows in
+// v, one pass of prow rows): the distinct experts [part E / nparts,
+// (part + 1) E / nparts) and their rows, into od.
+template <int RP>
+EM_DEV void dnw_delta_share(const DecodeArgs& a, RouteView& v, DnwLds& L, int nb, int prow, int part, int nparts) {
+    constexpr int NS = WsPiece<RP, DNW_THREADS>::NS;
+    const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
+    const int ncol = nb * DNW_COLS + wv * 16 + li;
+    const uint64_t starts = dnw_experts<RP>(v, L, 0, prow);
+    const int nexp = __popcll(starts);
+    const int ub = part * nexp / nparts, ue = (part + 1) * nexp / nparts;
+    if (ub >= ue) return;
+    const int r0 = L.dstart[ub], r1 = ue < nexp ? L.dstart[ue] : prow;
+    int slot_i[NS];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) slot_i[ms] = L.arow[min(ms * 16 + li, RP - 1)];
+    floatx4 acc[NS];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+    delta_down_pass<NS>(acc, a, L.dexp, L.dstart, starts, prow, slot_i, ncol, ub, ue);
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int i = ms * 16 + 4 * c + qq;
+            if (i >= r0 && i < r1) st_agent(&a.od[(size_t)v.rows[i] * a.d + ncol], acc[ms][qq]);
+        }
+}
+
+// y = sum_j w_j o_j in slot order over one column block; with HANDED, the
+// slots set in hot_slots (one bit per slot) add their handed-off delta first
+// and store the sum back as the slot's output.
+template <bool HANDED>
+EM_DEV void dnw_combine(const DecodeArgs& a, int nb, const uint32_t* hot_slots) {
+    // two outputs per thread and up to 16 slots each with every load in flight
+    // at once (unconditional loads: the compiler's waits stay counted), so the
+    // combine is one memory round trip per 1024 outputs
+    constexpr int KJ = 16;
+    const int n = a.T * DNW_COLS, nt = (int)blockDim.x;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 2 * nt) {
+        int t[2], col[2];
+        float acc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int i = min(i0 + it * nt, n - 1);
+            t[it] = i / DNW_COLS;
+            col[it] = nb * DNW_COLS + (i % DNW_COLS);
+        }
+        for (int j0 = 0; j0 < a.k; j0 += KJ) {
+            float wv[2][KJ], ov[2][KJ], dv[2][KJ];
+#pragma unroll
+            for (int it = 0; it < 2; ++it)
+#pragma unroll
+                for (int u = 0; u < KJ; ++u) {
+                    const size_t slot = (size_t)t[it] * a.k + min(j0 + u, a.k - 1);
+                    wv[it][u] = a.topk_w[slot];
+                    ov[it][u] = ld_agent(&a.o[slot * a.d + col[it]]);
+                    if constexpr (HANDED) dv[it][u] = ld_agent(&a.od[slot * a.d + col[it]]);
+                }
+#pragma unroll
+            for (int it = 0; it < 2; ++it)
+#pragma unroll
+                for (int u = 0; u < KJ; ++u) {
+                    if (j0 + u >= a.k) break;
+                    float o = ov[it][u];
+                    if constexpr (HANDED) {
+                        const int slot = t[it] * a.k + j0 + u;
+                        if ((hot_slots[slot >> 5] >> (slot & 31)) & 1u) {
+                            o += dv[it][u];
+                            if (i0 + it * nt < n) st_agent(&a.o[(size_t)slot * a.d + col[it]], o);
+                        }
+                    }
+                    acc[it] = fmaf(wv[it][u], o, acc[it]);
+                }
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+            if (i0 + it * nt < n) a.y[(size_t)t[it] * a.d + col[it]] = acc[it];
+    }
+}
+
 template <bool TILED>
 __global__ void __launch_bounds__(DNW_THREADS)
 dec_down_ws(DecodeArgs a) {
     __shared__ RouteView v;
     __shared__ DnwLds L;
     __shared__ int gcnt[64];
-    rv_load(v, a.idx, a.R);
-    if ((int)threadIdx.x < 64) gcnt[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < a.R; i += blockDim.x) atomicAdd(&gcnt[v.idx[i] / a.P], 1);
-    __syncthreads();
-    // passes that carry rows: only they arrive at the column block's counter
-    int live_passes = 0;
-    for (int gg = 0; gg < a.G; ++gg) live_passes += (gcnt[gg] + 31) / 32;
     const int nbd = a.d / DNW_COLS;
     const int per_pass = a.G * nbd;
     const int pass = blockIdx.x / per_pass;
@@ -1735,32 +1820,64 @@ dec_down_ws(DecodeArgs a) {
     // so that its activation rows are read into one L2
     const int bx = per_pass % 8 == 0 ? (loc & 7) * (per_pass / 8) + (loc >> 3) : loc;
     const int g = bx / nbd, nb = bx % nbd;
+    rv_load(v, a.idx, a.R);
+    if ((int)threadIdx.x < 64) gcnt[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.R; i += blockDim.x) atomicAdd(&gcnt[v.idx[i] / a.P], 1);
+    __syncthreads();
+    // passes that carry rows: only they arrive at the column block's counter
+    // group counts one per lane (G <= 64): the plan below is wave-wide
+    // arithmetic instead of a loop of LDS reads
+    const int lane = lane_id();
+    const int gc = lane < a.G ? gcnt[lane] : 0;
+    int live_passes = (gc + 31) / 32;                  // passes that carry rows: only they arrive
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) live_passes += __shfl_xor(live_passes, off, kWave);
     const int m0 = pass * 32;
     const int prow = min(gcnt[g] - m0, 32);
     if (prow <= 0) return;
+    // Hand-off of the delta down: when every group fits one pass, the groups
+    // of more than 16 rows (two subtiles, four times the staged activation of
+    // an 8-row group) give their column block's delta to the workgroups of
+    // the groups of at most 8 rows, split by distinct experts into equal
+    // shares, so that the hot groups' workgroups stop being the critical path.
+    // Every workgroup derives the same plan from the group counts.
+    const uint64_t hot = __ballot(gc > 16), light = __ballot(gc >= 1 && gc <= 8);
+    const bool one_pass = __ballot(gc > 32) == 0ull;
+    const int nhot = __popcll(hot), nlight = __popcll(light);
+    const int share = (one_pass && nhot > 0) ? nlight / nhot : 0;          // helpers per hot group
+    const bool handed = share > 0 && ((hot >> g) & 1ull);
+    const int my_light = ((light >> g) & 1ull) ? __popcll(light & ((1ull << g) - 1ull)) : -1;
+    int help_g = -1;
+    if (share > 0 && my_light >= 0 && my_light < share * nhot) {
+        uint64_t hm = hot;
+        for (int h = my_light / share; h > 0; --h) hm &= hm - 1ull;         // the (my_light / share)-th hot group
+        help_g = __ffsll((long long)hm) - 1;
+    }
     rv_group_rows(v, g, a.T, a.k, a.P, a.R);
-    if (prow > 16) dnw_pass<32, TILED>(a, v, L, g, nb, m0, prow);
-    else if (prow > 8) dnw_pass<16, TILED>(a, v, L, g, nb, m0, prow);
-    else dnw_pass<8, TILED>(a, v, L, g, nb, m0, prow);
+    if (prow > 24) dnw_pass<32, TILED>(a, v, L, g, nb, m0, prow, !handed);
+    else if (prow > 16) dnw_pass<24, TILED>(a, v, L, g, nb, m0, prow, !handed);
+    else if (prow > 8) dnw_pass<16, TILED>(a, v, L, g, nb, m0, prow, true);
+    else dnw_pass<8, TILED>(a, v, L, g, nb, m0, prow, true);
+    if (help_g >= 0) {
+        rv_group_rows(v, help_g, a.T, a.k, a.P, a.R);
+        dnw_delta_share<32>(a, v, L, nb, gcnt[help_g], my_light % share, share);
+    }
 
-    // ---- the last workgroup of this column block forms y = sum_j w_j o_j in slot order
+    // ---- the last workgroup of this column block forms y = sum_j w_j o_j in
+    // slot order (o_j = its stream part + its handed-off delta, stored back)
     if (!arrive_last(v, &a.cnt_c[nb], (uint32_t)live_passes)) return;
-    for (int i = threadIdx.x; i < a.T * DNW_COLS; i += blockDim.x) {
-        const int t = i / DNW_COLS, col = nb * DNW_COLS + (i % DNW_COLS);
-        float acc = 0.f;
-        for (int j0 = 0; j0 < a.k; j0 += 8) {
-            float wv8[8], ov8[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = min(j0 + u, a.k - 1);
-                wv8[u] = a.topk_w[t * a.k + j];
-                ov8[u] = ld_agent(&a.o[(size_t)(t * a.k + j) * a.d + col]);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (j0 + u < a.k) acc = fmaf(wv8[u], ov8[u], acc);
-        }
-        a.y[(size_t)t * a.d + col] = acc;
+    if (share > 0) {
+        // the slots of the groups that handed off their delta, one bit each
+        __shared__ uint32_t hot_slots[DEC_RMAX / 32];
+        for (int i = threadIdx.x; i < (a.R + 31) / 32; i += blockDim.x) hot_slots[i] = 0u;
+        __syncthreads();
+        for (int i = threadIdx.x; i < a.R; i += blockDim.x)
+            if (gcnt[v.idx[i] / a.P] > 16) atomicOr(&hot_slots[i >> 5], 1u << (i & 31));
+        __syncthreads();
+        dnw_combine<true>(a, nb, hot_slots);
+    } else {
+        dnw_combine<false>(a, nb, nullptr);
     }
 }
 

@@ -90,6 +90,7 @@ struct DecodeArgs {
     uint16_t* z2;       // [R][r]
     uint16_t* zl2;      // [R][rLp]
     float* o;           // [R][d]         expert output per slot
+    float* od;          // [R][d]         delta down of rows whose group hands it to another workgroup
     float* y;           // [T][d]
     uint32_t* cnt_e;    // [E]     arrivals per expert (activation kernel)
     uint32_t* cnt_c;    // [d/64]  arrivals per output column block (down kernel)

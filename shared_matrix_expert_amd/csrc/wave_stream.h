@@ -286,7 +286,8 @@ constexpr int WS_PIECE = 16384;          // elements per piece buffer (32 KB)
 
 template <int RP, int NT>
 struct WsPiece {
-    static constexpr int SK = WS_PIECE / RP < 1024 ? WS_PIECE / RP : 1024;   // elements per row and piece
+    // elements per row and piece: the largest power of two that fits, at most 1024
+    static constexpr int SK = WS_PIECE / RP >= 1024 ? 1024 : (WS_PIECE / RP >= 512 ? 512 : 256);
     static constexpr int BPS = SK / WS_KB;              // weight blocks per piece
     static constexpr int NS = RP > 16 ? 2 : 1;          // 16-row MFMA subtiles
     static constexpr int U = RP * SK / 8 / NT;          // 16-byte loads per thread and piece
