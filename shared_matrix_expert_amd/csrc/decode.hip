@@ -1284,17 +1284,43 @@ dec_act(DecodeArgs a) {
                 }
         }
         if (arrive_last(v, &a.cnt_e[e], (uint32_t)rpe)) {
-            for (int i = tid; i < nrows * N2; i += 256) {
-                const int row = i / N2, n2 = i % N2;
-                const int slot = v.rows[row];
-                float sum = 0.f;
-                for (int rr = 0; rr < rpe; ++rr) {
-                    const int j = (rr * NB) / rpe;
-                    sum += ld_agent(a.z2p + ((size_t)j * a.R + slot) * N2 + n2);
+            // two outputs per thread, eight ranges' partials of each in flight
+            // at once (unconditional loads), added in range order
+            constexpr int RU = 8;
+            const int n = nrows * N2;
+            for (int i0 = tid; i0 < n; i0 += 512) {
+                int slot[2], n2v[2];
+                float sum[2] = {0.f, 0.f};
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+                    const int i = min(i0 + 256 * it, n - 1), row = i / N2;
+                    n2v[it] = i - row * N2;
+                    slot[it] = v.rows[row];
                 }
-                const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum);
-                if (n2 < KC) a.z2[(size_t)slot * KC + n2] = bits;
-                else if (n2 - KC < a.rL) a.zl2[(size_t)slot * a.rLp + (n2 - KC)] = bits;
+                for (int r0 = 0; r0 < rpe; r0 += RU) {
+                    int jr[RU];
+#pragma unroll
+                    for (int u = 0; u < RU; ++u) jr[u] = (min(r0 + u, rpe - 1) * NB) / rpe;
+                    float p[2][RU];
+#pragma unroll
+                    for (int it = 0; it < 2; ++it)
+#pragma unroll
+                        for (int u = 0; u < RU; ++u)
+                            p[it][u] = ld_agent(a.z2p + ((size_t)jr[u] * a.R + slot[it]) * N2 + n2v[it]);
+#pragma unroll
+                    for (int it = 0; it < 2; ++it)
+#pragma unroll
+                        for (int u = 0; u < RU; ++u)
+                            if (r0 + u < rpe) sum[it] += p[it][u];
+                }
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+                    if (i0 + 256 * it >= n) continue;
+                    const uint16_t bits = (uint16_t)f32_to_bf16_rne(sum[it]);
+                    const int n2 = n2v[it];
+                    if (n2 < KC) a.z2[(size_t)slot[it] * KC + n2] = bits;
+                    else if (n2 - KC < a.rL) a.zl2[(size_t)slot[it] * a.rLp + (n2 - KC)] = bits;
+                }
             }
         }
         __syncthreads();
