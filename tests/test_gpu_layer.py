@@ -183,6 +183,43 @@ def test_prefill_layer_sampled():
     assert torch.equal(y, y2)
 
 
+def test_verify_delta_handoff():
+    """A verify batch routed by hand so that two groups carry 32 and 24 rows
+    (the 32- and 24-row staged passes) and the six others 1-8 rows each: the
+    hot groups hand their delta down to three light groups' workgroups each,
+    and the combine adds it back (the trace's expert outputs include it)."""
+    say("case: verify T=8, hand-built routing with 32- and 24-row groups")
+    D = synth.config(2).dims
+    T, k, P = D.T, D.top_k, D.experts_per_group
+    idx = np.zeros((T, k), dtype=np.int32)
+    for t in range(T):
+        if t < 4:
+            hot = [(3 * t + j) % 20 for j in range(8)]                 # group 0: 32 rows
+        else:
+            hot = [P + (2 * t + j) % 15 for j in range(6)]             # group 1: 24 rows
+        light = [(2 + (t + m) % 6) * P + (5 * t + m) % P for m in range(k - len(hot))]
+        idx[t] = hot + light
+    counts = np.bincount(idx.ravel() // P, minlength=D.n_experts // P)
+    assert counts[0] == 32 and counts[1] == 24 and all(1 <= c <= 8 for c in counts[2:]), counts
+    rng = np.random.default_rng(7)
+    w = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    x = synth.make_activations(2, 3)
+    Wdev = synth.make_weights(2, 3, device="cuda")
+    lay = Layer(D, Wdev)
+    idx_d = torch.from_numpy(idx).to("cuda")
+    w_d = torch.from_numpy(w).to("cuda")
+    y, tr = lay.forward(bits_to_dev(x), idx_d, w_d, trace=True)
+    torch.cuda.synchronize()
+    fw = moe_forward(x, idx, w.astype(np.float64), synth.weights_to_numpy(Wdev), P, keep=True)
+    ok, ratio = y_within_tolerance(y.cpu().numpy(), fw["y"])
+    say(f"  worst |dy| / bound = {ratio:.3g}")
+    assert ok, f"y outside tolerance (worst ratio {ratio:.3g})"
+    _check_trace(D, idx_d, tr, fw)
+    y2, _ = lay.forward(bits_to_dev(x), idx_d, w_d)
+    assert torch.equal(y, y2)
+
+
 @pytest.mark.parametrize("T", [2, 13, 16, 37, 200])
 def test_ragged_batches(T):
     """Token counts that leave partial tiles and cross the router's small/large
