@@ -329,6 +329,37 @@ class Stack:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
+    def time_graph(self, steps):
+        """The same pass captured once as a HIP graph (48 x (route, layer,
+        residual) launches) and replayed; returns (seconds per replay, whether
+        the first replay's output equals the eager pass bitwise)."""
+        torch = self.torch
+        self.step()
+        torch.cuda.synchronize()
+        ref = (self.xa if (self.n_layers - 1) % 2 == 0 else self.xb).clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        eager_stream = self.stream
+        with torch.cuda.stream(side):
+            self.stream = side
+            with torch.cuda.graph(g, stream=side):
+                self.step()
+        self.stream = eager_stream
+        torch.cuda.current_stream().wait_stream(side)
+        self.xa.zero_()
+        self.xb.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(ref, self.xa if (self.n_layers - 1) % 2 == 0 else self.xb))
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        del g
+        return sec, same
+
 
 # ---------------------------------------------------------------- CPU baseline -------
 
@@ -493,6 +524,11 @@ def main():
                     "frac": round(sb / ssec / 1e9 / HBM_PEAK_GBS, 4)},
         }
         log(f"  stack: {ssec * 1e3:.3f} ms per pass, {st.D.T / ssec:.1f} tokens/s")
+        gsec, gsame = st.time_graph(args.stack_steps)
+        line["stack_48"]["graph"] = {"value": round(st.D.T / gsec, 1), "unit": "tokens/s",
+                                     "ms_per_step": round(gsec * 1e3, 4), "equals_eager": gsame,
+                                     "what": "the same pass captured once as a HIP graph and replayed"}
+        log(f"  stack, HIP graph: {gsec * 1e3:.3f} ms per replay, equal to eager: {gsame}")
         del st
         torch.cuda.empty_cache()
 
