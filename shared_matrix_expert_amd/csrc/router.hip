@@ -207,25 +207,33 @@ EM_DEV uint64_t topk_key(float v, int i) {
 }
 
 template <int CTRL, int ROW_MASK>
-EM_DEV uint64_t dpp_max_step(uint64_t x) {
-    const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
-    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+EM_DEV uint32_t dpp_max_u32(uint32_t x) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROW_MASK, 0xF, false);
     return o > x ? o : x;
 }
 
-// Maximum key over the wave, the same value in every lane.
+// Maximum of an unsigned 32-bit value over the wave, the same value in every lane.
+EM_DEV uint32_t wave_max_u32(uint32_t x) {
+    x = dpp_max_u32<0xB1, 0xF>(x);       // quad_perm [1,0,3,2]
+    x = dpp_max_u32<0x4E, 0xF>(x);       // quad_perm [2,3,0,1]
+    x = dpp_max_u32<0x141, 0xF>(x);      // row_half_mirror
+    x = dpp_max_u32<0x140, 0xF>(x);      // row_mirror
+    x = dpp_max_u32<0x142, 0xA>(x);      // row_bcast:15
+    x = dpp_max_u32<0x143, 0xC>(x);      // row_bcast:31: lane 63 holds the maximum
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Maximum key over the wave, the same value in every lane: the maximum of
+// the upper halves (the logit bits), then, only when several lanes hold it,
+// the maximum lower half (~index) among those lanes.
 EM_DEV uint64_t wave_max_key(uint64_t x) {
-    x = dpp_max_step<0xB1, 0xF>(x);      // quad_perm [1,0,3,2]
-    x = dpp_max_step<0x4E, 0xF>(x);      // quad_perm [2,3,0,1]
-    x = dpp_max_step<0x141, 0xF>(x);     // row_half_mirror
-    x = dpp_max_step<0x140, 0xF>(x);     // row_mirror: every lane holds its row's maximum
-    x = dpp_max_step<0x142, 0xA>(x);     // row_bcast:15 into rows 1 and 3
-    x = dpp_max_step<0x143, 0xC>(x);     // row_bcast:31 into rows 2 and 3: lane 63 holds the maximum
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+    const uint32_t hi = (uint32_t)(x >> 32), lo = (uint32_t)x;
+    const uint32_t mh = wave_max_u32(hi);
+    const uint64_t tied = __ballot(hi == mh);
+    uint32_t ml;
+    if (__popcll(tied) == 1) ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((long long)tied) - 1);
+    else ml = wave_max_u32(hi == mh ? lo : 0u);
+    return ((uint64_t)mh << 32) | ml;
 }
 
 // Descending sort of N keys (N a power of two) with Batcher's odd-even merge
