@@ -89,7 +89,9 @@ Layout make_layout(const edge_moe_dims& d) {
     L.o = take((size_t)L.R * d.d * 4);
     L.fwd_bytes = off;
     L.logits = 0;
+    // fp32 logits, then (small batches) the router's K-slice sums
     L.route_bytes = align_up((size_t)T * E * 4);
+    if (em::router_split_ok((int)T, d.d, (int)E)) L.route_bytes += align_up(em::router_split_bytes((int)T, (int)E));
     return L;
 }
 
@@ -250,16 +252,22 @@ int edge_moe_route(const edge_moe_dims* dims, const uint16_t* x, const uint16_t*
     if (router_bias && !aligned(router_bias, 4)) return EDGE_MOE_EINVAL;
     if (logits_out && !aligned(logits_out, 4)) return EDGE_MOE_EINVAL;
     const Layout L = make_layout(*dims);
+    const edge_moe_dims& d = *dims;
     float* logits = logits_out;
     if (!logits) {
         if (!ws || !aligned(ws, kAlign)) return ws ? EDGE_MOE_EINVAL : EDGE_MOE_EWORKSPACE;
         if (ws_bytes < L.route_bytes) return EDGE_MOE_EWORKSPACE;
-        logits = reinterpret_cast<float*>(ws);
     }
+    // small batches use the K-split logits when the workspace is there for
+    // their slice sums (a caller that passes logits_out may pass no workspace)
+    double* part = nullptr;
+    if (em::router_split_ok(d.T, d.d, d.n_experts) && ws && aligned(ws, kAlign) && ws_bytes >= L.route_bytes)
+        part = reinterpret_cast<double*>(static_cast<char*>(ws) + align_up((size_t)d.T * d.n_experts * 4));
+    else if (!logits)
+        logits = reinterpret_cast<float*>(ws);
     st = check_device();
     if (st != EDGE_MOE_OK) return st;
-    const edge_moe_dims& d = *dims;
-    hipError_t err = em::launch_router(x, w_router, router_bias, logits, topk_idx, topk_w, d.T, d.d,
+    hipError_t err = em::launch_router(x, w_router, router_bias, logits, part, topk_idx, topk_w, d.T, d.d,
                                        d.n_experts, d.top_k, (hipStream_t)stream);
     return err == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
 }

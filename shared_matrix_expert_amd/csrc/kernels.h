@@ -100,8 +100,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 int decode_ns_down(int T);   // rows per down-kernel pass = 16 * decode_ns_down(T)
 bool decode_lds_ok(int T, int d, int h, int r, int rL, int gq, int S1);
 
+// Router launches.  `part` (nullable) is workspace for the K-split small-batch
+// path (router_split_ok shapes: RK_NSL x T x E doubles); `logits` may then be
+// null (no logits output), and must be given otherwise.
+bool router_split_ok(int T, int d, int E);
+size_t router_split_bytes(int T, int E);
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias,
-                         float* logits, int32_t* idx, float* w, int T, int d, int E, int k,
+                         float* logits, double* part, int32_t* idx, float* w, int T, int d, int E, int k,
                          hipStream_t stream);
 
 hipError_t launch_dispatch(const int32_t* idx, const DispatchBufs& db, int T, int k, int E,

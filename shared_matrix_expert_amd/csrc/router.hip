@@ -116,6 +116,63 @@ router_logits_small(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     }
 }
 
+// ------------------------------------------------------- K-split small batches ----
+// Up to 8 tokens, d = RK_NSL * 512.  A workgroup takes 8 experts and one K slice
+// of 512: the slice of the tokens' rows and of the experts' rows is staged in
+// LDS (16 KB instead of the whole x per workgroup), lane (t, e) of each wave
+// forms the exact float64 dot product over a quarter of the slice, and the
+// quarters are added in order.  The slice sums go to the workspace; the top-k
+// kernel adds the slices in order and rounds once.  Every partial sum of exact
+// bf16 products is exact in float64 here, as the whole sum is, so the logits
+// are the same bits as the one-pass kernel's.
+constexpr int RK_SLICE = 512;
+constexpr int RK_NSL = 8;
+
+__global__ void __launch_bounds__(256)
+router_logits_split(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                    double* __restrict__ part, int T, int d, int E) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[8][RK_SLICE + 8];    // rows 1040 B apart
+    __shared__ __attribute__((aligned(16))) uint16_t wsm[8][RK_SLICE + 8];
+    __shared__ double red[3][kWave];
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+    const int e0 = blockIdx.x * 8, k0 = blockIdx.y * RK_SLICE;
+    uint4 xv[2], wv8[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = tid + 256 * u, r = q >> 6, seg = q & 63;
+        xv[u] = *reinterpret_cast<const uint4*>(x + (size_t)min(r, T - 1) * d + k0 + 8 * seg);
+        wv8[u] = *reinterpret_cast<const uint4*>(wr + (size_t)(e0 + r) * d + k0 + 8 * seg);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = tid + 256 * u, r = q >> 6, seg = q & 63;
+        *reinterpret_cast<uint4*>(&xs[r][8 * seg]) = r < T ? xv[u] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&wsm[r][8 * seg]) = wv8[u];
+    }
+    __syncthreads();
+    const int t = lane & 7, e = lane >> 3;
+    double acc = 0.0;
+#pragma unroll 4
+    for (int kk = wv * (RK_SLICE / 4); kk < (wv + 1) * (RK_SLICE / 4); kk += 8) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&xs[t][kk]);
+        const uint4 b = *reinterpret_cast<const uint4*>(&wsm[e][kk]);
+        const uint32_t au[4] = {a.x, a.y, a.z, a.w}, bu[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc = fma((double)bf16_to_f32(au[q] & 0xFFFFu), (double)bf16_to_f32(bu[q] & 0xFFFFu), acc);
+            acc = fma((double)bf16_to_f32(au[q] >> 16), (double)bf16_to_f32(bu[q] >> 16), acc);
+        }
+    }
+    if (wv > 0) red[wv - 1][lane] = acc;
+    __syncthreads();
+    if (wv == 0 && t < T) {
+        double sum = acc + red[0][lane];
+        sum += red[1][lane];
+        sum += red[2][lane];
+        part[((size_t)blockIdx.y * T + t) * E + e0 + e] = sum;
+    }
+}
+
 // -------------------------------------------------------------- large batches ----
 // 128 tokens x 128 experts per workgroup, 8 x 8 float64 accumulators per thread,
 // K staged through LDS in chunks of 16 as float64.  Thread (ty, tx) owns tokens
@@ -267,18 +324,13 @@ EM_DEV uint64_t select_lanes(uint64_t a, uint64_t b, uint64_t lanes) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// The selection of one token's top k from its logits (lane l holds experts
+// l + 64 i), by one wave.
 template <int MAXPER>
-__global__ void __launch_bounds__(256)
-router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
-            float* __restrict__ topk_w, int T, int E, int k) {
+EM_DEV void topk_select(const float (&lv)[MAXPER], int t, int E, int k, int32_t* __restrict__ topk_idx,
+                        float* __restrict__ topk_w) {
     const int lane = lane_id();
-    const int t = blockIdx.x * 4 + wave_id();
-    if (t >= T) return;
     uint64_t key[MAXPER];
-    const float* row = logits + (size_t)t * E;
-    float lv[MAXPER];
-#pragma unroll
-    for (int i = 0; i < MAXPER; ++i) lv[i] = row[min(lane + kWave * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
         const int e = lane + kWave * i;
@@ -310,10 +362,79 @@ router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
     }
 }
 
+template <int MAXPER>
+__global__ void __launch_bounds__(256)
+router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+            int T, int E, int k) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + wave_id();
+    if (t >= T) return;
+    const float* row = logits + (size_t)t * E;
+    float lv[MAXPER];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) lv[i] = row[min(lane + kWave * i, E - 1)];
+    topk_select<MAXPER>(lv, t, E, k, topk_idx, topk_w);
+}
+
+// One workgroup per token for the K-split logits: every thread adds the slice
+// sums of two experts in slice order (all loads in flight), rounds once, adds
+// the bias, and stores the logit (to LDS, and to `logits` when given); then
+// one wave selects.
+__global__ void __launch_bounds__(256)
+router_topk_split(const double* __restrict__ part, const float* __restrict__ bias, float* __restrict__ logits,
+                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int E, int k) {
+    __shared__ float lg[8 * kWave];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    double pv[2][RK_NSL];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int sl = 0; sl < RK_NSL; ++sl)
+            pv[h][sl] = part[((size_t)sl * T + t) * E + min(tid + 256 * h, E - 1)];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int e = tid + 256 * h;
+        double sum = pv[h][0];
+#pragma unroll
+        for (int sl = 1; sl < RK_NSL; ++sl) sum += pv[h][sl];
+        float l = (float)sum;
+        if (e < E) {
+            if (bias) l = l + bias[e];
+            lg[e] = l;
+            if (logits) logits[(size_t)t * E + e] = l;
+        }
+    }
+    __syncthreads();
+    if (wave_id() != 0) return;
+    float lv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lv[i] = lg[min(lane_id() + kWave * i, E - 1)];
+    topk_select<8>(lv, t, E, k, topk_idx, topk_w);
+}
+
+
 // -------------------------------------------------------------- launchers -------
+size_t router_split_bytes(int T, int E) { return (size_t)RK_NSL * T * E * sizeof(double); }
+
+bool router_split_ok(int T, int d, int E) {
+    return T <= 8 && d == RK_NSL * RK_SLICE && E % 8 == 0 && E <= 8 * kWave;
+}
+
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias,
-                         float* logits, int32_t* idx, float* w, int T, int d, int E, int k,
+                         float* logits, double* part, int32_t* idx, float* w, int T, int d, int E, int k,
                          hipStream_t stream) {
+    if (part && router_split_ok(T, d, E)) {
+        prof_begin(stream);
+        router_logits_split<<<dim3(E / 8, RK_NSL), 256, 0, stream>>>(x, wr, part, T, d, E);
+        prof_end(stream, "router_logits_split");
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        prof_begin(stream);
+        router_topk_split<<<T, 256, 0, stream>>>(part, bias, logits, idx, w, T, E, k);
+        prof_end(stream, "router_topk");
+        return hipGetLastError();
+    }
+    if (!logits) return hipErrorInvalidValue;
     if (T <= 2 * RS_TOK && d <= RS_D && d % 128 == 0) {
         const int ntg = (T + RS_TOK - 1) / RS_TOK;
         prof_begin(stream);

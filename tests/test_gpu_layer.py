@@ -313,14 +313,14 @@ def test_top1_routing():
     assert torch.all(w == 1.0)
 
 
-@pytest.mark.parametrize("E,T", [(64, 8), (512, 8), (1024, 8), (512, 40)])
-def test_route_ties(E, T):
+@pytest.mark.parametrize("E,T,d", [(64, 8, 256), (512, 8, 256), (1024, 8, 256), (512, 40, 256), (512, 8, 4096)])
+def test_route_ties(E, T, d):
     """Many equal logits (experts share one of 5 weight rows, every 13th row is
     zero): the order must be descending logit, equal logits by lower index.
-    Covers both top-k register layouts (E <= 512 and E <= 1024) and both logits
-    kernels (T <= 16 and larger batches)."""
-    say(f"case: route ties E={E} T={T}")
-    D = synth.Dims(T=T, d=256, h=256, n_experts=E, experts_per_group=max(E // 16, 4), top_k=10,
+    Covers both top-k register layouts (E <= 512 and E <= 1024) and the three
+    logits kernels (T <= 16; larger batches; the K-split one at d = 4096)."""
+    say(f"case: route ties E={E} T={T} d={d}")
+    D = synth.Dims(T=T, d=d, h=256, n_experts=E, experts_per_group=max(E // 16, 4), top_k=10,
                    delta_rank=8, lora_rank=2, quant_group=32)
     rng = np.random.default_rng(E + T)
     x = synth.bf16_bits_from_f32(rng.standard_normal((T, D.d), dtype=np.float32))
