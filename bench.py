@@ -65,13 +65,18 @@ def kernel_bytes(D, idx: np.ndarray):
     d, h, r, rL, E = D.d, D.h, D.delta_rank, D.lora_rank, D.n_experts
     x_b = T * d * 2                       # the batch, bf16
     logits_b = T * E * 4
+    split = T <= 8 and d == 4096 and E % 8 == 0 and E <= 512
+    split_b = 8 * T * E * 8
     gw_up = per["s_up"] + per["lu_u"] + per["lu_v"]
     gw_dn = per["s_dn"] + per["ld_u"] + per["ld_v"]
     return {
-        # router (both paths)
+        # router: the one-pass logits kernels write fp32 logits that the top-k
+        # reads; the K-split one (up to 8 tokens, d = 4096) writes 8 fp64 slice
+        # sums per logit, which the top-k reads instead
         "router_logits_small": per["w_router"] + x_b + logits_b,
         "router_logits_tiled": per["w_router"] + x_b + logits_b,
-        "router_topk": logits_b + R * 8,
+        "router_logits_split": per["w_router"] + x_b + split_b,
+        "router_topk": (split_b if split else logits_b) + R * 8,
         # decode / verify path: each touched group's and expert's weights once,
         # the kernel's inputs read once and its outputs written once
         "dec_up": G * (per["s_up"] + per["lu_u"]) + X * per["a_up"] + x_b
