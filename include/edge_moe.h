@@ -134,10 +134,21 @@ size_t edge_moe_workspace_bytes(const edge_moe_dims* dims);
  *   topk_idx     [T][k] int32 out: selected experts, descending logit, ties to
  *                the lower index
  *   topk_w       [T][k] float32 out: softmax over the k selected logits
- *   logits_out   [T][E] float32 out or NULL: the logits, each the correctly
- *                rounded float32 of the exact dot product (accumulated in
- *                float64), plus the bias added in float32
+ *   logits_out   [T][E] float32 out or NULL: the logits, each the float64
+ *                sum of the bf16 x bf16 products rounded once to float32,
+ *                then the bias added in float32 and the sum rounded again
  *   ws, ws_bytes device workspace (>= edge_moe_workspace_bytes(dims))
+ * Exactness.  Every bf16 x bf16 product is exact in float64.  The float64
+ * sum is the exact dot product, and each logit the correctly rounded float32
+ * of it, whenever the products of the dot are all multiples of 2^Q and the
+ * sum of their magnitudes is below 2^(53+Q) (then every partial sum, in any
+ * order, is an exact float64).  At d = 4096 it holds whenever the ratio of the
+ * largest to the smallest nonzero magnitude of x's row, times the same ratio
+ * for w_router's row, is below 2^25.  Outside it
+ * the float64 accumulation may round, and a logit can differ from the
+ * correctly rounded value by one float32 unit in the last place when the exact
+ * sum lies within that rounding error of a float32 midpoint; this is not
+ * detected.  The selection and weights follow the logits as computed.
  * Non-finite inputs are not supported (undefined results). */
 int edge_moe_route(const edge_moe_dims* dims, const uint16_t* x, const uint16_t* w_router,
                    const float* router_bias, int32_t* topk_idx, float* topk_w,
@@ -213,7 +224,9 @@ int edge_moe_abi_version(void);
  * and the per-kernel elapsed times are accumulated under the kernel's name.
  * edge_moe_prof_read fills up to `cap` entries (name, launches, total ms) after
  * synchronising the recorded events and returns the number of kernel names;
- * edge_moe_prof_reset clears the table.  Host-side bookkeeping, not thread-safe. */
+ * edge_moe_prof_reset clears the table.  Host-side bookkeeping for
+ * measurement, guarded by one lock: calls from several threads are safe, and
+ * while profiling is on every enqueue also records two events on its stream. */
 int  edge_moe_prof_enable(int on);
 int  edge_moe_prof_read(char (*names)[64], int64_t* launches, double* total_ms, int cap);
 void edge_moe_prof_reset(void);

@@ -1,6 +1,7 @@
 // C-ABI entry points: validation, workspace layout and launch sequencing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <mutex>
 #include <string>
@@ -97,22 +98,7 @@ Layout make_layout(const edge_moe_dims& d) {
 
 // Small-batch path: T <= 64 tokens and at most 1024 (token, slot) pairs.
 bool use_decode(const edge_moe_dims& d) {
-    // EDGE_MOE_GENERAL_PATH=1 forces the general path (used by tests to cover it)
-    static const bool force_general = [] {
-        const char* v = getenv("EDGE_MOE_GENERAL_PATH");
-        return v && v[0] == '1';
-    }();
-    return !force_general && d.T <= 64 && (int64_t)d.T * d.top_k <= 1024 && d.experts_per_group <= 64;
-}
-
-// EDGE_MOE_OLD_GEMM=1 keeps large batches on the per-wave streaming GEMMs
-// instead of the LDS-tiled shared-matrix GEMMs (used by tests to cover both).
-bool force_old_gemm() {
-    static const bool v = [] {
-        const char* e = getenv("EDGE_MOE_OLD_GEMM");
-        return e && e[0] == '1';
-    }();
-    return v;
+    return d.T <= 64 && (int64_t)d.T * d.top_k <= 1024 && d.experts_per_group <= 64;
 }
 
 struct DecLayout {
@@ -175,27 +161,31 @@ int check_device() {
 }
 
 // ----------------------------------------------------------------- profiling ----
+// Measurement-only state (off unless edge_moe_prof_enable(1)).  One mutex
+// guards the event pool and the table, so concurrent calls from several host
+// threads may profile; the flag is read without the lock on the fast path.
 struct ProfEntry { std::string name; hipEvent_t e0, e1; };
 struct ProfState {
-    bool on = false;
+    std::atomic<bool> on{false};
+    std::mutex mu;
     std::vector<ProfEntry> pending;
     std::vector<hipEvent_t> pool;
-    hipEvent_t cur = nullptr;
+    std::unordered_map<hipStream_t, hipEvent_t> cur;     // open bracket per stream
     std::vector<std::string> order;
     std::unordered_map<std::string, std::pair<int64_t, double>> table;
 };
 ProfState& prof() { static ProfState s; return s; }
 
-hipEvent_t prof_event() {
-    ProfState& p = prof();
+// caller holds p.mu
+hipEvent_t prof_event(ProfState& p) {
     if (!p.pool.empty()) { hipEvent_t e = p.pool.back(); p.pool.pop_back(); return e; }
     hipEvent_t e = nullptr;
     hipEventCreate(&e);
     return e;
 }
 
-void prof_drain() {
-    ProfState& p = prof();
+// caller holds p.mu
+void prof_drain(ProfState& p) {
     for (auto& en : p.pending) {
         hipEventSynchronize(en.e1);
         float ms = 0.f;
@@ -214,18 +204,23 @@ void prof_drain() {
 namespace em {
 void prof_begin(hipStream_t s) {
     ProfState& p = prof();
-    if (!p.on) return;
-    p.cur = prof_event();
-    hipEventRecord(p.cur, s);
+    if (!p.on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(p.mu);
+    hipEvent_t e = prof_event(p);
+    hipEventRecord(e, s);
+    p.cur[s] = e;
 }
 void prof_end(hipStream_t s, const char* name) {
     ProfState& p = prof();
-    if (!p.on || !p.cur) return;
-    hipEvent_t e1 = prof_event();
+    if (!p.on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(p.mu);
+    auto it = p.cur.find(s);
+    if (it == p.cur.end()) return;
+    hipEvent_t e1 = prof_event(p);
     hipEventRecord(e1, s);
-    p.pending.push_back({name, p.cur, e1});
-    p.cur = nullptr;
-    if (p.pending.size() > 4096) prof_drain();
+    p.pending.push_back({name, it->second, e1});
+    p.cur.erase(it);
+    if (p.pending.size() > 4096) prof_drain(p);
 }
 }  // namespace em
 
@@ -421,7 +416,7 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     a.max_etiles = (int)((R + a.mt - 1) / a.mt + (E < R ? E : R));
     a.max_gtiles_u = (int)((L.Umax + a.mt - 1) / a.mt + G);
     a.max_gtiles_r = (int)((R + a.mt - 1) / a.mt + G);
-    a.pf = em::prefill_gemm_ok(d.d, d.h, d.delta_rank, d.lora_rank, d.quant_group) && !force_old_gemm() ? 1 : 0;
+    a.pf = em::prefill_gemm_ok(d.d, d.h, d.delta_rank, d.lora_rank, d.quant_group) ? 1 : 0;
     a.umax = L.Umax;
     a.rmax = R;
 
@@ -510,15 +505,13 @@ const char* edge_moe_status_string(int status) {
 int edge_moe_abi_version(void) { return EDGE_MOE_ABI_VERSION; }
 
 int edge_moe_prof_enable(int on) {
-    ProfState& p = prof();
-    const int was = p.on ? 1 : 0;
-    p.on = on != 0;
-    return was;
+    return prof().on.exchange(on != 0) ? 1 : 0;
 }
 
 int edge_moe_prof_read(char (*names)[64], int64_t* launches, double* total_ms, int cap) {
-    prof_drain();
     ProfState& p = prof();
+    std::lock_guard<std::mutex> lk(p.mu);
+    prof_drain(p);
     int i = 0;
     for (const auto& n : p.order) {
         if (i < cap) {
@@ -537,8 +530,9 @@ int edge_moe_prof_read(char (*names)[64], int64_t* launches, double* total_ms, i
 }
 
 void edge_moe_prof_reset(void) {
-    prof_drain();
     ProfState& p = prof();
+    std::lock_guard<std::mutex> lk(p.mu);
+    prof_drain(p);
     p.table.clear();
     p.order.clear();
 }

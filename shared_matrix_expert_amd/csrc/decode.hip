@@ -20,6 +20,8 @@
 // needs (an expert's rows, a group's tokens or rows) from topk_idx in LDS.
 // Every cross-workgroup sum is taken in a fixed order, so results are
 // bitwise reproducible.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_ops.h"
@@ -1910,19 +1912,23 @@ dec_down_ws(DecodeArgs a) {
 // ------------------------------------------------------------------ launcher -------
 // Workgroups of `kernel` (256 threads) that fit on the current device at once:
 // compute units x resident workgroups per unit, cached per kernel and device.
+// The cache is written with atomic stores: threads racing on the first call
+// compute and store the same value.
 template <class K>
 static int resident_grid(K kernel) {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0, per = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, 0) != hipSuccess || per <= 0) per = 1;
-        cached[dev] = cus * per;
+        v = cus * per;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 // Shapes the wave-streamed shared down takes: quant groups of 128, r = 128,
 // LoRA rank a multiple of 8 up to 32, h a multiple of one staged piece (1024
@@ -1949,16 +1955,18 @@ static bool up_ws_ok(const DecodeArgs& a) {
 }
 
 static int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        cached[dev] = cus;
+        v = cus;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 template <int NS, bool LDSP>

@@ -171,14 +171,84 @@ def test_tile_shared_layout():
         assert np.array_equal(dq.cpu().numpy().reshape(-1), _tiled_reference(q))
 
 
-def test_prefill_layer_sampled():
-    say("case: prefill C3 seed=0, sampled tokens")
+def _tile_cover_sample(offs, row_tok, P, G, T, target, seed=0, tile=128):
+    """Tokens chosen so that every 128-row tile of the prefill GEMMs holds at
+    least one of them: the shared-up rows (distinct tokens of each group, by
+    token), the shared-down rows (each group's rows, by expert then token) and
+    the rank-128 input rows (each expert's rows, by token).  Greedy over the
+    tiles in order, then random tokens up to `target`."""
+    rng = np.random.default_rng(seed)
+    tiles = []                                   # arrays of the tokens in each tile
+    for g in range(G):
+        rows = row_tok[offs[g * P]:offs[(g + 1) * P]]
+        for t0 in range(0, rows.size, tile):
+            tiles.append(rows[t0:t0 + tile])
+        u = np.unique(rows)
+        for t0 in range(0, u.size, tile):
+            tiles.append(u[t0:t0 + tile])
+    for e in range(G * P):
+        rows = row_tok[offs[e]:offs[e + 1]]
+        for t0 in range(0, rows.size, tile):
+            tiles.append(rows[t0:t0 + tile])
+    chosen = set()
+    for tl in tiles:
+        if not chosen.intersection(tl.tolist()):
+            chosen.add(int(rng.choice(tl)))
+    n_cover = len(chosen)
+    while len(chosen) < max(target, n_cover):
+        chosen.add(int(rng.integers(T)))
+    return np.array(sorted(chosen)), n_cover, len(tiles)
+
+
+def test_prefill_layer_tile_cover():
+    """The 16K-token prefill at full size: the whole permutation (163,840 slots)
+    against a numpy lexsort, and logits, indices and y against the oracle on
+    >= 1024 tokens chosen so that every 128-row tile of every prefill GEMM
+    (shared up, shared down, the rank-128 inputs of every expert) holds a
+    checked row."""
+    say("case: prefill C3 seed=0, tile-covering token sample")
     D = synth.config(3).dims
     x, wr, bias = _inputs(3, 0)
-    rng = np.random.default_rng(0)
-    sample = np.unique(np.concatenate([[0, D.T - 1], rng.choice(D.T, 30, replace=False)]))
-    lay, idx, w, y, _, _ = _run_parity(D, x, wr, bias, synth.make_weights(3, 0, device="cuda"),
-                                       sample=sample)
+    Wdev = synth.make_weights(3, 0, device="cuda")
+    lay = Layer(D, Wdev)
+    xd = bits_to_dev(x)
+    idx, w, lg = lay.route(xd, bits_to_dev(wr), f32_to_dev(bias))
+    R = D.T * D.top_k
+    tr = {"expert_offsets": torch.empty(D.n_experts + 1, dtype=torch.int32, device=DEV),
+          "row_token": torch.empty(R, dtype=torch.int32, device=DEV),
+          "row_slot": torch.empty(R, dtype=torch.int32, device=DEV)}
+    y = torch.empty(D.T, D.d, dtype=torch.float32, device=DEV)
+    em.edge_moe_forward(D, xd, idx, w, lay.W, y, lay.ws, trace=tr)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    offs, rt, rs = expected_permutation(idx_h, D.n_experts)
+    assert np.array_equal(tr["expert_offsets"].cpu().numpy(), offs), "expert offsets differ"
+    assert np.array_equal(tr["row_token"].cpu().numpy(), rt), "row tokens differ"
+    assert np.array_equal(tr["row_slot"].cpu().numpy(), rs), "row slots differ"
+    sample, n_cover, n_tiles = _tile_cover_sample(offs, rt, D.experts_per_group, D.n_groups, D.T, 1024)
+    say(f"  {n_cover} tokens cover {n_tiles} row tiles; {sample.size} tokens checked")
+    ref = route(x[sample], wr, bias, D.top_k)
+    assert np.array_equal(lg.cpu().numpy()[sample].astype(np.float64), ref["logits"]), "logits differ"
+    assert np.array_equal(idx_h[sample], ref["idx"]), "expert indices differ"
+    assert np.max(np.abs(w.cpu().numpy()[sample] - ref["w"])) <= 1e-6
+    fw = moe_forward(x[sample], ref["idx"], ref["w"], synth.weights_to_numpy(Wdev), D.experts_per_group)
+    ok, ratio = y_within_tolerance(y.cpu().numpy()[sample], fw["y"])
+    say(f"  worst |dy| / bound = {ratio:.3g}")
+    assert ok, f"y outside tolerance (worst ratio {ratio:.3g})"
+    y2, _ = lay.forward(xd, idx, w)
+    assert torch.equal(y, y2)
+
+
+def test_general_fallback_traced():
+    """A batch above the decode limit at shapes the LDS-tiled prefill GEMMs do
+    not take (quant groups of 32, r = 8): every stage on the general GEMM, with
+    the permutation, activations and expert outputs checked."""
+    say("case: general fallback GEMMs, C0 shapes at T=100, traced")
+    D = synth.config(0).dims.with_T(100)
+    x = synth.make_activations(0, 4, T=100)
+    wr, _ = synth.make_router(0, 4)
+    lay, idx, w, y, tr, fw = _run_parity(D, x, wr, None, synth.make_weights(0, 4, device="cuda"), keep=True)
+    _check_trace(D, idx, tr, fw)
     y2, _ = lay.forward(bits_to_dev(x), idx, w)
     assert torch.equal(y, y2)
 
@@ -268,11 +338,12 @@ def test_graph_replay_two_layers():
         assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {rep} differs from the eager pass"
 
 
-@pytest.mark.parametrize("T", [2, 13, 16, 37, 200])
+@pytest.mark.parametrize("T", [2, 13, 16, 24, 32, 37, 200])
 def test_ragged_batches(T):
     """Token counts that leave partial tiles and cross the router's small/large
     paths; 13 and 16 put more than 8 tokens into a group, so the shared up
-    stages x as 16 rows x 1024 elements instead of 8 x 2048."""
+    stages x as 16 rows x 1024 elements instead of 8 x 2048; 24 and 32 take
+    the two-subtile decode kernels."""
     say(f"case: ragged T={T}")
     D = synth.config(1).dims.with_T(T)
     x = synth.make_activations(1, 5, T=T)
@@ -360,6 +431,21 @@ def test_workspace_too_small_is_rejected():
     assert ei.value.status == em.EDGE_MOE_EWORKSPACE
 
 
+def _kernel_names(fn):
+    """Names of the library kernels that fn() enqueues (from the library's
+    kernel timing table)."""
+    em.edge_moe_prof_reset()
+    em.edge_moe_prof_enable(True)
+    try:
+        fn()
+        torch.cuda.synchronize()
+    finally:
+        em.edge_moe_prof_enable(False)
+    names = set(em.edge_moe_prof_read())
+    em.edge_moe_prof_reset()
+    return names
+
+
 def test_stack_48_teacher_forced():
     """The 48-layer stack (T=8, independent routers, residual between layers):
     the chain runs on the GPU; on sampled layers the oracle recomputes the layer
@@ -382,12 +468,23 @@ def test_stack_48_teacher_forced():
     row_scaled = (12, 24, cfg.layers - 1)
     lay = None
     x = bits_to_dev(synth.make_activations(4, 0))
+    # the kernels a verify batch with decode-tiled weights runs (the benchmark's
+    # stack takes the same path): every layer below must run exactly these
+    x2 = bits_to_dev(synth.make_activations(2, 0))
+    ref_lay = Layer(D, synth.make_weights(2, 0, device="cuda"))
+    ridx, rw, _ = ref_lay.route(x2, bits_to_dev(synth.make_router(2, 0)[0]), None)
+    ref_names = _kernel_names(lambda: ref_lay.forward(x2, ridx, rw))
+    del ref_lay
     for layer in range(cfg.layers):
         wr, _ = synth.make_router(4, 0, layer)
         W = synth.make_weights(4, 0, layer, device="cuda")
-        lay = Layer(D, W) if lay is None else lay
-        lay.W = W
+        if lay is None:
+            lay = Layer(D, W)                       # decode-tiled copies, as in the benchmark
+        else:
+            lay.W = em.tile_weights(D, W)
         idx, w, _ = lay.route(x, bits_to_dev(wr), None)
+        names = _kernel_names(lambda: lay.forward(x, idx, w))
+        assert names == ref_names, f"layer {layer}: kernels {names} differ from the verify path's {ref_names}"
         y, _ = lay.forward(x, idx, w)
         x_next = torch.empty_like(x)
         em.edge_moe_residual(x, y, x_next)

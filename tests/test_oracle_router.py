@@ -126,3 +126,36 @@ def test_skewed_verify_calibration():
         wr, bias = synth.make_router(2, seed, layer)
         idx = route(x, wr, bias, D.top_k)["idx"]
         assert int(np.sum(idx < 128)) == 48
+
+
+def test_bias_add_rounds_twice_closed_form():
+    """The bias is added to the already rounded fp32 logit and the sum is
+    rounded again (two roundings, each to nearest-even).
+
+    x = [1, 2^-30, 0, ...], W_r row = [1, 1, 0, ...], bias = 2^-24:
+    RN32(1 + 2^-30) = 1 exactly, then 1 + 2^-24 sits halfway between 1 and
+    1 + 2^-23 and ties to the even 1.  One rounding of the whole sum would
+    give 1 + 2^-23; no rounding after the add would leave 1 + 2^-24.  The
+    negated token with bias -2^-24 checks the same tie below -1.
+    """
+    d, E = 8, 4
+    xf = np.zeros((2, d), dtype=np.float32)
+    xf[0, 0], xf[0, 1] = 1.0, 2.0 ** -30
+    xf[1, 0], xf[1, 1] = -1.0, -(2.0 ** -30)
+    wf = np.zeros((E, d), dtype=np.float32)
+    wf[0, 0] = wf[0, 1] = 1.0
+    wf[1, 0] = wf[1, 1] = 1.0
+    x = synth.bf16_bits_from_f32(xf)
+    w = synth.bf16_bits_from_f32(wf)
+    assert codecs.bf16_to_f64(x)[0, 1] == 2.0 ** -30
+    bias = np.zeros(E, dtype=np.float32)
+    bias[0] = np.float32(2.0 ** -24)
+    bias[1] = np.float32(-(2.0 ** -24))
+    lg = route(x, w, bias, 2)["logits"]
+    assert lg[0, 0] == 1.0
+    assert lg[1, 1] == -1.0
+    # without a tie the bias shows: -1 + 2^-24 is exact (spacing below 1 is
+    # 2^-24), and 1 + 1.5 * 2^-24 rounds up to 1 + 2^-23
+    assert lg[1, 0] == -1.0 + 2.0 ** -24
+    bias[0] = np.float32(3 * 2.0 ** -25)
+    assert route(x, w, bias, 2)["logits"][0, 0] == 1.0 + 2.0 ** -23
