@@ -94,6 +94,12 @@ def kernel_bytes(D, idx: np.ndarray):
                        + R * (r + rL) * 2 + R * 4 + T * d * 4,
         "dec_down_wst": G * (per["s_dn"] + per["ld_v"]) + X * per["b_dn"] + R * h * 2
                         + R * (r + rL) * 2 + R * 4 + T * d * 4,
+        # the persistent decode layer: every touched group's and distinct
+        # expert's weights once, the batch read once and y written once (its
+        # intermediates stay in the workspace and the caches)
+        "dec_layer": G * (per["s_up"] + per["s_dn"] + per["lu_u"] + per["lu_v"] + per["ld_u"] + per["ld_v"])
+                     + X * (per["a_up"] + per["b_up"] + per["a_dn"] + per["b_dn"]) + x_b + T * d * 4,
+        "pl_clear": 1536 * 4,
         # general (prefill) path
         "gemm_z1": X * per["a_up"] + R * d * 2 + R * r * 2,
         "lora_in_up": G * per["lu_u"] + U * d * 2,

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define EDGE_MOE_ABI_VERSION 2
+#define EDGE_MOE_ABI_VERSION 3
 
 /* Status codes. */
 #define EDGE_MOE_OK           0
@@ -92,12 +92,15 @@ typedef struct edge_moe_dims {
 } edge_moe_dims;
 
 /* Weights of one layer (device pointers, layouts above; 16-byte aligned).
- * The last three members are optional decode-tiled copies of the int4 codes
- * written by edge_moe_tile_shared (the scales stay in the row-major arrays):
- * s_up_t and s_dn_t NULL or both set, a_up_t NULL or set.  When they are set,
- * batches of at most 16 tokens stream them instead of the row-major s_up_q /
- * s_dn_q / a_up_q (the row-major copies stay required: larger batches and the
- * other paths read them); both copies must hold the same values. */
+ * The last four members are optional stored copies of the int4 codes written
+ * by edge_moe_tile_shared (the scales stay in the row-major arrays): s_up_t
+ * and s_dn_t NULL or both set, a_up_t and a_dn_t each NULL or set.  When they
+ * are set, batches of at most 16 tokens stream them instead of the row-major
+ * codes (the row-major copies stay required: larger batches and the other
+ * paths read them); both copies must hold the same values.  With all four
+ * set, batches of at most 8 tokens (at most 128 token-slot pairs, d = 2048 or
+ * 4096, r = 128, rL = 8 or 16, quant groups of 128) run as one persistent
+ * launch after a small counter-clearing one. */
 typedef struct edge_moe_weights {
     const uint8_t*  s_up_q;  const uint16_t* s_up_scale;
     const uint8_t*  s_dn_q;  const uint16_t* s_dn_scale;
@@ -110,6 +113,7 @@ typedef struct edge_moe_weights {
     const uint8_t*  s_up_t;    /* optional, tiled s_up codes */
     const uint8_t*  s_dn_t;    /* optional, tiled s_dn codes */
     const uint8_t*  a_up_t;    /* optional, tiled a_up codes */
+    const uint8_t*  a_dn_t;    /* optional, column-blocked a_dn codes */
 } edge_moe_weights;
 
 /* Optional per-stage outputs of edge_moe_forward_traced (device pointers; any
@@ -193,7 +197,8 @@ int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream);
 const char* edge_moe_status_string(int status);
 
 /* Decode-tiled copy of the int4 codes of one matrix set (which = 0: s_up
- * [G][h][d], which = 1: s_dn [G][d][h], which = 2: a_up [E][r][d]), written
+ * [G][h][d], which = 1: s_dn [G][d][h], which = 2: a_up [E][r][d]; which = 3:
+ * the column-blocked a_dn [E][r][h], defined at the end), written
  * from the row-major packed codes src_q into dst_q of the same size (M*N*K/2
  * bytes for M matrices of N x K).  A stored-format conversion done once per
  * layer, outside any step: the layer's values are unchanged, and the scales
@@ -210,8 +215,15 @@ const char* edge_moe_status_string(int status);
  * the 32 codes of one row that a 16 x 16 x 32 matrix-core operand needs, and
  * a workgroup that streams one tile group reads one contiguous region.
  *
+ * Column-blocked a_dn (which = 3; requires r = 128 and h a multiple of 128):
+ * for expert e and block cb of 128 elements of h, the 128 rows' 64-byte
+ * segments follow each other: the 16 bytes at
+ *     (e * h/128 + cb) * 8192 + n * 64 + 16 j
+ * hold elements [128 cb + 32 j, +32) of row n of a_dn[e], packed as in the
+ * row-major layout.  One block of all rows is then one contiguous 8 KB.
+ *
  * Errors: EDGE_MOE_EINVAL for null or not 16-byte aligned pointers, or which
- * not 0, 1 or 2; EDGE_MOE_EUNSUPPORTED when the shape is outside the layout
+ * not 0..3; EDGE_MOE_EUNSUPPORTED when the shape is outside the layout
  * above.  src and dst must not overlap. */
 int edge_moe_tile_shared(const edge_moe_dims* dims, int32_t which, const uint8_t* src_q, uint8_t* dst_q,
                          void* stream);

@@ -40,14 +40,14 @@ class CDims(ctypes.Structure):
 _WEIGHT_FIELDS = ("s_up_q", "s_up_scale", "s_dn_q", "s_dn_scale", "a_up_q", "a_up_scale",
                   "b_up_q", "b_up_scale", "a_dn_q", "a_dn_scale", "b_dn_q", "b_dn_scale",
                   "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v",
-                  "s_up_t", "s_dn_t", "a_up_t")
+                  "s_up_t", "s_dn_t", "a_up_t", "a_dn_t")
 # keys of the weight dicts made by the input generator -> struct fields (the
-# last three, the decode-tiled codes, are optional)
+# last four, the decode-tiled and column-blocked codes, are optional)
 _WEIGHT_KEYS = ("s_up", "s_up_scale", "s_dn", "s_dn_scale", "a_up", "a_up_scale",
                 "b_up", "b_up_scale", "a_dn", "a_dn_scale", "b_dn", "b_dn_scale",
                 "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v",
-                "s_up_t", "s_dn_t", "a_up_t")
-_OPTIONAL_KEYS = ("s_up_t", "s_dn_t", "a_up_t")
+                "s_up_t", "s_dn_t", "a_up_t", "a_dn_t")
+_OPTIONAL_KEYS = ("s_up_t", "s_dn_t", "a_up_t", "a_dn_t")
 
 
 class CWeights(ctypes.Structure):
@@ -138,7 +138,8 @@ def cweights(weights: dict) -> CWeights:
 
 
 def edge_moe_tile_shared(dims, which, src_q, dst_q, stream=None) -> None:
-    """Decode-tiled copy of the codes of s_up (which=0), s_dn (1) or a_up (2)."""
+    """Decode-tiled copy of the codes of s_up (which=0), s_dn (1) or a_up (2),
+    or the column-blocked copy of a_dn (3)."""
     st = load().edge_moe_tile_shared(ctypes.byref(cdims(dims)), int(which), _ptr(src_q), _ptr(dst_q),
                                      _stream(stream))
     if st != EDGE_MOE_OK:
@@ -147,12 +148,14 @@ def edge_moe_tile_shared(dims, which, src_q, dst_q, stream=None) -> None:
 
 def tile_weights(dims, weights: dict, stream=None) -> dict:
     """A copy of the weight dict with the decode-tiled codes added (new device
-    tensors of the sizes of s_up / s_dn / a_up; a_up only when its rank is a
-    multiple of 128)."""
+    tensors of the sizes of s_up / s_dn / a_up / a_dn; a_up only when its rank
+    is a multiple of 128, a_dn only when its rank is 128)."""
     import torch
     out = dict(weights)
-    for which, key in ((0, "s_up"), (1, "s_dn"), (2, "a_up")):
+    for which, key in ((0, "s_up"), (1, "s_dn"), (2, "a_up"), (3, "a_dn")):
         if which == 2 and dims.delta_rank % 128:
+            continue
+        if which == 3 and dims.delta_rank != 128:
             continue
         q = torch.empty_like(weights[key])
         edge_moe_tile_shared(dims, which, weights[key], q, stream)

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libedge_moe.so")
-SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "decode.hip", "layer.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -103,8 +103,9 @@ bool use_decode(const edge_moe_dims& d) {
 
 struct DecLayout {
     size_t hs, z1p, zlp, act, z2p, z2, zl2, o, od, cnt_e, cnt_c, scratch, bytes;
+    size_t pl_ctr, pl_z1p, pl_zlp, pl_z1b, pl_zlb, pl_z2p;   // persistent layer (T <= 8, r = 128)
     int S1, cb2, ncb2, N2;
-    bool lds;
+    bool lds, pl;
 };
 
 DecLayout make_dec_layout(const edge_moe_dims& d) {
@@ -130,6 +131,16 @@ DecLayout make_dec_layout(const edge_moe_dims& d) {
     L.cnt_e = take((size_t)d.n_experts * 4);
     L.cnt_c = take((size_t)(d.d / 64) * 4);
     L.scratch = take(64 * 4);
+    // the persistent layer's buffers, for the shapes it can take
+    L.pl = T <= 8 && R <= 128 && d.delta_rank == 128 && d.lora_rank <= 16;
+    if (L.pl) {
+        L.pl_ctr = take((size_t)em::PL_C_COUNT * 4);
+        L.pl_z1p = take((size_t)4 * R * 128 * 4);
+        L.pl_zlp = take((size_t)4 * T * G * 16 * 4);
+        L.pl_z1b = take((size_t)R * 128 * 2);
+        L.pl_zlb = take((size_t)T * G * 16 * 2);
+        L.pl_z2p = take((size_t)(d.h / 128) * R * em::PL_Z2W * 4);
+    }
     L.bytes = off;
     return L;
 }
@@ -140,6 +151,7 @@ bool aligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) == 0; }
 // of 1024 (whole tile groups of 128 rows, blocks of 256, and each row's scales
 // a whole number of 16-byte pieces); for A_up also r a multiple of 128.
 bool tile_shape_ok(const edge_moe_dims& d, int which = 0) {
+    if (which == 3) return d.delta_rank == 128 && d.h % 128 == 0;
     return d.quant_group == 128 && d.d % 1024 == 0 && d.h % 1024 == 0 && (which != 2 || d.delta_rank % 128 == 0);
 }
 
@@ -317,7 +329,7 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.a_up = wt->a_up_q; a.a_up_s = wt->a_up_scale; a.b_up = wt->b_up_q; a.b_up_s = wt->b_up_scale;
     a.a_dn = wt->a_dn_q; a.a_dn_s = wt->a_dn_scale; a.b_dn = wt->b_dn_q; a.b_dn_s = wt->b_dn_scale;
     a.lu_u = wt->lora_up_u; a.lu_v = wt->lora_up_v; a.ld_u = wt->lora_dn_u; a.ld_v = wt->lora_dn_v;
-    a.s_up_t = wt->s_up_t; a.s_dn_t = wt->s_dn_t; a.a_up_t = wt->a_up_t;
+    a.s_up_t = wt->s_up_t; a.s_dn_t = wt->s_dn_t; a.a_up_t = wt->a_up_t; a.a_dn_t = wt->a_dn_t;
     a.hs = reinterpret_cast<float*>(base + L.hs);
     a.z1p = reinterpret_cast<float*>(base + L.z1p);
     a.zlp = reinterpret_cast<float*>(base + L.zlp);
@@ -331,8 +343,17 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     a.cnt_c = reinterpret_cast<uint32_t*>(base + L.cnt_c);
     a.scratch = reinterpret_cast<float*>(base + L.scratch);
     a.od = reinterpret_cast<float*>(base + L.od);
+    if (L.pl) {
+        a.pl_ctr = reinterpret_cast<uint32_t*>(base + L.pl_ctr);
+        a.pl_z1p = reinterpret_cast<float*>(base + L.pl_z1p);
+        a.pl_zlp = reinterpret_cast<float*>(base + L.pl_zlp);
+        a.pl_z1b = reinterpret_cast<uint16_t*>(base + L.pl_z1b);
+        a.pl_zlb = reinterpret_cast<uint16_t*>(base + L.pl_zlb);
+        a.pl_z2p = reinterpret_cast<float*>(base + L.pl_z2p);
+    }
+    a.pl_trace_o = trace && trace->expert_out ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t err = em::launch_decode(a, s);
+    hipError_t err = (L.pl && em::dec_layer_ok(a)) ? em::launch_dec_layer(a, s) : em::launch_decode(a, s);
     if (err != hipSuccess) return EDGE_MOE_EHIP;
     if (trace) {
         // intermediates are stored per slot here; the permutation arrays come
@@ -376,6 +397,10 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     if (wt->a_up_t) {
         if (!aligned(wt->a_up_t, 16)) return EDGE_MOE_EINVAL;
         if (!tile_shape_ok(*dims, 2)) return EDGE_MOE_EUNSUPPORTED;
+    }
+    if (wt->a_dn_t) {
+        if (!aligned(wt->a_dn_t, 16)) return EDGE_MOE_EINVAL;
+        if (!tile_shape_ok(*dims, 3)) return EDGE_MOE_EUNSUPPORTED;
     }
     if (!ws) return EDGE_MOE_EWORKSPACE;
     if (!aligned(ws, kAlign)) return EDGE_MOE_EINVAL;
@@ -464,20 +489,21 @@ int edge_moe_tile_shared(const edge_moe_dims* dims, int32_t which, const uint8_t
                          void* stream) {
     const int st = check_dims(dims);
     if (st != EDGE_MOE_OK) return st;
-    if (which < 0 || which > 2) return EDGE_MOE_EINVAL;
+    if (which < 0 || which > 3) return EDGE_MOE_EINVAL;
     if (!aligned(src_q, 16) || !aligned(dst_q, 16)) return EDGE_MOE_EINVAL;
     if (!tile_shape_ok(*dims, which)) return EDGE_MOE_EUNSUPPORTED;
-    const int G = which == 2 ? dims->n_experts : dims->n_experts / dims->experts_per_group;
+    const int G = which >= 2 ? dims->n_experts : dims->n_experts / dims->experts_per_group;
     const int N = which == 0 ? dims->h : (which == 1 ? dims->d : dims->delta_rank);
-    const int K = which == 1 ? dims->h : dims->d;
+    const int K = (which == 1 || which == 3) ? dims->h : dims->d;
     const size_t qb = (size_t)G * N * K / 2;
     const char* s8 = reinterpret_cast<const char*>(src_q);
     const char* d8 = reinterpret_cast<const char*>(dst_q);
     if (d8 < s8 + qb && s8 < d8 + qb) return EDGE_MOE_EINVAL;
     const int dst_st = check_device();
     if (dst_st != EDGE_MOE_OK) return dst_st;
-    return em::launch_tile_shared(src_q, dst_q, G, N, K, (hipStream_t)stream) == hipSuccess ? EDGE_MOE_OK
-                                                                                            : EDGE_MOE_EHIP;
+    const hipError_t err = which == 3 ? em::launch_colblock(src_q, dst_q, G, N, K, (hipStream_t)stream)
+                                      : em::launch_tile_shared(src_q, dst_q, G, N, K, (hipStream_t)stream);
+    return err == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
 }
 
 int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream) {

@@ -393,6 +393,31 @@ tile_shared_q(uint4* __restrict__ dst, const uint8_t* __restrict__ src, int G, i
     }
 }
 
+// Column-blocked copy of M matrices N x K (packed int4): for matrix m and
+// block cb of 128 K elements, the N rows' 64-byte segments follow each other,
+// so one block of all N rows is one contiguous N * 64 bytes.
+__global__ void __launch_bounds__(256)
+colblock_q(uint4* __restrict__ dst, const uint8_t* __restrict__ src, int M, int N, int K) {
+    const size_t units = (size_t)M * N * K / 32;          // 16-byte units
+    const size_t per_cb = (size_t)N * 4;
+    const size_t per_m = (size_t)(K / 128) * per_cb;
+    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (size_t)gridDim.x * 256) {
+        const size_t m = u / per_m, rm = u % per_m;
+        const size_t cb = rm / per_cb, rc = rm % per_cb;
+        const size_t n = rc / 4, j = rc % 4;
+        dst[u] = *reinterpret_cast<const uint4*>(src + (m * N + n) * (size_t)(K / 2) + cb * 64 + 16 * j);
+    }
+}
+
+hipError_t launch_colblock(const uint8_t* src_q, uint8_t* dst_q, int M, int N, int K, hipStream_t stream) {
+    const size_t units = (size_t)M * N * K / 32;
+    const size_t bq = (units + 255) / 256 < 8192 ? (units + 255) / 256 : 8192;
+    prof_begin(stream);
+    colblock_q<<<(unsigned)bq, 256, 0, stream>>>(reinterpret_cast<uint4*>(dst_q), src_q, M, N, K);
+    prof_end(stream, "colblock");
+    return hipGetLastError();
+}
+
 hipError_t launch_tile_shared(const uint8_t* src_q, uint8_t* dst_q, int G, int N, int K, hipStream_t stream) {
     const size_t units = (size_t)G * N * K / 32;
     const size_t bq = (units + 255) / 256 < 8192 ? (units + 255) / 256 : 8192;

@@ -94,7 +94,30 @@ struct DecodeArgs {
     float* y;           // [T][d]
     uint32_t* cnt_e;    // [E]     arrivals per expert (activation kernel)
     uint32_t* cnt_c;    // [d/64]  arrivals per output column block (down kernel)
+    // persistent single-launch layer (layer.hip)
+    const uint8_t* a_dn_t;  // column-blocked A_dn codes [E][h/128][r][64 B] (or null)
+    uint32_t* pl_ctr;   // [PL_C_COUNT] task queue head and arrival counters (zeroed per launch)
+    float* pl_z1p;      // [4][R][r]     K-slice partial sums of A_up x
+    float* pl_zlp;      // [4][T][G][16] K-slice partial sums of U_up x
+    uint16_t* pl_z1b;   // [R][r]        z1 (R1), bf16
+    uint16_t* pl_zlb;   // [T][G][16]    zl (R2), bf16
+    float* pl_z2p;      // [h/128][R][PL_Z2W] per-column-block partial sums of A_dn a, U_dn a
+    int pl_trace_o;     // store o + od back into o (per-slot outputs for a trace)
 };
+
+// Counter words of the persistent layer (uint32 at pl_ctr).
+constexpr int PL_C_HEAD = 0;        // next task
+constexpr int PL_C_ZREADY = 1;      // experts and groups whose z1 / zl are rounded
+constexpr int PL_C_UP = 2;          // [64] up tasks done per group
+constexpr int PL_C_Z2 = 66;         // [64] R4 / R5 reduction parts done per group
+constexpr int PL_C_Z1E = 130;       // [1024] A_up x slices done per expert
+constexpr int PL_C_ZLG = 1154;      // [64] U_up x slices done per group
+constexpr int PL_C_DN = 1218;       // [256] down tasks done per 128-column block of d
+constexpr int PL_C_ERR = 1474;      // set when a bounded wait gives up
+constexpr int PL_C_COUNT = 1536;
+constexpr int PL_Z2W = 160;         // floats per partial row (r + rL <= 144, five cache lines)
+bool dec_layer_ok(const DecodeArgs& a);
+hipError_t launch_dec_layer(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 int decode_ns_down(int T);   // rows per down-kernel pass = 16 * decode_ns_down(T)
@@ -127,6 +150,7 @@ hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);
 hipError_t launch_act(const LayerArgs& a, hipStream_t s);     // needs r == 128, h % 256 == 0
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_tile_shared(const uint8_t* src_q, uint8_t* dst_q, int G, int N, int K, hipStream_t stream);
+hipError_t launch_colblock(const uint8_t* src_q, uint8_t* dst_q, int M, int N, int K, hipStream_t stream);
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,
                            hipStream_t stream);
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert em.edge_moe_abi_version() == 2
+    assert em.edge_moe_abi_version() == 3
     for st in (0, -1, -2, -3, -4):
         assert em.status_string(st)
     assert em.status_string(7) == "unknown status"
@@ -143,11 +143,14 @@ def test_tiled_weights_all_or_none():
         cw = em.CWeights(*ptrs)
         return lib.edge_moe_forward(ctypes.byref(em.cdims(dims)), 0x10000, 0x20000, 0x30000, ctypes.byref(cw),
                                     0x40000, 0x100000, em.edge_moe_workspace_bytes(dims), None)
-    assert fwd(D, [0x50000] * 16 + [0x60000, None, None]) == em.EDGE_MOE_EINVAL      # s_up without s_dn
-    assert fwd(D, [0x50000] * 16 + [0x60008, 0x70000, None]) == em.EDGE_MOE_EINVAL   # not 16-byte aligned
-    assert fwd(D, [0x50000] * 16 + [None, None, 0x80008]) == em.EDGE_MOE_EINVAL      # a_up not aligned
-    T0 = synth.config(0).dims                                                        # quant groups of 32
-    assert fwd(T0, [0x50000] * 19) == em.EDGE_MOE_EUNSUPPORTED
+    assert fwd(D, [0x50000] * 16 + [0x60000, None, None, None]) == em.EDGE_MOE_EINVAL      # s_up without s_dn
+    assert fwd(D, [0x50000] * 16 + [0x60008, 0x70000, None, None]) == em.EDGE_MOE_EINVAL   # not 16-byte aligned
+    assert fwd(D, [0x50000] * 16 + [None, None, 0x80008, None]) == em.EDGE_MOE_EINVAL      # a_up not aligned
+    assert fwd(D, [0x50000] * 16 + [None, None, None, 0x90008]) == em.EDGE_MOE_EINVAL      # a_dn not aligned
+    T0 = synth.config(0).dims                                                              # quant groups of 32
+    assert fwd(T0, [0x50000] * 20) == em.EDGE_MOE_EUNSUPPORTED
+    D64 = synth.Dims(**{**D.__dict__, "delta_rank": 64})                                  # a_dn needs r = 128
+    assert fwd(D64, [0x50000] * 16 + [None, None, None, 0x90000]) == em.EDGE_MOE_EUNSUPPORTED
 
 
 def test_tile_shared_validation_before_device():
@@ -161,7 +164,7 @@ def test_tile_shared_validation_before_device():
     def call(**kw):
         a = {**ok, **kw}
         return lib.edge_moe_tile_shared(cd, a["which"], ctypes.c_void_p(a["sq"]), ctypes.c_void_p(a["dq"]), None)
-    assert call(which=3) == em.EDGE_MOE_EINVAL
+    assert call(which=4) == em.EDGE_MOE_EINVAL
     assert call(which=-1) == em.EDGE_MOE_EINVAL
     assert call(sq=base + 8) == em.EDGE_MOE_EINVAL                 # not 16-byte aligned
     assert call(dq=base + 64) == em.EDGE_MOE_EINVAL                # overlaps the source
@@ -171,4 +174,6 @@ def test_tile_shared_validation_before_device():
                                     ctypes.c_void_p(base + big), None) == em.EDGE_MOE_EUNSUPPORTED
     D8 = synth.Dims(**{**D.__dict__, "delta_rank": 64})            # a_up rank not a multiple of 128
     assert lib.edge_moe_tile_shared(ctypes.byref(em.cdims(D8)), 2, ctypes.c_void_p(base),
+                                    ctypes.c_void_p(base + big), None) == em.EDGE_MOE_EUNSUPPORTED
+    assert lib.edge_moe_tile_shared(ctypes.byref(em.cdims(D8)), 3, ctypes.c_void_p(base),
                                     ctypes.c_void_p(base + big), None) == em.EDGE_MOE_EUNSUPPORTED
