@@ -177,6 +177,20 @@ int edge_moe_forward_traced(const edge_moe_dims* dims, const uint16_t* x,
                             const edge_moe_weights* weights, float* y, void* ws,
                             size_t ws_bytes, void* stream, const edge_moe_trace* trace);
 
+/* edge_moe_forward without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a 16 MiB array that the library holds on each GPU it runs on
+ * until the process ends (its device address is looked up once per device, on
+ * the first call there).  Every call on a GPU uses that GPU's one array, so
+ * calls that overlap on one GPU (concurrent streams or threads) race and must
+ * be serialised by the caller; each call overwrites what it reads.  Returns
+ * EDGE_MOE_EWORKSPACE when edge_moe_workspace_bytes(dims) exceeds 16 MiB (at
+ * d = 4096, h = 8192, 512 experts, top-10: up to 17 tokens); otherwise as
+ * edge_moe_forward. */
+int edge_moe_forward_noalloc(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                             const float* topk_w, const edge_moe_weights* weights, float* y, void* stream);
+
 /* Residual between stacked layers (a12): x_out[t][i] = bf16(x[t][i] + y[t][i]),
  * the exact sum rounded once to the nearest bf16 (ties to even).  The layers
  * are stacked 48 deep in the pages' model (byteiota, Not Compression -

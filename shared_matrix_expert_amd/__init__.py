@@ -28,7 +28,8 @@ EDGE_MOE_EHIP = -4
 EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_forward_traced", "edge_moe_residual", "edge_moe_status_string",
             "edge_moe_abi_version", "edge_moe_copy", "edge_moe_tile_shared",
-            "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset")
+            "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset",
+            "edge_moe_forward_noalloc")
 
 
 class CDims(ctypes.Structure):
@@ -92,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(CWeights), vp, vp, sz, vp,
                                             ctypes.POINTER(CTrace)]
     lib.edge_moe_forward_traced.restype = i32
+    lib.edge_moe_forward_noalloc.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights), vp, vp]
+    lib.edge_moe_forward_noalloc.restype = i32
     lib.edge_moe_residual.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     lib.edge_moe_residual.restype = i32
     lib.edge_moe_copy.argtypes = [vp, vp, sz, vp]
@@ -207,6 +210,15 @@ def edge_moe_forward(dims, x, topk_idx, topk_w, weights, y, ws, stream=None, tra
         st = lib.edge_moe_forward_traced(*args, ctypes.byref(tr))
     if st != EDGE_MOE_OK:
         raise EdgeMoeError("edge_moe_forward", st)
+
+
+def edge_moe_forward_noalloc(dims, x, topk_idx, topk_w, weights, y, stream=None) -> None:
+    """edge_moe_forward with the library's own per-device scratch as workspace
+    (no allocation; calls that overlap on one GPU race)."""
+    st = load().edge_moe_forward_noalloc(ctypes.byref(cdims(dims)), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+                                         ctypes.byref(cweights(weights)), _ptr(y), _stream(stream))
+    if st != EDGE_MOE_OK:
+        raise EdgeMoeError("edge_moe_forward_noalloc", st)
 
 
 def edge_moe_residual(x, y, x_out, stream=None) -> None:

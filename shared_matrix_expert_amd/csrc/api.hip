@@ -211,6 +211,30 @@ void prof_drain(ProfState& p) {
     p.pending.clear();
 }
 
+// ------------------------------------------------------ allocation-free variant --
+// The workspace of edge_moe_forward_noalloc: one file-scope device array, which
+// each GPU holds its own copy of for the life of the process.  Host code only
+// uses the array through the device address hipGetSymbolAddress returns for
+// the current device (the array's own name on the host is not that address).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's scratch (looked up once per device),
+// or null if the lookup failed.
+void* scratch_ptr() {
+    static std::mutex mu;
+    static void* ptrs[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
 }  // namespace
 
 namespace em {
@@ -473,6 +497,18 @@ int edge_moe_forward_traced(const edge_moe_dims* dims, const uint16_t* x,
                             const edge_moe_weights* weights, float* y, void* ws,
                             size_t ws_bytes, void* stream, const edge_moe_trace* trace) {
     return forward_impl(dims, x, topk_idx, topk_w, weights, y, ws, ws_bytes, stream, trace);
+}
+
+int edge_moe_forward_noalloc(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                             const float* topk_w, const edge_moe_weights* weights, float* y, void* stream) {
+    const int st = check_dims(dims);
+    if (st != EDGE_MOE_OK) return st;
+    if (edge_moe_workspace_bytes(dims) > kScratchBytes) return EDGE_MOE_EWORKSPACE;
+    const int dst = check_device();
+    if (dst != EDGE_MOE_OK) return dst;
+    void* ws = scratch_ptr();
+    if (!ws) return EDGE_MOE_EHIP;
+    return forward_impl(dims, x, topk_idx, topk_w, weights, y, ws, kScratchBytes, stream, nullptr);
 }
 
 int edge_moe_residual(int32_t T, int32_t d, const uint16_t* x, const float* y, uint16_t* x_out,
