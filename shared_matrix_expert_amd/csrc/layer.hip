@@ -47,7 +47,7 @@ constexpr int PL_WAVES = 8;
 constexpr int PL_THREADS = 64 * PL_WAVES;
 constexpr int PL_T = 8;            // tokens (staged x rows)
 constexpr int PL_RMAX = 128;       // slots T * k
-constexpr int PL_Z1S = 4;          // K slices of A_up x
+constexpr int PL_Z1S = 2;          // K slices of A_up x
 constexpr int PL_ZLS = 4;          // K slices of U_up x
 constexpr int PL_Z2P = 8;          // parts of a group's R4 / R5 reduction
 constexpr int PL_ZP = 136;         // LDS row stride (elements) of z1 and activation rows
@@ -80,6 +80,7 @@ struct PlLds {
     int arow[32], dexp[32], dstart[32];
     int task;
     uint32_t wflag, aflag;
+    uint32_t zready;                       // this workgroup has seen every z1 / zl rounded
 };
 
 // ------------------------------------------------------------------ helpers -------
@@ -122,8 +123,12 @@ EM_DEV bool pl_arrive(PlLds& L, uint32_t* c, uint32_t expected) {
 EM_DEV bool pl_wait(PlLds& L, uint32_t* c, uint32_t target, uint32_t* err) {
     if (threadIdx.x == 0) {
         uint32_t ok = 1u, n = 0u;
+        // doubling pauses between polls (up to ~0.4 us): waiters do not crowd
+        // the counter that producers are adding to
+        int pause = 1;
         while (__hip_atomic_fetch_add(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(4);
+            for (int i = 0; i < pause; ++i) __builtin_amdgcn_s_sleep(1);
+            pause = min(2 * pause, 16);
             if (++n > PL_SPIN_MAX) {
                 ok = 0u;
                 __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -356,11 +361,40 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
         }
     };
 
+    // ---- z1 rows of the group's slots and zl rows of the tokens.  Once this
+    // workgroup has seen them all rounded (its earlier up tasks), the loads go
+    // out before the stream and land in LDS after it; otherwise they follow
+    // the wait after the stream.
+    const int tid = threadIdx.x;
+    uint4 zv[2], zlv;
+    auto z_issue = [&]() {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + PL_THREADS * u, row = min(i >> 4, nrg - 1);
+            zv[u] = ld16(a.pl_z1b + (size_t)V.rows[gr0 + row] * KC + 8 * (i & 15));
+        }
+        const int tok = min(tid >> 1, a.T - 1);
+        zlv = ld16(a.pl_zlb + ((size_t)tok * a.G + g) * 16 + 8 * (tid & 1));
+    };
+    auto z_store = [&]() {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + PL_THREADS * u, row = i >> 4;
+            if (row < nrg) *reinterpret_cast<uint4*>(&L.z1_l[row][8 * (i & 15)]) = zv[u];
+        }
+        for (int i = tid + 2 * PL_THREADS; i < nrg * 16; i += PL_THREADS)      // rows past 64
+            *reinterpret_cast<uint4*>(&L.z1_l[i >> 4][8 * (i & 15)]) =
+                ld16(a.pl_z1b + (size_t)V.rows[gr0 + (i >> 4)] * KC + 8 * (i & 15));
+        if (tid < 32) *reinterpret_cast<uint4*>(&L.zl_l[tid >> 1][8 * (tid & 1)]) = (tid >> 1) < a.T ? zlv : zero_u4();
+    };
+    const bool zr = L.zready != 0u;
+    if (zr) z_issue();
+
     // ---- S_up x (whole K) through a ring of four blocks.  Turns of four blocks
     // run in a loop that refills each slot right after its block (loads in the
     // same order in the prologue and the loop, so the waits count the loads
-    // behind them); the last turn refills nothing and instead issues the first
-    // eight experts' B_up rows and the V_up row.
+    // behind them); the last turn refills nothing and instead issues the
+    // first eight experts' B_up and A_dn rows and the V_up and U_dn rows.
     WsSrcT src;
     const size_t tgi = (size_t)g * ncb + cb;
     ws_src_t(src, a.s_up_t + tgi * 64 * a.d, a.s_up_s + tgi * a.d, a.d / KC, wv);
@@ -384,10 +418,11 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
         }
         scc = scn;
     }
-    PlRing ru0, ru1;
+    PlRing ru0, ru1, rd0, rd1;
     fetch_bup(ru0, x0);
     fetch_bup(ru1, x0 + 4);
     uint4 vup = ld16(a.lu_v + ((size_t)g * a.h + col) * a.rL + min(8 * c, a.rL - 8));
+    fetch_adn(rd0, x0);
 #pragma unroll
     for (int j = 0; j < WS_RING; ++j) {
         const uint32_t sp = j == 0 ? scc.x : (j == 1 ? scc.y : (j == 2 ? scc.z : scc.w));
@@ -395,19 +430,12 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
     }
     if (8 * c >= a.rL) vup = zero_u4();
 
-    // ---- z1 of the group's rows and zl of the tokens (the first tasks of the queue)
-    if (!pl_wait(L, &a.pl_ctr[PL_C_ZREADY], (uint32_t)(V.X + V.NG), &a.pl_ctr[PL_C_ERR])) return false;
-    for (int i = threadIdx.x; i < nrg * 16; i += PL_THREADS) {
-        const int row = i >> 4, sg = i & 15;
-        *reinterpret_cast<uint4*>(&L.z1_l[row][8 * sg]) = ld16(a.pl_z1b + (size_t)V.rows[gr0 + row] * KC + 8 * sg);
+    if (!zr) {
+        if (!pl_wait(L, &a.pl_ctr[PL_C_ZREADY], (uint32_t)(V.X + V.NG), &a.pl_ctr[PL_C_ERR])) return false;
+        if (tid == 0) L.zready = 1u;
+        z_issue();
     }
-    if (threadIdx.x < 32) {
-        const int tok = threadIdx.x >> 1, p = threadIdx.x & 1;
-        *reinterpret_cast<uint4*>(&L.zl_l[tok][8 * p]) =
-            tok < a.T ? ld16(a.pl_zlb + ((size_t)tok * a.G + g) * 16 + 8 * p) : zero_u4();
-    }
-    PlRing rd0, rd1;
-    fetch_adn(rd0, x0);
+    z_store();
     fetch_adn(rd1, x0 + 4);
     __syncthreads();
 
@@ -450,6 +478,12 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
     }
     __syncthreads();
 
+    // the U_dn rows of the block (R5), in flight while the R4 inputs are formed
+    uint4 ub[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        ub[st] = ld16(a.ld_u + ((size_t)g * a.rL + min(li, a.rL - 1)) * a.h + cb * 128 + 32 * st + 8 * c);
+
     // ---- the block's activation rows to the workspace (read by the down tasks)
     for (int i = threadIdx.x; i < nrg * 16; i += PL_THREADS) {
         const int row = i >> 4, sg = i & 15;
@@ -487,10 +521,6 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
     }
     // ---- R5 inputs over the block: U_dn rows (rL <= 16) against 16-row subtiles of the group's rows
     if (16 * wv < nrg) {
-        uint4 ub[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-            ub[st] = ld16(a.ld_u + ((size_t)g * a.rL + min(li, a.rL - 1)) * a.h + cb * 128 + 32 * st + 8 * c);
         for (int j = wv; 16 * j < nrg; j += PL_WAVES) {
             floatx4 t = zero4();
 #pragma unroll
@@ -666,6 +696,7 @@ dec_layer(DecodeArgs a) {
         const int r = i / SPR, sg = i % SPR;
         *reinterpret_cast<uint4*>(L.u.xs + (size_t)r * D + 8 * ((sg & ~15) | ((sg & 15) ^ (r & 15)))) = xv[u];
     }
+    if (threadIdx.x == 0) L.zready = 0u;
     __syncthreads();
     WsAct ar;
     ar.row[0] = L.u.xs + (size_t)min(li, PL_T - 1) * D;
