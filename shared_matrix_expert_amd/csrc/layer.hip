@@ -69,14 +69,14 @@ struct PlView {
 };
 
 struct PlLds {
-    union {
+    union alignas(16) {
         uint16_t xs[PL_T * 4096];          // staged x rows (d <= 4096)
         uint16_t pieces[2 * WS_PIECE];     // down tasks: two staged activation pieces
     } u;
-    uint16_t z1_l[PL_RMAX][PL_ZP];         // the group's z1 rows (up tasks)
-    uint16_t a_l[PL_RMAX][PL_ZP];          // the group's activation rows over 128 columns
+    alignas(16) uint16_t z1_l[PL_RMAX][PL_ZP];   // the group's z1 rows (up tasks)
+    alignas(16) uint16_t a_l[PL_RMAX][PL_ZP];    // the group's activation rows over 128 columns
     float red[PL_WAVES][256];              // per-wave 16 x 16 tiles
-    uint16_t zl_l[16][24];                 // zl rows of the tokens
+    alignas(16) uint16_t zl_l[16][24];     // zl rows of the tokens
     int arow[32], dexp[32], dstart[32];
     int task;
     uint32_t wflag, aflag;
@@ -321,44 +321,49 @@ EM_DEV void pl_zl(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
 }
 
 // ------------------------------------------------------------------ UP -------------
-// The delta pieces of four experts for this lane: 16 bytes of codes and a scale.
-struct PlRing {
-    uint4 w[4];
-    uint32_t s[4];
+// One expert's operands over a 128-column block, for this lane: its B_up rows
+// (column tiles t = 0..7: row 16 t + lane % 16, K elements [32 c, 32 c + 32)
+// of r = 128, c = lane / 16) and its A_dn rows (R4 tiles t: row 16 t + lane %
+// 16, the block's columns [32 c, 32 c + 32)), each 8 KB contiguous per wave,
+// with one scale per row.
+struct PlBlk {
+    uint4 bu[8], ad[8];
+    uint32_t bs[8], as[8];
 };
 
-// One (group, 128-column block): every wave streams one 16-row tile of S_up
-// (whole K, four blocks ahead) against the staged x rows; the last blocks
-// leave room for the first eight experts' B_up rows.  Then, per distinct
-// expert of the group, h = S_up x + V_up zl + B_up z1 (its rows only), SiLU
-// and R3 into the block's activation rows; then the R4 inputs A_dn a over the
-// block (wave w: A_dn rows 16w..16w+15 of each expert) and the R5 inputs
-// U_dn a, as partial sums per block.
+// One (group, 128-column block).  Every wave streams one 16-row tile of S_up
+// (whole K, four blocks ahead) against the staged x rows; the last turn of the
+// stream also issues each wave's first expert's B_up rows.  After V_up zl is
+// added, the group's distinct experts are dealt to the waves (wave w: experts
+// w, w + 8, ...), and a wave takes its expert through the whole block on its
+// own: h = S_up x + V_up zl + B_up z1 over the 128 columns for the expert's
+// rows, SiLU and R3 into the block's activation rows, then the R4 inputs
+// A_dn a over the block as partial sums, with no barrier between the two.  The
+// R5 inputs U_dn a of all the group's rows follow one barrier later.
 template <int NBD>
 EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& ar, int gi, int cb) {
     const int lane = lane_id(), wv = wave_id(), c = lane >> 4, li = lane & 15;
     const int g = V.gl[gi];
     const int ncb = a.h / 128;
-    const int col = cb * 128 + 16 * wv + li;              // this lane's h column
+    const int col = cb * 128 + 16 * wv + li;              // this lane's h column in the stream
     const int x0 = V.gx[g], x1 = V.gx[g + 1];
     const int gr0 = V.goff[g], nrg = V.goff[g + 1] - gr0;
 
-    auto fetch_bup = [&](PlRing& r, int u0) {
+    auto fetch_bu = [&](PlBlk& k, int xi) {
+        const int e = V.xe[min(xi, x1 - 1)];
+        const uint8_t* bu = a.b_up + ((size_t)e * a.h + cb * 128 + li) * (KC / 2) + 16 * c;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = V.xe[min(u0 + q, x1 - 1)];
-            r.w[q] = ld16(a.b_up + ((size_t)e * a.h + col) * (KC / 2) + 16 * c);
-            r.s[q] = a.b_up_s[(size_t)e * a.h + col];
-        }
+        for (int t = 0; t < 8; ++t) k.bu[t] = ld16(bu + t * 16 * (KC / 2));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) k.bs[t] = a.b_up_s[(size_t)e * a.h + cb * 128 + 16 * t + li];
     };
-    auto fetch_adn = [&](PlRing& r, int u0) {
+    auto fetch_ad = [&](PlBlk& k, int xi) {
+        const int e = V.xe[min(xi, x1 - 1)];
+        const uint8_t* ad = a.a_dn_t + ((size_t)e * ncb + cb) * (KC * KC / 2) + li * (KC / 2) + 16 * c;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = V.xe[min(u0 + q, x1 - 1)];
-            const int n2 = 16 * wv + li;
-            r.w[q] = ld16(a.a_dn_t + ((size_t)e * ncb + cb) * (KC * KC / 2) + n2 * (KC / 2) + 16 * c);
-            r.s[q] = a.a_dn_s[((size_t)e * KC + n2) * ncb + cb];
-        }
+        for (int t = 0; t < 8; ++t) k.ad[t] = ld16(ad + t * 16 * (KC / 2));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) k.as[t] = a.a_dn_s[((size_t)e * KC + 16 * t + li) * ncb + cb];
     };
 
     // ---- z1 rows of the group's slots and zl rows of the tokens.  Once this
@@ -394,7 +399,7 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
     // run in a loop that refills each slot right after its block (loads in the
     // same order in the prologue and the loop, so the waits count the loads
     // behind them); the last turn refills nothing and instead issues the
-    // first eight experts' B_up and A_dn rows and the V_up and U_dn rows.
+    // wave's first expert's B_up rows and the V_up row.
     WsSrcT src;
     const size_t tgi = (size_t)g * ncb + cb;
     ws_src_t(src, a.s_up_t + tgi * 64 * a.d, a.s_up_s + tgi * a.d, a.d / KC, wv);
@@ -418,11 +423,9 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
         }
         scc = scn;
     }
-    PlRing ru0, ru1, rd0, rd1;
-    fetch_bup(ru0, x0);
-    fetch_bup(ru1, x0 + 4);
+    PlBlk bk;
+    fetch_bu(bk, x0 + wv);
     uint4 vup = ld16(a.lu_v + ((size_t)g * a.h + col) * a.rL + min(8 * c, a.rL - 8));
-    fetch_adn(rd0, x0);
 #pragma unroll
     for (int j = 0; j < WS_RING; ++j) {
         const uint32_t sp = j == 0 ? scc.x : (j == 1 ? scc.y : (j == 2 ? scc.z : scc.w));
@@ -435,54 +438,70 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
         if (tid == 0) L.zready = 1u;
         z_issue();
     }
+    fetch_ad(bk, x0 + wv);
     z_store();
-    fetch_adn(rd1, x0 + 4);
     __syncthreads();
 
-    // ---- LoRA up: S_up x + V_up zl per token, kept per wave in LDS
+    // ---- LoRA up: S_up x + V_up zl per token and column, into LDS (red[t]:
+    // column tile t of the block, [token][16 columns])
     {
         const uint4 za = 8 * c < a.rL ? lds16(&L.zl_l[li][8 * c]) : zero_u4();
         acc[0] = mfma_bf16(za, vup, acc[0]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) L.red[wv][(4 * c + q) * 16 + li] = acc[0][q];
     }
-
-    // ---- per expert: h = that + B_up z1, a = R3(SiLU(h)) for the expert's rows
-    auto consume_up = [&](const PlRing& r, int u0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int xi = u0 + q;
-            if (xi >= x1) break;
-            const int r0 = V.xoff[xi] - gr0, nr = V.xoff[xi + 1] - V.xoff[xi];
-            uint4 af[1][4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) af[0][s] = li < nr ? lds16(&L.z1_l[r0 + li][32 * c + 8 * s]) : zero_u4();
-            floatx4 t[1] = {zero4()};
-            mac_fast<1>(t, af, r.w[q], r.s[q]);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int row = 4 * c + qq;
-                if (row < nr) {
-                    const int tok = V.rtok[gr0 + r0 + row];
-                    const float hv = t[0][qq] + L.red[wv][tok * 16 + li];
-                    L.a_l[r0 + row][16 * wv + li] = (uint16_t)f32_to_bf16_rne(silu(hv));
-                }
-            }
-        }
-    };
-    for (int u0 = x0; u0 < x1; u0 += 8) {
-        consume_up(ru0, u0);
-        fetch_bup(ru0, u0 + 8);
-        consume_up(ru1, u0 + 4);
-        fetch_bup(ru1, u0 + 12);
-    }
-    __syncthreads();
-
-    // the U_dn rows of the block (R5), in flight while the R4 inputs are formed
+    // the U_dn rows of the block (R5), in flight during the experts
     uint4 ub[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
         ub[st] = ld16(a.ld_u + ((size_t)g * a.rL + min(li, a.rL - 1)) * a.h + cb * 128 + 32 * st + 8 * c);
+    __syncthreads();
+
+    // ---- this wave's experts, each through the whole block
+    float* z2p = a.pl_z2p + (size_t)cb * a.R * PL_Z2W;
+    for (int xi = x0 + wv; xi < x1; xi += PL_WAVES) {
+        const int r0 = V.xoff[xi] - gr0, nr = V.xoff[xi + 1] - V.xoff[xi];
+        int tokq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tokq[q] = V.rtok[gr0 + r0 + min(4 * c + q, nr - 1)];
+        {
+            uint4 af[1][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[0][s] = li < nr ? lds16(&L.z1_l[r0 + li][32 * c + 8 * s]) : zero_u4();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                floatx4 h[1] = {zero4()};
+                mac_fast<1>(h, af, bk.bu[t], bk.bs[t]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = 4 * c + q;
+                    if (row < nr)
+                        L.a_l[r0 + row][16 * t + li] =
+                            (uint16_t)f32_to_bf16_rne(silu(h[0][q] + L.red[t][tokq[q] * 16 + li]));
+                }
+            }
+        }
+        {
+            uint4 af[1][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[0][s] = li < nr ? lds16(&L.a_l[r0 + li][32 * c + 8 * s]) : zero_u4();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                floatx4 z[1] = {zero4()};
+                mac_fast<1>(z, af, bk.ad[t], bk.as[t]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = 4 * c + q;
+                    if (row < nr) st_agent(&z2p[(size_t)(gr0 + r0 + row) * PL_Z2W + 16 * t + li], z[0][q]);
+                }
+            }
+        }
+        if (xi + PL_WAVES < x1) {
+            fetch_bu(bk, xi + PL_WAVES);
+            fetch_ad(bk, xi + PL_WAVES);
+        }
+    }
+    __syncthreads();
 
     // ---- the block's activation rows to the workspace (read by the down tasks)
     for (int i = threadIdx.x; i < nrg * 16; i += PL_THREADS) {
@@ -492,47 +511,18 @@ EM_DEV bool pl_up(const DecodeArgs& a, const PlView& V, PlLds& L, const WsAct& a
         st_agent_u64(dst, (uint64_t)v.x | ((uint64_t)v.y << 32));
         st_agent_u64(dst + 4, (uint64_t)v.z | ((uint64_t)v.w << 32));
     }
-
-    // ---- R4 inputs over the block: wave w takes A_dn rows 16w..16w+15 of every expert
-    float* z2p = a.pl_z2p + (size_t)cb * a.R * PL_Z2W;
-    auto consume_dn = [&](const PlRing& r, int u0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int xi = u0 + q;
-            if (xi >= x1) break;
-            const int r0 = V.xoff[xi] - gr0, nr = V.xoff[xi + 1] - V.xoff[xi];
-            uint4 af[1][4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) af[0][s] = li < nr ? lds16(&L.a_l[r0 + li][32 * c + 8 * s]) : zero_u4();
-            floatx4 t[1] = {zero4()};
-            mac_fast<1>(t, af, r.w[q], r.s[q]);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int row = 4 * c + qq;
-                if (row < nr) st_agent(&z2p[(size_t)(gr0 + r0 + row) * PL_Z2W + 16 * wv + li], t[0][qq]);
-            }
-        }
-    };
-    for (int u0 = x0; u0 < x1; u0 += 8) {
-        consume_dn(rd0, u0);
-        fetch_adn(rd0, u0 + 8);
-        consume_dn(rd1, u0 + 4);
-        fetch_adn(rd1, u0 + 12);
-    }
     // ---- R5 inputs over the block: U_dn rows (rL <= 16) against 16-row subtiles of the group's rows
-    if (16 * wv < nrg) {
-        for (int j = wv; 16 * j < nrg; j += PL_WAVES) {
-            floatx4 t = zero4();
+    for (int j = wv; 16 * j < nrg; j += PL_WAVES) {
+        floatx4 t = zero4();
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const uint4 av = 16 * j + li < nrg ? lds16(&L.a_l[16 * j + li][32 * st + 8 * c]) : zero_u4();
-                t = mfma_bf16(av, ub[st], t);
-            }
+        for (int st = 0; st < 4; ++st) {
+            const uint4 av = 16 * j + li < nrg ? lds16(&L.a_l[16 * j + li][32 * st + 8 * c]) : zero_u4();
+            t = mfma_bf16(av, ub[st], t);
+        }
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int row = 16 * j + 4 * c + qq;
-                if (row < nrg && li < a.rL) st_agent(&z2p[(size_t)(gr0 + row) * PL_Z2W + KC + li], t[qq]);
-            }
+        for (int qq = 0; qq < 4; ++qq) {
+            const int row = 16 * j + 4 * c + qq;
+            if (row < nrg && li < a.rL) st_agent(&z2p[(size_t)(gr0 + row) * PL_Z2W + KC + li], t[qq]);
         }
     }
     pl_publish(&a.pl_ctr[PL_C_UP + g]);
