@@ -196,14 +196,19 @@ class Workload:
         else:
             W = {k: v.cuda() for k, v in synth.make_weights(cfg_id, seed, layer, device="cpu").items()}
         if D.T <= 16 and D.quant_group == 128 and D.d % 1024 == 0 and D.h % 1024 == 0:
-            W = em.tile_weights(D, W)
+            W = em.tile_weights(D, W)          # kinds 0-3: the decode kernels and the persistent launch
         return W
+
+    persistent = False   # the layer through edge_moe_forward_persistent (one persistent launch)
 
     def step(self, i):
         L = self.layers[i % len(self.layers)]
         em, D = self.em, self.D
         em.edge_moe_route(D, self.x, L["wr"], L["bias"], self.idx, self.w, None, self.ws, self.stream)
-        em.edge_moe_forward(D, self.x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
+        if self.persistent:
+            em.edge_moe_forward_persistent(D, self.x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
+        else:
+            em.edge_moe_forward(D, self.x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
 
     def routed_indices(self):
         """Expert indices of every layer instance (from one step each)."""
@@ -423,6 +428,25 @@ def cpu_baseline_prefill(wl: Workload, n_tokens: int = 16):
 
 # ---------------------------------------------------------------- main ---------------
 
+def persistent_line(wl, steps, warmup, tag):
+    """The same workload through the persistent launch: tokens/s, per-kernel
+    event times, and the layer kernel's HBM roofline."""
+    wl.persistent = True
+    idxs = wl.routed_indices()
+    sec = wl.time_steps(steps, warmup)
+    kt = wl.kernel_times(max(20, steps // 4))
+    name, roof = roofline_hbm(wl.D, idxs, kt)
+    roof["traffic"] = stored_traffic(name, tag)
+    sb = float(np.mean([step_bytes(wl.D, ix) for ix in idxs]))
+    wl.persistent = False
+    log(f"  persistent launch ({tag}): {sec * 1e6:.1f} us per step")
+    return {"value": round(wl.D.T / sec, 1), "unit": "tokens/s", "steps": steps, "ms_per_step": round(sec * 1e3, 5),
+            "what": "route, then the layer as one persistent launch (edge_moe_forward_persistent)",
+            "roofline": roof, "kernels": kernel_table(wl.D, idxs, kt),
+            "step_hbm": {"bytes_per_step": int(sb), "achieved_GBs": round(sb / sec / 1e9, 1),
+                         "frac": round(sb / sec / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -494,6 +518,7 @@ def main():
         "step_hbm": {"bytes_per_step": int(sb), "achieved_GBs": round(sb / sec / 1e9, 1),
                      "frac": round(sb / sec / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    line["persistent"] = persistent_line(wl, args.steps, args.warmup, "verify_t8")
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         line["cpu_baseline"] = cpu_baseline(wl)
@@ -518,6 +543,7 @@ def main():
                          "frac": round(dsb / dsec / 1e9 / HBM_PEAK_GBS, 4)},
         }
         log(f"  decode: {dsec * 1e6:.1f} us per step")
+        line["decode_t1"]["persistent"] = persistent_line(wd, args.steps, args.warmup, "decode_t1")
         del wd
         torch.cuda.empty_cache()
 

@@ -98,9 +98,8 @@ typedef struct edge_moe_dims {
  * are set, batches of at most 16 tokens stream them instead of the row-major
  * codes (the row-major copies stay required: larger batches and the other
  * paths read them); both copies must hold the same values.  With all four
- * set, batches of at most 8 tokens (at most 128 token-slot pairs, d = 2048 or
- * 4096, r = 128, rL = 8 or 16, quant groups of 128) run as one persistent
- * launch after a small counter-clearing one. */
+ * set, edge_moe_forward_persistent can run the layer as one persistent launch
+ * (see there). */
 typedef struct edge_moe_weights {
     const uint8_t*  s_up_q;  const uint16_t* s_up_scale;
     const uint8_t*  s_dn_q;  const uint16_t* s_dn_scale;
@@ -169,6 +168,24 @@ int edge_moe_route(const edge_moe_dims* dims, const uint16_t* x, const uint16_t*
 int edge_moe_forward(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                      const float* topk_w, const edge_moe_weights* weights, float* y,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* The expert layer of a decode or verify batch as one persistent launch
+ * (after a small one that clears its counters): one workgroup per compute
+ * unit takes tasks from a queue in the workspace - the R1 / R2 inputs, the
+ * shared up with the fused delta up, activation and R4 / R5 partial sums per
+ * 128 columns, the R4 / R5 reductions, and the shared, LoRA and delta down per
+ * 128 output columns, the last of which forms y.  The launch ramps between the
+ * layer's phases are gone and phases overlap across groups (the pages: the
+ * layer runs 48 deep and generation is bound by weight reads - byteiota, Not
+ * Compression - Architecture; launch post, Under the Hood, Scheduling).
+ * Same arguments, results and tolerances as edge_moe_forward (trace: as
+ * edge_moe_forward_traced, NULL for none); requires T <= 8, T * top_k <= 128,
+ * d = 4096, h a multiple of 1024 up to 16384, r = 128, rL = 8 or 16, quant
+ * groups of 128, experts_per_group <= 64, and all four stored copies in
+ * `weights` (edge_moe_tile_shared kinds 0-3); EDGE_MOE_EUNSUPPORTED otherwise. */
+int edge_moe_forward_persistent(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                                const float* topk_w, const edge_moe_weights* weights, float* y, void* ws,
+                                size_t ws_bytes, void* stream, const edge_moe_trace* trace);
 
 /* edge_moe_forward that also copies per-stage intermediates into `trace`
  * (host struct of device pointers, NULL = none). */

@@ -29,7 +29,7 @@ EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_forward_traced", "edge_moe_residual", "edge_moe_status_string",
             "edge_moe_abi_version", "edge_moe_copy", "edge_moe_tile_shared",
             "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset",
-            "edge_moe_forward_noalloc")
+            "edge_moe_forward_noalloc", "edge_moe_forward_persistent")
 
 
 class CDims(ctypes.Structure):
@@ -93,6 +93,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(CWeights), vp, vp, sz, vp,
                                             ctypes.POINTER(CTrace)]
     lib.edge_moe_forward_traced.restype = i32
+    lib.edge_moe_forward_persistent.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights),
+                                                vp, vp, sz, vp, ctypes.POINTER(CTrace)]
+    lib.edge_moe_forward_persistent.restype = i32
     lib.edge_moe_forward_noalloc.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights), vp, vp]
     lib.edge_moe_forward_noalloc.restype = i32
     lib.edge_moe_residual.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
@@ -210,6 +213,17 @@ def edge_moe_forward(dims, x, topk_idx, topk_w, weights, y, ws, stream=None, tra
         st = lib.edge_moe_forward_traced(*args, ctypes.byref(tr))
     if st != EDGE_MOE_OK:
         raise EdgeMoeError("edge_moe_forward", st)
+
+
+def edge_moe_forward_persistent(dims, x, topk_idx, topk_w, weights, y, ws, stream=None, trace=None) -> None:
+    """The decode / verify layer as one persistent launch (T <= 8, stored copies
+    of kinds 0-3 in `weights`); trace as edge_moe_forward's."""
+    tr = None if trace is None else CTrace(*(_ptr(trace.get(n)) for n, _ in CTrace._fields_))
+    st = load().edge_moe_forward_persistent(ctypes.byref(cdims(dims)), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+                                            ctypes.byref(cweights(weights)), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream), None if tr is None else ctypes.byref(tr))
+    if st != EDGE_MOE_OK:
+        raise EdgeMoeError("edge_moe_forward_persistent", st)
 
 
 def edge_moe_forward_noalloc(dims, x, topk_idx, topk_w, weights, y, stream=None) -> None:

@@ -338,7 +338,7 @@ static hipError_t copy_perm_trace(const edge_moe_trace* trace, const em::Dispatc
 
 static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint16_t* x,
                           const int32_t* topk_idx, const float* topk_w, const edge_moe_weights* wt,
-                          float* y, void* ws, void* stream, const edge_moe_trace* trace) {
+                          float* y, void* ws, void* stream, const edge_moe_trace* trace, bool persistent) {
     char* base = reinterpret_cast<char*>(ws);
     em::DecodeArgs a{};
     a.T = d.T; a.d = d.d; a.h = d.h; a.E = d.n_experts; a.P = d.experts_per_group;
@@ -377,7 +377,7 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
     }
     a.pl_trace_o = trace && trace->expert_out ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t err = (L.pl && em::dec_layer_ok(a)) ? em::launch_dec_layer(a, s) : em::launch_decode(a, s);
+    hipError_t err = persistent ? em::launch_dec_layer(a, s) : em::launch_decode(a, s);
     if (err != hipSuccess) return EDGE_MOE_EHIP;
     if (trace) {
         // intermediates are stored per slot here; the permutation arrays come
@@ -400,7 +400,7 @@ static int forward_decode(const edge_moe_dims& d, const DecLayout& L, const uint
 
 static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                         const float* topk_w, const edge_moe_weights* wt, float* y, void* ws,
-                        size_t ws_bytes, void* stream, const edge_moe_trace* trace) {
+                        size_t ws_bytes, void* stream, const edge_moe_trace* trace, bool persistent = false) {
     int st = check_dims(dims);
     if (st != EDGE_MOE_OK) return st;
     if (!wt) return EDGE_MOE_EINVAL;
@@ -437,7 +437,17 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     if (st != EDGE_MOE_OK) return st;
 
     const edge_moe_dims& d = *dims;
-    if (dec) return forward_decode(d, DL, x, topk_idx, topk_w, wt, y, ws, stream, trace);
+    if (persistent) {
+        // the persistent launch takes decode batches whose shapes it supports
+        if (!dec || !DL.pl) return EDGE_MOE_EUNSUPPORTED;
+        em::DecodeArgs probe{};
+        probe.T = d.T; probe.d = d.d; probe.h = d.h; probe.E = d.n_experts; probe.P = d.experts_per_group;
+        probe.G = d.n_experts / d.experts_per_group; probe.R = d.T * d.top_k; probe.r = d.delta_rank;
+        probe.rL = d.lora_rank; probe.gq = d.quant_group;
+        probe.s_up_t = wt->s_up_t; probe.s_dn_t = wt->s_dn_t; probe.a_up_t = wt->a_up_t; probe.a_dn_t = wt->a_dn_t;
+        if (!em::dec_layer_ok(probe)) return EDGE_MOE_EUNSUPPORTED;
+    }
+    if (dec) return forward_decode(d, DL, x, topk_idx, topk_w, wt, y, ws, stream, trace, persistent);
     char* base = reinterpret_cast<char*>(ws);
     em::LayerArgs a{};
     a.T = d.T; a.d = d.d; a.h = d.h; a.E = d.n_experts; a.P = d.experts_per_group;
@@ -490,6 +500,12 @@ int edge_moe_forward(const edge_moe_dims* dims, const uint16_t* x, const int32_t
                      const float* topk_w, const edge_moe_weights* weights, float* y, void* ws,
                      size_t ws_bytes, void* stream) {
     return forward_impl(dims, x, topk_idx, topk_w, weights, y, ws, ws_bytes, stream, nullptr);
+}
+
+int edge_moe_forward_persistent(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                                const float* topk_w, const edge_moe_weights* weights, float* y, void* ws,
+                                size_t ws_bytes, void* stream, const edge_moe_trace* trace) {
+    return forward_impl(dims, x, topk_idx, topk_w, weights, y, ws, ws_bytes, stream, trace, true);
 }
 
 int edge_moe_forward_traced(const edge_moe_dims* dims, const uint16_t* x,

@@ -66,6 +66,7 @@ struct PlView {
     int16_t gl[64];                // groups with rows, most rows first
     int32_t dnpre[65];             // first down task of each listed group
     int X, NG, total, n_z1, n_zl, n_up, n_z2, dn_arrivals;
+    int nkh;                       // K parts of a down task (2 when full-K tasks would not fill the GPU)
 };
 
 struct PlLds {
@@ -209,11 +210,18 @@ EM_DEV void pl_view(const DecodeArgs& a, PlView& V) {
         int ng = 0;
         for (int g = 0; g < a.G; ++g) ng += V.goff[g + 1] > V.goff[g];
         const int nnb = a.d / 128;
+        int np = 0;
+        for (int i = 0; i < ng; ++i) {
+            const int g = V.gl[i];
+            np += (V.goff[g + 1] - V.goff[g] + 31) / 32;
+        }
+        const int nkh = np * nnb < (int)gridDim.x ? 2 : 1;
+        V.nkh = nkh;
         int n = 0;
         for (int i = 0; i < ng; ++i) {
             V.dnpre[i] = n;
             const int g = V.gl[i];
-            n += (V.goff[g + 1] - V.goff[g] + 31) / 32 * nnb * 2;
+            n += (V.goff[g + 1] - V.goff[g] + 31) / 32 * nnb * nkh;
         }
         V.dnpre[ng] = n;
         V.NG = ng;
@@ -564,8 +572,9 @@ EM_DEV bool pl_z2red(const DecodeArgs& a, const PlView& V, PlLds& L, int gi, int
 }
 
 // ------------------------------------------------------------------ DOWN -----------
-// y = sum_j w_j (o_j + od_j) in slot order over one 128-column block.
-EM_DEV void pl_combine(const DecodeArgs& a, int nb) {
+// y = sum_j w_j (o_j + od_j) in slot order over one 128-column block (od only
+// when the down tasks were split over two K halves).
+EM_DEV void pl_combine(const DecodeArgs& a, int nb, int nkh) {
     constexpr int KJ = 16;
     const int n = a.T * 128;
     for (int i = threadIdx.x; i < n; i += PL_THREADS) {
@@ -578,7 +587,7 @@ EM_DEV void pl_combine(const DecodeArgs& a, int nb) {
                 const size_t slot = (size_t)t * a.k + min(j0 + u, a.k - 1);
                 wv[u] = a.topk_w[slot];
                 ov[u] = ld_agent(&a.o[slot * a.d + col]);
-                dv[u] = ld_agent(&a.od[slot * a.d + col]);
+                dv[u] = nkh == 2 ? ld_agent(&a.od[slot * a.d + col]) : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < KJ; ++u) {
@@ -592,10 +601,10 @@ EM_DEV void pl_combine(const DecodeArgs& a, int nb) {
     }
 }
 
-// One (group, pass of <= 32 rows, 128 output columns, half of h): S_dn a over
-// the half with the rows staged through LDS in pieces, then (first half) the
-// LoRA down, and half of the pass's experts' delta down; the per-slot result
-// goes to o (first half) or od (second half).
+// One (group, pass of <= 32 rows, 128 output columns, K part kh of nkh): S_dn
+// a over the part of h with the rows staged through LDS in pieces, then (first
+// part) the LoRA down, and the part's share of the pass's experts' delta down;
+// the per-slot result goes to o (first part) or od (second part).
 template <int RP>
 EM_DEV bool pl_down(const DecodeArgs& a, const PlView& V, PlLds& L, int gi, int pass, int nb, int kh) {
     constexpr int NS = WsPiece<RP, PL_THREADS>::NS;
@@ -604,7 +613,8 @@ EM_DEV bool pl_down(const DecodeArgs& a, const PlView& V, PlLds& L, int gi, int 
     const int m0 = V.goff[g] + 32 * pass;
     const int prow = min(32, V.goff[g + 1] - m0);
     const int ncol = nb * 128 + 16 * wv + li;
-    const int hh = a.h / 2;
+    const int nkh = V.nkh;
+    const int hh = a.h / nkh;
     if (!pl_wait(L, &a.pl_ctr[PL_C_UP + g], (uint32_t)(a.h / 128), &a.pl_ctr[PL_C_ERR])) return false;
     // the pass's rows and their distinct experts (rows are sorted by expert)
     if ((int)threadIdx.x < RP) L.arow[threadIdx.x] = V.rows[m0 + min((int)threadIdx.x, prow - 1)];
@@ -646,8 +656,8 @@ EM_DEV bool pl_down(const DecodeArgs& a, const PlView& V, PlLds& L, int gi, int 
         }
     }
     const int nexp = __popcll(starts);
-    delta_down_pass<NS>(acc, a, L.dexp, L.dstart, starts, prow, slot_i, ncol, kh ? nexp / 2 : 0,
-                        kh ? nexp : nexp / 2);
+    delta_down_pass<NS>(acc, a, L.dexp, L.dstart, starts, prow, slot_i, ncol, kh * nexp / nkh,
+                        (kh + 1) * nexp / nkh);
     float* out = kh ? a.od : a.o;
 #pragma unroll
     for (int ms = 0; ms < NS; ++ms)
@@ -656,7 +666,7 @@ EM_DEV bool pl_down(const DecodeArgs& a, const PlView& V, PlLds& L, int gi, int 
             const int i = ms * 16 + 4 * c + qq;
             if (i < prow) st_agent(&out[(size_t)V.rows[m0 + i] * a.d + ncol], acc[ms][qq]);
         }
-    if (pl_arrive(L, &a.pl_ctr[PL_C_DN + nb], (uint32_t)V.dn_arrivals)) pl_combine(a, nb);
+    if (pl_arrive(L, &a.pl_ctr[PL_C_DN + nb], (uint32_t)V.dn_arrivals)) pl_combine(a, nb, nkh);
     return true;
 }
 
@@ -729,7 +739,8 @@ dec_layer(DecodeArgs a) {
         int gi = 0;
         while (V.dnpre[gi + 1] <= j) ++gi;
         j -= V.dnpre[gi];
-        const int pass = j / (2 * nnb), nb = (j / 2) % nnb, kh = j % 2;
+        const int nkh = V.nkh;
+        const int pass = j / (nkh * nnb), nb = (j / nkh) % nnb, kh = j % nkh;
         const int g = V.gl[gi];
         const int prow = min(32, V.goff[g + 1] - V.goff[g] - 32 * pass);
         // two staging shapes (8 or 32 rows) keep the kernel within its registers

@@ -33,8 +33,9 @@ class Layer:
     shared matrices also get their decode-tiled copies where the shape allows
     (as in the benchmark); tiled=False keeps the row-major ones only."""
 
-    def __init__(self, D, weights: dict, tiled=None):
+    def __init__(self, D, weights: dict, tiled=None, persistent=False):
         self.D = D
+        self.persistent = persistent
         if tiled is None:
             tiled = bool(weights) and tile_ok(D)
         self.W = em.tile_weights(D, weights) if tiled else weights
@@ -59,7 +60,10 @@ class Layer:
                   "row_slot": torch.empty(R, dtype=torch.int32, device=DEV),
                   "act": torch.empty(R, D.h, dtype=torch.int16, device=DEV),
                   "expert_out": torch.empty(R, D.d, dtype=torch.float32, device=DEV)}
-        em.edge_moe_forward(D, x, idx, w, self.W, y, self.ws, trace=tr)
+        if self.persistent:
+            em.edge_moe_forward_persistent(D, x, idx, w, self.W, y, self.ws, trace=tr)
+        else:
+            em.edge_moe_forward(D, x, idx, w, self.W, y, self.ws, trace=tr)
         return y, tr
 
 

@@ -43,8 +43,8 @@ def _check_route(D, x, wr, bias, lay, sample=None):
     return idx, w, ref
 
 
-def _run_parity(D, x, wr, bias, Wdev, sample=None, keep=False, tiled=None):
-    lay = Layer(D, Wdev, tiled=tiled)
+def _run_parity(D, x, wr, bias, Wdev, sample=None, keep=False, tiled=None, persistent=False):
+    lay = Layer(D, Wdev, tiled=tiled, persistent=persistent)
     idx, w, ref = _check_route(D, x, wr, bias, lay, sample)
     y, tr = lay.forward(bits_to_dev(x), idx, w, trace=keep)
     torch.cuda.synchronize()
@@ -122,6 +122,48 @@ def test_verify_skewed_layer(seed):
     # determinism
     y2, _ = lay.forward(bits_to_dev(x), idx, w)
     assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("cfg,seed", [(1, 0), (1, 2), (2, 0), (2, 2)])
+def test_persistent_layer(cfg, seed):
+    """The single persistent launch (edge_moe_forward_persistent) on the decode
+    and verify batches, traced: permutation, activations and expert outputs
+    per slot, y, and bitwise equal repeats."""
+    say(f"case: persistent layer cfg={cfg} seed={seed}")
+    D = synth.config(cfg).dims
+    x, wr, bias = _inputs(cfg, seed)
+    lay, idx, w, y, tr, fw = _run_parity(D, x, wr, bias, synth.make_weights(cfg, seed, device="cuda"),
+                                         keep=True, persistent=True)
+    _check_trace(D, idx, tr, fw)
+    y2, _ = lay.forward(bits_to_dev(x), idx, w)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("T", [2, 5])
+def test_persistent_ragged(T):
+    say(f"case: persistent layer, ragged T={T}")
+    D = synth.config(1).dims.with_T(T)
+    x = synth.make_activations(1, 6, T=T)
+    wr, _ = synth.make_router(1, 6)
+    _run_parity(D, x, wr, None, synth.make_weights(1, 6, device="cuda"), persistent=True)
+
+
+def test_persistent_unsupported_shapes():
+    """Shapes outside the persistent launch's limits are refused before anything runs."""
+    D = synth.config(2).dims.with_T(12)                       # more than 8 tokens
+    lay = Layer(D, synth.make_weights(2, 0, device="cuda"), persistent=True)
+    x = bits_to_dev(synth.make_activations(2, 0, T=12))
+    idx = torch.zeros(D.T, D.top_k, dtype=torch.int32, device=DEV)
+    w = torch.zeros(D.T, D.top_k, dtype=torch.float32, device=DEV)
+    with pytest.raises(em.EdgeMoeError) as ei:
+        lay.forward(x, idx, w)
+    assert ei.value.status == em.EDGE_MOE_EUNSUPPORTED
+    D8 = synth.config(2).dims
+    lay = Layer(D8, synth.make_weights(2, 0, device="cuda"), tiled=False, persistent=True)
+    x = bits_to_dev(synth.make_activations(2, 0))
+    with pytest.raises(em.EdgeMoeError) as ei:                 # no stored copies
+        lay.forward(x, idx[:8], w[:8])
+    assert ei.value.status == em.EDGE_MOE_EUNSUPPORTED
 
 
 def test_verify_row_major_weights():
@@ -305,6 +347,14 @@ def test_verify_delta_handoff():
     _check_trace(D, idx_d, tr, fw)
     y2, _ = lay.forward(bits_to_dev(x), idx_d, w_d)
     assert torch.equal(y, y2)
+    # the same batch through the persistent launch (32-row passes of the down tasks)
+    lay.persistent = True
+    y3, tr3 = lay.forward(bits_to_dev(x), idx_d, w_d, trace=True)
+    torch.cuda.synchronize()
+    ok, ratio = y_within_tolerance(y3.cpu().numpy(), fw["y"])
+    say(f"  persistent: worst |dy| / bound = {ratio:.3g}")
+    assert ok, f"persistent y outside tolerance (worst ratio {ratio:.3g})"
+    _check_trace(D, idx_d, tr3, fw)
 
 
 def test_graph_replay_two_layers():
