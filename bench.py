@@ -265,7 +265,7 @@ def stored_traffic(kernel: str, workload_tag: str):
     if not os.path.exists(path):
         return None
     t = read_traffic(path)
-    if t.get("sources_sha256") != sources_digest():
+    if t.get("sources_sha256") != sources_digest(kernel):
         return None
     return int(float(t["traffic_bytes_per_dispatch"]))
 
@@ -447,6 +447,43 @@ def persistent_line(wl, steps, warmup, tag):
                          "frac": round(sb / sec / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
+def calibrate(em, torch):
+    """Measured peaks on this GPU, beside the published ones: a plain device
+    copy of 1 GiB (read + write bytes over time) and the matrix-core
+    calibration launch (the faster of two and four workgroups of four waves
+    per compute unit)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        em.edge_moe_copy(b, a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        em.edge_moe_copy(b, a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters, best = 20000, (0.0, "")
+    for per_cu in (2, 4):                      # two and four waves per SIMD
+        blocks = per_cu * cus
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        em.edge_moe_mfma_peak(out, blocks, 100)
+        e0.record()
+        em.edge_moe_mfma_peak(out, blocks, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        rate = blocks * 4 * iters * 8 * 16384 / (e0.elapsed_time(e1) / 1e3) / 1e12
+        if rate > best[0]:
+            best = (rate, f"{blocks} x 256 threads, {iters} rounds")
+    return {"copy_GBs": round(2 * n / copy_s / 1e9, 1), "copy_bytes": n,
+            "mfma_bf16_TFLOPs": round(best[0], 1), "mfma_launch": best[1],
+            "published": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,6 +495,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--stack-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="skip the verify T=8 workload (profiling runs)")
+    ap.add_argument("--no-calibrate", action="store_true")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (counter calibration)")
@@ -483,47 +522,49 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {n} bytes done")
 
-    # ---- verify T=8, skewed routing, rotating layer instances
-    log("building verify workload ...")
-    wl = Workload(2, args.layers, host_init=args.host_init)
-    D = wl.D
-    idxs = wl.routed_indices()
-    sec = wl.time_steps(args.steps, args.warmup)
-    ktimes = wl.kernel_times(max(20, args.steps // 4))
-    for k, (n, ms) in sorted(ktimes.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
-        log(f"  verify kernel {k:22s} launches {n:5d} avg {ms * 1e3:8.2f} us")
-    kname, roof = roofline_hbm(D, idxs, ktimes)
-    roof["traffic"] = stored_traffic(kname, "verify_t8")
-    sb = float(np.mean([step_bytes(D, ix) for ix in idxs]))
-    line = {
-        "metric": METRIC,
-        "value": round(D.T / sec, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(sec * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "speculative-verify batch T=8, skewed routing (48 of 80 top-10 picks "
-                               "in 2 of 8 groups), one layer: d=4096 h=8192 E=512 (8 groups of 64) "
-                               "top-10, int4 shared/delta (Gq=128, fp16 scales), r=128, bf16 LoRA "
-                               "rL=16; steps rotate over %d layer instances" % args.layers,
-                   "T": D.T, "layers_rotated": args.layers},
-        "roofline": roof,
-        "kernels": kernel_table(D, idxs, ktimes),
-        "step_hbm": {"bytes_per_step": int(sb), "achieved_GBs": round(sb / sec / 1e9, 1),
-                     "frac": round(sb / sec / 1e9 / HBM_PEAK_GBS, 4)},
-    }
-    line["persistent"] = persistent_line(wl, args.steps, args.warmup, "verify_t8")
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host ...")
-        line["cpu_baseline"] = cpu_baseline(wl)
-    del wl
-    torch.cuda.empty_cache()
+    line = {"metric": METRIC, "note": "verify workload skipped (--no-verify)"}
+    if not args.no_verify:
+        # ---- verify T=8, skewed routing, rotating layer instances
+        log("building verify workload ...")
+        wl = Workload(2, args.layers, host_init=args.host_init)
+        D = wl.D
+        idxs = wl.routed_indices()
+        sec = wl.time_steps(args.steps, args.warmup)
+        ktimes = wl.kernel_times(max(20, args.steps // 4))
+        for k, (n, ms) in sorted(ktimes.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+            log(f"  verify kernel {k:22s} launches {n:5d} avg {ms * 1e3:8.2f} us")
+        kname, roof = roofline_hbm(D, idxs, ktimes)
+        roof["traffic"] = stored_traffic(kname, "verify_t8")
+        sb = float(np.mean([step_bytes(D, ix) for ix in idxs]))
+        line = {
+            "metric": METRIC,
+            "value": round(D.T / sec, 1),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(sec * 1e3, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "speculative-verify batch T=8, skewed routing (48 of 80 top-10 picks "
+                                   "in 2 of 8 groups), one layer: d=4096 h=8192 E=512 (8 groups of 64) "
+                                   "top-10, int4 shared/delta (Gq=128, fp16 scales), r=128, bf16 LoRA "
+                                   "rL=16; steps rotate over %d layer instances" % args.layers,
+                       "T": D.T, "layers_rotated": args.layers},
+            "roofline": roof,
+            "kernels": kernel_table(D, idxs, ktimes),
+            "step_hbm": {"bytes_per_step": int(sb), "achieved_GBs": round(sb / sec / 1e9, 1),
+                         "frac": round(sb / sec / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        line["persistent"] = persistent_line(wl, args.steps, args.warmup, "verify_t8")
+        if not args.no_cpu_baseline:
+            log("timing the oracle on the host ...")
+            line["cpu_baseline"] = cpu_baseline(wl)
+        del wl
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         log("building decode workload (T=1) ...")
@@ -591,6 +632,9 @@ def main():
         }
         if not args.no_cpu_baseline:
             line["prefill_16k"]["cpu_baseline"] = cpu_baseline_prefill(wp)
+    if not args.no_calibrate:
+        line["calibration"] = calibrate(em, torch)
+        log(f"  calibration: {line['calibration']}")
     print(json.dumps(line), flush=True)
 
 

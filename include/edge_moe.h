@@ -224,6 +224,15 @@ int edge_moe_residual(int32_t T, int32_t d, const uint16_t* x, const float* y, u
  * calibrate the memory-traffic counters of a profiler against bytes. */
 int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Matrix-core rate calibration (not a step of the layer): `blocks` workgroups
+ * of four waves each run `iters` rounds of eight independent bf16 MFMA chains
+ * (16 x 16 x 32, 16384 flops each), so one launch performs
+ * blocks * 4 * iters * 8 * 16384 flops; out[blocks * 256] float receives a
+ * fold of the accumulators.  Timed by the caller (events on `stream`), it
+ * gives the measured dense bf16 rate to set beside the published peak.
+ * EDGE_MOE_EINVAL for a null or misaligned out or non-positive counts. */
+int edge_moe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* edge_moe_status_string(int status);
 

@@ -29,7 +29,7 @@ EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_forward_traced", "edge_moe_residual", "edge_moe_status_string",
             "edge_moe_abi_version", "edge_moe_copy", "edge_moe_tile_shared",
             "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset",
-            "edge_moe_forward_noalloc", "edge_moe_forward_persistent")
+            "edge_moe_forward_noalloc", "edge_moe_forward_persistent", "edge_moe_mfma_peak")
 
 
 class CDims(ctypes.Structure):
@@ -96,6 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_moe_forward_persistent.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights),
                                                 vp, vp, sz, vp, ctypes.POINTER(CTrace)]
     lib.edge_moe_forward_persistent.restype = i32
+    lib.edge_moe_mfma_peak.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.edge_moe_mfma_peak.restype = i32
     lib.edge_moe_forward_noalloc.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights), vp, vp]
     lib.edge_moe_forward_noalloc.restype = i32
     lib.edge_moe_residual.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
@@ -224,6 +226,13 @@ def edge_moe_forward_persistent(dims, x, topk_idx, topk_w, weights, y, ws, strea
                                             _stream(stream), None if tr is None else ctypes.byref(tr))
     if st != EDGE_MOE_OK:
         raise EdgeMoeError("edge_moe_forward_persistent", st)
+
+
+def edge_moe_mfma_peak(out, blocks, iters, stream=None) -> None:
+    """Matrix-core calibration launch (blocks * 4 * iters * 8 * 16384 flops)."""
+    st = load().edge_moe_mfma_peak(_ptr(out), int(blocks), int(iters), _stream(stream))
+    if st != EDGE_MOE_OK:
+        raise EdgeMoeError("edge_moe_mfma_peak", st)
 
 
 def edge_moe_forward_noalloc(dims, x, topk_idx, topk_w, weights, y, stream=None) -> None:

@@ -19,17 +19,29 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libedge_moe.so")
-SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "decode.hip", "layer.hip", "prefill.hip"]
+SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "decode.hip", "layer.hip",
+           "prefill.hip", "calib.hip"]
 ARCH = "gfx950"
 
 
-def sources_digest() -> str:
-    """sha256 over the library's sources and public header: identifies the
-    kernels a stored profile was taken from."""
+# The source file of each kernel family (by kernel-name prefix); a stored
+# profile of a kernel stays valid while that file and the headers are unchanged.
+KERNEL_SOURCES = (("dec_layer", "layer.hip"), ("pl_", "layer.hip"), ("dec_", "decode.hip"),
+                  ("router_", "router.hip"), ("perm_", "dispatch.hip"), ("pf_", "prefill.hip"),
+                  ("mfma_peak", "calib.hip"), ("copy_bytes", "gemm.hip"))
+
+
+def sources_digest(kernel: str = "") -> str:
+    """sha256 over the headers and either every source (no kernel given) or the
+    source file of `kernel`: identifies the code a stored profile was taken from."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
-    for f in files + ["../../include/edge_moe.h"]:
+    headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    if kernel:
+        hit = [f for pre, f in KERNEL_SOURCES if kernel.startswith(pre)]
+        srcs = hit[:1] if hit else srcs
+    for f in headers + srcs + ["../../include/edge_moe.h"]:
         with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()

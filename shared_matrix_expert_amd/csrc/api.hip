@@ -569,6 +569,13 @@ int edge_moe_copy(void* dst, const void* src, size_t bytes, void* stream) {
     return em::launch_copy(dst, src, bytes, (hipStream_t)stream) == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
 }
 
+int edge_moe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream) {
+    if (!aligned(out, 4) || blocks < 1 || iters < 1) return EDGE_MOE_EINVAL;
+    const int st = check_device();
+    if (st != EDGE_MOE_OK) return st;
+    return em::launch_mfma_peak(out, blocks, iters, (hipStream_t)stream) == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
+}
+
 const char* edge_moe_status_string(int status) {
     switch (status) {
         case EDGE_MOE_OK: return "ok";

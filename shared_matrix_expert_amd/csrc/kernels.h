@@ -149,6 +149,7 @@ hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, h
 hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);
 hipError_t launch_act(const LayerArgs& a, hipStream_t s);     // needs r == 128, h % 256 == 0
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t stream);
 hipError_t launch_tile_shared(const uint8_t* src_q, uint8_t* dst_q, int G, int N, int K, hipStream_t stream);
 hipError_t launch_colblock(const uint8_t* src_q, uint8_t* dst_q, int M, int N, int K, hipStream_t stream);
 hipError_t launch_residual(int T, int d, const uint16_t* x, const float* y, uint16_t* x_out,

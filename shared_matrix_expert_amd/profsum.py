@@ -128,7 +128,7 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, calib_bytes: int, cmd_f
           ("fetch_kib_per_dispatch", f"{f_k:.1f}"), ("write_kib_per_dispatch", f"{w_k:.1f}"),
           ("calib_bytes", calib_bytes), ("calib_fetch_kib", f"{f_c:.1f}"), ("calib_write_kib", f"{w_c:.1f}"),
           ("fetch_factor", f"{ff:.4f}"), ("write_factor", f"{fw:.4f}"),
-          ("traffic_bytes_per_dispatch", f"{tb:.0f}"), ("sources_sha256", sources_digest())]
+          ("traffic_bytes_per_dispatch", f"{tb:.0f}"), ("sources_sha256", sources_digest(kernel))]
     head = (f"# HBM traffic of {kernel} ({workload})\n"
             "# FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by bytes / counter of the plain\n"
             "# copy kernel copy_bytes over calib_bytes bytes in the same run.\n")

@@ -133,6 +133,13 @@ def test_copy_validation_before_any_device_call():
         assert lib.edge_moe_copy(ctypes.c_void_p(dst), ctypes.c_void_p(src), n, None) == em.EDGE_MOE_EINVAL
 
 
+def test_mfma_peak_validation_before_any_device_call():
+    lib = em.load()
+    base = 1 << 40                          # never dereferenced: rejected first
+    for out, blocks, iters in [(0, 1, 1), (base + 2, 1, 1), (base, 0, 1), (base, 1, 0), (base, -4, 8)]:
+        assert lib.edge_moe_mfma_peak(ctypes.c_void_p(out), blocks, iters, None) == em.EDGE_MOE_EINVAL
+
+
 def test_tiled_weights_all_or_none():
     """The decode-tiled codes are optional: s_up's and s_dn's both or neither,
     a_up's on its own; aligned; only for shapes the layout takes."""
