@@ -11,6 +11,11 @@ reads for the library's plain copy kernel of known size (``copy_bytes``)::
     python -m shared_matrix_expert_amd.profsum traffic FETCH_DIR WRITE_DIR --kernel dec_act \\
         --calib-bytes 268435456 --cmd-fetch "..." --cmd-write "..."
 
+Per-dispatch means of any counters of one ``--pmc`` run, for chosen kernels::
+
+    python -m shared_matrix_expert_amd.profsum counters OUT_DIR --kernels "pf_gemm<0>,pf_gemm<1>" \
+        --cmd "..."
+
 The traffic summary records the digest of the library sources it was taken
 with, so that a reader can tell whether it still describes the current kernels.
 """
@@ -135,6 +140,53 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, calib_bytes: int, cmd_f
     return head + "".join(f"{k}: {v}\n" for k, v in kv)
 
 
+def counters(out_dir: str, kernels: list, cmd: str, title: str) -> str:
+    """Markdown table: per-dispatch mean of every counter in the run for each
+    kernel (matched by name with or without template arguments), then the
+    ratios that follow from them when the counters are present."""
+    path = _find(out_dir, "counter_collection.csv")
+    acc = defaultdict(float)
+    names, ctrs = {}, []
+    for r in csv.DictReader(open(path)):
+        c = _col(r, "Counter_Name").split("[")[0]
+        if c not in ctrs:
+            ctrs.append(c)
+        did = _col(r, "Dispatch_Id", "Dispatch_ID")
+        acc[(did, c)] += float(_col(r, "Counter_Value"))
+        names[did] = (_base(_col(r, "Kernel_Name")), _short(_col(r, "Kernel_Name")))
+    lines = [f"# {title}", "", f"Command: `{cmd}`", "",
+             "Per-dispatch means (each counter summed over its instances within a dispatch):", "",
+             "| kernel | dispatches | " + " | ".join(ctrs) + " |",
+             "|---|---:|" + "---:|" * len(ctrs)]
+    derived = []
+    for k in kernels:
+        dids = [d for d, (b, s_) in names.items() if k in (b, s_)]
+        if not dids:
+            lines.append(f"| {k} | 0 |" + " |" * len(ctrs))
+            continue
+        m = {c: sum(acc[(d, c)] for d in dids) / len(dids) for c in ctrs}
+        lines.append(f"| {k} | {len(dids)} | " + " | ".join(f"{m[c]:.4g}" for c in ctrs) + " |")
+        row = []
+        if m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+            row.append(("bf16 flops (MOPS x 512)", f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}"))
+        if m.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in m:
+            row.append(("SQ_INSTS_VALU / SQ_INSTS_MFMA",
+                        f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.3f}"))
+        if m.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in m:
+            row.append(("LDS bank-conflict cycles per LDS instruction",
+                        f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_INSTS_LDS']:.3f}"))
+        if m.get("SQ_BUSY_CU_CYCLES") and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            row.append(("MFMA busy cycles / CU busy cycles",
+                        f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_BUSY_CU_CYCLES']:.3f}"))
+        if row:
+            derived.append((k, row))
+    if derived:
+        lines += ["", "Derived:", ""]
+        for k, row in derived:
+            lines += [f"- {k}: " + "; ".join(f"{a} = {b}" for a, b in row)]
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path: str) -> dict:
     out = {}
     for line in open(path):
@@ -161,9 +213,16 @@ def main(argv=None):
     b.add_argument("--cmd-fetch", required=True)
     b.add_argument("--cmd-write", required=True)
     b.add_argument("--workload", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("out_dir")
+    c.add_argument("--kernels", required=True, help="comma-separated kernel names")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", default="rocprofv3 counters")
     args = ap.parse_args(argv)
     if args.what == "stats":
         sys.stdout.write(stats(args.out_dir, args.cmd, args.title, args.match))
+    elif args.what == "counters":
+        sys.stdout.write(counters(args.out_dir, args.kernels.split(","), args.cmd, args.title))
     else:
         sys.stdout.write(traffic(args.fetch_dir, args.write_dir, args.kernel, args.calib_bytes,
                                  args.cmd_fetch, args.cmd_write, args.workload))
