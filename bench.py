@@ -270,6 +270,43 @@ def stored_traffic(kernel: str, workload_tag: str):
     return int(float(t["traffic_bytes_per_dispatch"]))
 
 
+# Library kernel names (the per-kernel event table) and their names in a
+# rocprofv3 kernel trace, for the kernels that can be a roofline's dominant one.
+TRACE_NAMES = {"dec_down_wst": "dec_down_ws<true>", "dec_down_ws": "dec_down_ws<false>", "dec_act": "dec_act<1>",
+               "dec_up_ws": "dec_up_ws", "dec_layer": "dec_layer<16>", "router_topk": "router_topk_split",
+               "router_logits_split": "router_logits_split", "pf_down": "pf_gemm<1>",
+               "pf_shared_up": "pf_gemm<0>", "pf_z1": "pf_gemm<2>", "pf_z2": "pf_gemm<3>",
+               "pf_delta_up_act": "pf_act"}
+
+
+def rocprof_avg_ms(kernel: str, workload_tag: str):
+    """Average launch time of `kernel` in the committed rocprofv3 kernel
+    statistics of the workload (profiles/<tag>_kernels.md), or None."""
+    path = os.path.join(ROOT, "profiles", f"{workload_tag}_kernels.md")
+    want = TRACE_NAMES.get(kernel, kernel)
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 4 and cells[0] == want:
+            return float(cells[3]) / 1e3
+    return None
+
+
+def add_rocprof(roof, workload_tag):
+    """Beside the live event time that `frac` uses: the same kernel's rocprofv3
+    average from profiles/ and the fraction it gives."""
+    ms = rocprof_avg_ms(roof["kernel"], workload_tag)
+    roof["avg_ms_rocprof"] = round(ms, 5) if ms else None
+    if ms:
+        if roof["unit"] == "GB/s":
+            roof["frac_rocprof"] = round(roof["bytes_per_launch"] / (ms * 1e-3) / 1e9 / roof["peak"], 4)
+        else:
+            roof["frac_rocprof"] = round(roof["flops_per_launch"] / (ms * 1e-3) / 1e12 / roof["peak"], 4)
+    roof["time_source"] = "frac: HIP events around each launch in this run; frac_rocprof: profiles/%s_kernels.md" % workload_tag
+    return roof
+
+
 def kernel_table(D, idxs, ktimes):
     """Per-kernel average time, algorithmic bytes and the HBM rate they imply."""
     out = {}
@@ -437,6 +474,7 @@ def persistent_line(wl, steps, warmup, tag):
     kt = wl.kernel_times(max(20, steps // 4))
     name, roof = roofline_hbm(wl.D, idxs, kt)
     roof["traffic"] = stored_traffic(name, tag)
+    add_rocprof(roof, tag)
     sb = float(np.mean([step_bytes(wl.D, ix) for ix in idxs]))
     wl.persistent = False
     log(f"  persistent launch ({tag}): {sec * 1e6:.1f} us per step")
@@ -535,6 +573,7 @@ def main():
             log(f"  verify kernel {k:22s} launches {n:5d} avg {ms * 1e3:8.2f} us")
         kname, roof = roofline_hbm(D, idxs, ktimes)
         roof["traffic"] = stored_traffic(kname, "verify_t8")
+        add_rocprof(roof, "verify_t8")
         sb = float(np.mean([step_bytes(D, ix) for ix in idxs]))
         line = {
             "metric": METRIC,
@@ -574,6 +613,7 @@ def main():
         dkt = wd.kernel_times(max(20, args.steps // 4))
         dname, droof = roofline_hbm(wd.D, didx, dkt)
         droof["traffic"] = stored_traffic(dname, "decode_t1")
+        add_rocprof(droof, "decode_t1")
         dsb = float(np.mean([step_bytes(wd.D, ix) for ix in didx]))
         line["decode_t1"] = {
             "value": round(wd.D.T / dsec, 1), "unit": "tokens/s", "steps": args.steps,
@@ -620,6 +660,7 @@ def main():
             log(f"  prefill kernel {k:22s} launches {n:5d} avg {ms:9.3f} ms")
         pname, proof = roofline_mfma(wp.D, pidx, pk)
         proof["traffic"] = stored_traffic(pname, "prefill_16k")
+        add_rocprof(proof, "prefill_16k")
         total_fl = float(np.mean([step_flops(wp.D, ix) for ix in pidx]))
         line["prefill_16k"] = {
             "value": round(wp.D.T / psec, 1), "unit": "tokens/s", "steps": args.prefill_steps,
