@@ -416,8 +416,8 @@ _NS2_FAULT = pytest.mark.skip(reason="faulted the GPU (memory aperture violation
 def test_ragged_batches(T):
     """Token counts that leave partial tiles and cross the router's small/large
     paths; 13 and 16 put more than 8 tokens into a group, so the shared up
-    stages x as 16 rows x 1024 elements instead of 8 x 2048; 24 and 32 take
-    the two-subtile decode kernels."""
+    stages x as 16 rows x 1024 elements instead of 8 x 2048; 24 and 32 would
+    run the four-subtile kernels and are skipped for the reason given."""
     say(f"case: ragged T={T}")
     D = synth.config(1).dims.with_T(T)
     x = synth.make_activations(1, 5, T=T)
