@@ -10,6 +10,8 @@ Modules
 codecs : exact decoders of the storage formats (bf16, fp16, packed int4) and the
          round-to-nearest-even helpers used at the layer's rounding points.
 layer  : route() and moe_forward() in "contract" and "exact" modes.
+mx     : the microscaling variant: MXFP4 (E2M1 + E8M0) weights, MXFP8 (E4M3)
+         product inputs, moe_forward_mx().
 
 Every function cites the passage it follows.  Parity status of each function is
 listed in its docstring; the only unpinned quantity is the absolute value of a
@@ -17,5 +19,5 @@ whole layer's output against the pages, which print no worked example
 ("parity unpinned" for that comparison; every internal step is pinned by the
 tests under tests/test_oracle_*.py).
 """
-from . import codecs, layer  # noqa: F401
+from . import codecs, layer, mx  # noqa: F401
 from .layer import route, moe_forward  # noqa: F401

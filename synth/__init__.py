@@ -39,7 +39,7 @@ import numpy as np
 __all__ = [
     "Dims", "CONFIGS", "config", "make_activations", "make_router",
     "make_weights", "quantize_int4_torch", "bf16_bits_from_f32",
-    "skew_bias_table", "WEIGHT_STD",
+    "skew_bias_table", "WEIGHT_STD", "make_weights_mx", "quantize_mxfp4_torch",
 ]
 
 WEIGHT_STD = 0.02  # std of every expert weight before quantisation
@@ -91,6 +91,10 @@ CONFIGS: Dict[int, Config] = {
     2: Config(2, "verify T=8 skewed", Dims(T=8, **_FULL), router_std=0.02, skew=True),
     3: Config(3, "prefill T=16384", Dims(T=16384, **_FULL), router_std=1.0 / 64.0),
     4: Config(4, "48-layer stack T=8", Dims(T=8, **_FULL), router_std=0.02, layers=48),
+    # small shapes for the MXFP4 variant (rank 128, several groups, T past the decode range)
+    5: Config(5, "mx small T=96", Dims(T=96, d=512, h=1024, n_experts=64, experts_per_group=8,
+                                       top_k=4, delta_rank=128, lora_rank=16, quant_group=32),
+              router_std=0.02),
 }
 
 
@@ -246,6 +250,82 @@ def make_weights(cfg_id: int, seed: int, layer: int = 0, device="cpu",
     out["b_up"], out["b_up_scale"] = _int4_tensor("b_up", (E, h, r), D.gq(r), *args, zero=zero_delta)
     out["a_dn"], out["a_dn_scale"] = _int4_tensor("a_dn", (E, r, h), D.gq(h), *args, zero=zero_delta)
     out["b_dn"], out["b_dn_scale"] = _int4_tensor("b_dn", (E, d, r), D.gq(r), *args, zero=zero_delta)
+    out["lora_up_u"] = _bf16_tensor("lora_up_u", (G, rL, d), *args, zero=zero_lora)
+    out["lora_up_v"] = _bf16_tensor("lora_up_v", (G, h, rL), *args, zero=zero_lora)
+    out["lora_dn_u"] = _bf16_tensor("lora_dn_u", (G, rL, h), *args, zero=zero_lora)
+    out["lora_dn_v"] = _bf16_tensor("lora_dn_v", (G, d, rL), *args, zero=zero_lora)
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# MXFP4 expert weights (the microscaling variant of the layer)
+# ----------------------------------------------------------------------------------
+
+MX_BLOCK = 32
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mxfp4_torch(w):
+    """Round float32 weights to MXFP4 along the last axis (OCP Microscaling
+    Formats v1.0): per block of 32, E8M0 byte X = floor(log2(amax)) - 2 + 127
+    (2 = the exponent of E2M1's largest value), limited to 0..254 (0 for an
+    all-zero block); each element is the E2M1 value nearest to w / 2^(X-127),
+    ties to the even code, saturated at 6.  Returns (codes packed two per byte,
+    element 2i in the low nibble: uint8 [..., K/2]; E8M0 bytes uint8 [..., K/32]).
+    This is the storage rounding of the synthetic weights, not a step of the layer."""
+    import torch
+    K = w.shape[-1]
+    assert K % MX_BLOCK == 0
+    lead = w.shape[:-1]
+    b = w.reshape(*lead, K // MX_BLOCK, MX_BLOCK).to(torch.float32)
+    amax = b.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                        # amax = m * 2^ex, m in [0.5, 1)
+    X = torch.where(amax > 0, (ex - 1 - 2 + 127).clamp(0, 254), torch.zeros_like(ex))
+    scale = torch.pow(torch.tensor(2.0, device=w.device), (X - 127).to(torch.float32))
+    a = (b.abs() / scale.unsqueeze(-1)).clamp(max=6.0)
+    grid = torch.tensor(_E2M1_GRID, device=w.device)
+    mids = (grid[:-1] + grid[1:]) / 2
+    idx = (a.unsqueeze(-1) > mids).sum(-1)           # nearest, the lower one at a tie
+    tie = (a.unsqueeze(-1) == mids).any(-1)
+    idx = torch.where(tie & (idx % 2 == 1), idx + 1, idx)
+    code = (idx | torch.where(b < 0, 8, 0)).to(torch.uint8).reshape(*lead, K)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), X.to(torch.uint8).contiguous()
+
+
+def _mxfp4_tensor(name, shape, cfg_id, layer, seed, device, zero=False):
+    import torch
+    if zero:
+        K = shape[-1]
+        return (torch.zeros(*shape[:-1], K // 2, dtype=torch.uint8, device=device),
+                torch.zeros(*shape[:-1], K // MX_BLOCK, dtype=torch.uint8, device=device))
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(cfg_id, layer, name, seed))
+    qs, ss = [], []
+    for i in range(shape[0]):
+        w = torch.randn(*shape[1:], generator=g, device=device, dtype=torch.float32) * WEIGHT_STD
+        q, s = quantize_mxfp4_torch(w)
+        qs.append(q)
+        ss.append(s)
+    return torch.stack(qs).contiguous(), torch.stack(ss).contiguous()
+
+
+def make_weights_mx(cfg_id: int, seed: int, layer: int = 0, device="cpu",
+                    zero_delta: bool = False, zero_lora: bool = False) -> dict:
+    """The MXFP4 variant of make_weights: the same draws (same streams, same
+    N(0, 0.02^2)), rounded to MXFP4 instead of int4.  Layouts: codes as the
+    int4 ones ([N][K/2], two per byte), E8M0 scales uint8 [N][K/32] under the
+    same "_scale" names; LoRA factors bf16 as in make_weights."""
+    D = CONFIGS[cfg_id].dims
+    G, E, d, h, r, rL = D.n_groups, D.n_experts, D.d, D.h, D.delta_rank, D.lora_rank
+    out = {}
+    args = (cfg_id, layer, seed, device)
+    out["s_up"], out["s_up_scale"] = _mxfp4_tensor("s_up", (G, h, d), *args)
+    out["s_dn"], out["s_dn_scale"] = _mxfp4_tensor("s_dn", (G, d, h), *args)
+    out["a_up"], out["a_up_scale"] = _mxfp4_tensor("a_up", (E, r, d), *args, zero=zero_delta)
+    out["b_up"], out["b_up_scale"] = _mxfp4_tensor("b_up", (E, h, r), *args, zero=zero_delta)
+    out["a_dn"], out["a_dn_scale"] = _mxfp4_tensor("a_dn", (E, r, h), *args, zero=zero_delta)
+    out["b_dn"], out["b_dn_scale"] = _mxfp4_tensor("b_dn", (E, d, r), *args, zero=zero_delta)
     out["lora_up_u"] = _bf16_tensor("lora_up_u", (G, rL, d), *args, zero=zero_lora)
     out["lora_up_v"] = _bf16_tensor("lora_up_v", (G, h, rL), *args, zero=zero_lora)
     out["lora_dn_u"] = _bf16_tensor("lora_dn_u", (G, rL, h), *args, zero=zero_lora)
