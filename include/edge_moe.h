@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define EDGE_MOE_ABI_VERSION 3
+#define EDGE_MOE_ABI_VERSION 4
 
 /* Status codes. */
 #define EDGE_MOE_OK           0
@@ -207,6 +207,58 @@ int edge_moe_forward_traced(const edge_moe_dims* dims, const uint16_t* x,
  * edge_moe_forward. */
 int edge_moe_forward_noalloc(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                              const float* topk_w, const edge_moe_weights* weights, float* y, void* stream);
+
+/* ---------------------------------------------------------------- MX variant --
+ * The expert layer with its six large matrices in MXFP4 instead of int4: the
+ * microscaling format of the Open Compute Project's MX specification v1.0,
+ * MI355X's native 4-bit floating format.  The pages ship 4-bit floating-point
+ * builds of the model (byteiota "Edge0-145B: Run a 145B Open-Source Model on
+ * Your Laptop", What You Need to Run It).
+ *
+ * Layouts: each matrix is stored N x K like the int4 one; codes [N][K/2] bytes,
+ * two E2M1 codes per byte (element 2i in the low nibble: sign bit 3, exponent
+ * bits 2..1 with bias 1, mantissa bit 0); scales [N][K/32] bytes, one E8M0
+ * power of two 2^(X - 127) per 32 consecutive elements along K (X = 255 is
+ * NaN: not allowed).  The weight is code value * 2^(X - 127) exactly.  LoRA
+ * factors are bf16 as in edge_moe_weights.  16-byte aligned device pointers.
+ *
+ * Arithmetic: the int4 layer's, except that the inputs of the four large
+ * MXFP4 products, x (for S_up, A_up) and a (for S_dn, A_dn), are first
+ * quantised to MXFP8 along K, per block of 32: E8M0 byte
+ * X = floor(log2(block max |v|)) - 8 + 127 limited to 0..254 (0 for an
+ * all-zero block), each element v / 2^(X - 127) rounded to the nearest E4M3
+ * value (ties to even, magnitudes past 448 saturated to 448).  The rank-r
+ * inputs z1, z2 (bf16 after R1, R4) meet B_up, B_dn unquantised, and the
+ * LoRA products take x and a unquantised; R1-R5 round to bf16 as in the int4
+ * layer.  The large products run on the scaled FP4 x FP8 matrix cores, which
+ * sum the 128 products of one instruction to about 2^-13.5 of their
+ * magnitude sum, so results meet the layer's tolerance, not bit equality.
+ * B_up and B_dn scale bytes must not exceed 252 (their weights are formed in
+ * bf16).
+ *
+ * Shapes: delta_rank 128, d and h multiples of 256 (at least 256), lora_rank a
+ * multiple of 8 from 8 to 32; any T.  quant_group is not used.  Other shapes:
+ * EDGE_MOE_EUNSUPPORTED.  Every batch size runs the tiled large-batch kernels. */
+typedef struct edge_moe_weights_mx {
+    const uint8_t*  s_up_q;  const uint8_t* s_up_e;   /* [G][h][d/2], [G][h][d/32] */
+    const uint8_t*  s_dn_q;  const uint8_t* s_dn_e;   /* [G][d][h/2], [G][d][h/32] */
+    const uint8_t*  a_up_q;  const uint8_t* a_up_e;   /* [E][r][d/2], [E][r][d/32] */
+    const uint8_t*  b_up_q;  const uint8_t* b_up_e;   /* [E][h][r/2], [E][h][r/32] */
+    const uint8_t*  a_dn_q;  const uint8_t* a_dn_e;   /* [E][r][h/2], [E][r][h/32] */
+    const uint8_t*  b_dn_q;  const uint8_t* b_dn_e;   /* [E][d][r/2], [E][d][r/32] */
+    const uint16_t* lora_up_u; const uint16_t* lora_up_v;
+    const uint16_t* lora_dn_u; const uint16_t* lora_dn_v;
+} edge_moe_weights_mx;
+
+/* Workspace bytes of edge_moe_forward_mx (0 for invalid or unsupported dims). */
+size_t edge_moe_workspace_bytes_mx(const edge_moe_dims* dims);
+
+/* The MX expert layer (a3-a11), arguments as edge_moe_forward_traced (trace may
+ * be NULL); ws_bytes >= edge_moe_workspace_bytes_mx(dims).  The same status
+ * codes; asynchronous on `stream`. */
+int edge_moe_forward_mx(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                        const float* topk_w, const edge_moe_weights_mx* weights, float* y, void* ws,
+                        size_t ws_bytes, void* stream, const edge_moe_trace* trace);
 
 /* Residual between stacked layers (a12): x_out[t][i] = bf16(x[t][i] + y[t][i]),
  * the exact sum rounded once to the nearest bf16 (ties to even).  The layers

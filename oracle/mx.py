@@ -20,10 +20,14 @@ Readings (each listed in the design notes, "MX variant"):
 * Weights (S_up, S_dn, A_up, B_up, A_dn, B_dn) are stored as MXFP4 along K
   (two codes per byte, element 2i in the low nibble of byte i; E8M0 scales
   [N][K/32]).  LoRA factors stay bf16.
-* Every input of a product with an MXFP4 matrix is quantised to MXFP8 (E4M3)
-  along K first: the token rows x (for S_up and A_up), the rounded rank-r
-  inputs z1 and z2 (for B_up and B_dn), the activation rows a (for S_dn and
-  A_dn).  The LoRA products take the unquantised x and a, as in the int4 layer.
+* The inputs of the large MXFP4 products are quantised to MXFP8 (E4M3) along
+  K first: the token rows x (for S_up and A_up) and the activation rows a (for
+  S_dn and A_dn), where the matrix cores multiply FP4 by FP8.  The rank-r
+  inputs z1 and z2 (already rounded to bf16 by R1 and R4) meet B_up and B_dn
+  unquantised: a second rounding there, to 3-bit mantissas, would make every
+  delta jump with the last bit of z1 or z2, and those products are a few
+  percent of the work.  The LoRA products take the unquantised x and a, as in
+  the int4 layer.
 * The block scale is the specification's: X = floor(log2(amax)) - 8 + 127
   (8 = the exponent of E4M3's largest normal), limited to 0..254, X = 0 for an
   all-zero block; each element is v / 2^(X - 127) rounded to the nearest E4M3
@@ -38,8 +42,9 @@ their bit-field definitions and against each other's grids; the E4M3 encoder
 against a brute-force nearest-value search; the block scale's range property;
 quantisation error bounds and scale equivariance; the layer against the int4
 oracle on inputs for which every quantiser is the identity (so the MX mode
-reduces to a layer the int4 pins already fix), and against the same layer with
-the quantiser disabled (which must then differ).
+reduces to a layer the int4 pins already fix), against the same layer with
+the quantiser disabled (which must then differ), and identity-structured
+weights that show where the quantiser sits and where it does not.
 """
 from __future__ import annotations
 
@@ -174,9 +179,9 @@ def moe_forward_mx(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray, W: dict,
 
     For token t and slot j with expert e in group g:
         x~ = Q(x)                                    (MXFP8 of the token row)
-        h  = S_up_g x~ + B_up_e Q(R1(A_up_e x~)) + V_up_g R2(U_up_g x)
+        h  = S_up_g x~ + B_up_e R1(A_up_e x~) + V_up_g R2(U_up_g x)
         a  = R3(SiLU(h));  a~ = Q(a)
-        o  = S_dn_g a~ + B_dn_e Q(R4(A_dn_e a~)) + V_dn_g R5(U_dn_g a)
+        o  = S_dn_g a~ + B_dn_e R4(A_dn_e a~) + V_dn_g R5(U_dn_g a)
         y_t = sum_{j=0..k-1} w_tj o_tj                (slot order)
     with every weight its exact MXFP4 value and Q the MXFP8 round trip along
     the product's K.  ``quantise=False`` replaces Q by the identity (used by
@@ -228,7 +233,7 @@ def moe_forward_mx(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray, W: dict,
             Bup = dq(W["b_up"][e], W["b_up_scale"][e], r)
             z1 = rn_bf16(Xgq[m] @ Aup.T)                            # R1
             z1_all[m] = z1
-            H[m] += Q(z1) @ Bup.T
+            H[m] += z1 @ Bup.T
         A = rn_bf16(silu(H))                                        # R3
         Aq = Q(A)
         zl2 = rn_bf16(A @ Udn.T)                                    # R5 (unquantised a)
@@ -240,7 +245,7 @@ def moe_forward_mx(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray, W: dict,
             Bdn = dq(W["b_dn"][e], W["b_dn_scale"][e], r)
             z2 = rn_bf16(Aq[m] @ Adn.T)                             # R4
             z2_all[m] = z2
-            Og[m] += Q(z2) @ Bdn.T
+            Og[m] += z2 @ Bdn.T
         O[tt, jj] = Og
         if keep:
             inter["z1"][tt, jj] = z1_all

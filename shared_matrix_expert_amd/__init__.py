@@ -29,7 +29,8 @@ EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_forward_traced", "edge_moe_residual", "edge_moe_status_string",
             "edge_moe_abi_version", "edge_moe_copy", "edge_moe_tile_shared",
             "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset",
-            "edge_moe_forward_noalloc", "edge_moe_forward_persistent", "edge_moe_mfma_peak")
+            "edge_moe_forward_noalloc", "edge_moe_forward_persistent", "edge_moe_mfma_peak",
+            "edge_moe_workspace_bytes_mx", "edge_moe_forward_mx")
 
 
 class CDims(ctypes.Structure):
@@ -53,6 +54,16 @@ _OPTIONAL_KEYS = ("s_up_t", "s_dn_t", "a_up_t", "a_dn_t")
 
 class CWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
+
+
+# the MX variant: E8M0 scale bytes in place of the fp16 scales, no tiled copies
+_WEIGHT_FIELDS_MX = ("s_up_q", "s_up_e", "s_dn_q", "s_dn_e", "a_up_q", "a_up_e",
+                     "b_up_q", "b_up_e", "a_dn_q", "a_dn_e", "b_dn_q", "b_dn_e",
+                     "lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v")
+
+
+class CWeightsMX(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS_MX]
 
 
 class CTrace(ctypes.Structure):
@@ -96,6 +107,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_moe_forward_persistent.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights),
                                                 vp, vp, sz, vp, ctypes.POINTER(CTrace)]
     lib.edge_moe_forward_persistent.restype = i32
+    lib.edge_moe_workspace_bytes_mx.argtypes = [ctypes.POINTER(CDims)]
+    lib.edge_moe_workspace_bytes_mx.restype = sz
+    lib.edge_moe_forward_mx.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeightsMX),
+                                        vp, vp, sz, vp, ctypes.POINTER(CTrace)]
+    lib.edge_moe_forward_mx.restype = i32
     lib.edge_moe_mfma_peak.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
     lib.edge_moe_mfma_peak.restype = i32
     lib.edge_moe_forward_noalloc.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights), vp, vp]
@@ -143,6 +159,26 @@ def _stream(stream) -> Optional[int]:
 
 def cweights(weights: dict) -> CWeights:
     return CWeights(*(_ptr(weights.get(k) if k in _OPTIONAL_KEYS else weights[k]) for k in _WEIGHT_KEYS))
+
+
+def cweights_mx(weights: dict) -> CWeightsMX:
+    """Struct of an MX weight dict (keys as the int4 ones: codes under the
+    matrix name, E8M0 bytes under "<name>_scale")."""
+    return CWeightsMX(*(_ptr(weights[k]) for k in _WEIGHT_KEYS[:16]))
+
+
+def edge_moe_workspace_bytes_mx(dims) -> int:
+    return int(load().edge_moe_workspace_bytes_mx(ctypes.byref(cdims(dims))))
+
+
+def edge_moe_forward_mx(dims, x, topk_idx, topk_w, weights, y, ws, stream=None, trace=None) -> None:
+    """The expert layer with MXFP4 shared and delta matrices."""
+    tr = None if trace is None else ctypes.byref(CTrace(*(_ptr(trace.get(n)) for n, _ in CTrace._fields_)))
+    st = load().edge_moe_forward_mx(ctypes.byref(cdims(dims)), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+                                    ctypes.byref(cweights_mx(weights)), _ptr(y), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream), tr)
+    if st != EDGE_MOE_OK:
+        raise EdgeMoeError("edge_moe_forward_mx", st)
 
 
 def edge_moe_tile_shared(dims, which, src_q, dst_q, stream=None) -> None:

@@ -496,6 +496,105 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     return EDGE_MOE_OK;
 }
 
+// ---------------------------------------------------------------- MX variant --
+// The general layout followed by the MXFP8 copies of the product inputs.
+struct MxLayout {
+    Layout L;
+    size_t xq, xs, aq, as, bytes;
+};
+
+static MxLayout make_mx_layout(const edge_moe_dims& d) {
+    MxLayout M{};
+    M.L = make_layout(d);
+    size_t off = M.L.fwd_bytes;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    const size_t T = (size_t)d.T, R = (size_t)M.L.R;
+    M.xq = take(T * d.d);
+    M.xs = take(T * d.d / 32);
+    M.aq = take(R * d.h);
+    M.as = take(R * d.h / 32);
+    M.bytes = off;
+    return M;
+}
+
+static bool mx_dims_ok(const edge_moe_dims& d) {
+    return em::mx_layer_ok(d.d, d.h, d.delta_rank, d.lora_rank);
+}
+
+size_t edge_moe_workspace_bytes_mx(const edge_moe_dims* dims) {
+    if (check_dims(dims) != EDGE_MOE_OK || !mx_dims_ok(*dims)) return 0;
+    const MxLayout M = make_mx_layout(*dims);
+    return M.bytes > M.L.route_bytes ? M.bytes : M.L.route_bytes;
+}
+
+int edge_moe_forward_mx(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                        const float* topk_w, const edge_moe_weights_mx* wt, float* y, void* ws,
+                        size_t ws_bytes, void* stream, const edge_moe_trace* trace) {
+    int st = check_dims(dims);
+    if (st != EDGE_MOE_OK) return st;
+    if (!wt) return EDGE_MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(y, 16))
+        return EDGE_MOE_EINVAL;
+    const void* wptrs[16] = {wt->s_up_q, wt->s_up_e, wt->s_dn_q, wt->s_dn_e, wt->a_up_q, wt->a_up_e,
+                             wt->b_up_q, wt->b_up_e, wt->a_dn_q, wt->a_dn_e, wt->b_dn_q, wt->b_dn_e,
+                             wt->lora_up_u, wt->lora_up_v, wt->lora_dn_u, wt->lora_dn_v};
+    for (const void* p : wptrs)
+        if (!aligned(p, 16)) return EDGE_MOE_EINVAL;
+    if (!mx_dims_ok(*dims)) return EDGE_MOE_EUNSUPPORTED;
+    if (!ws) return EDGE_MOE_EWORKSPACE;
+    if (!aligned(ws, kAlign)) return EDGE_MOE_EINVAL;
+    const MxLayout M = make_mx_layout(*dims);
+    if (ws_bytes < M.bytes) return EDGE_MOE_EWORKSPACE;
+    st = check_device();
+    if (st != EDGE_MOE_OK) return st;
+
+    const edge_moe_dims& d = *dims;
+    const Layout& L = M.L;
+    char* base = reinterpret_cast<char*>(ws);
+    em::LayerArgs a{};
+    a.T = d.T; a.d = d.d; a.h = d.h; a.E = d.n_experts; a.P = d.experts_per_group;
+    a.G = L.G; a.k = d.top_k; a.r = d.delta_rank; a.rL = d.lora_rank; a.gq = 32;
+    a.mt = 64;
+    a.x = x; a.topk_w = topk_w;
+    a.s_up = wt->s_up_q; a.s_dn = wt->s_dn_q; a.a_up = wt->a_up_q; a.b_up = wt->b_up_q;
+    a.a_dn = wt->a_dn_q; a.b_dn = wt->b_dn_q;
+    a.s_up_e = wt->s_up_e; a.s_dn_e = wt->s_dn_e; a.a_up_e = wt->a_up_e; a.b_up_e = wt->b_up_e;
+    a.a_dn_e = wt->a_dn_e; a.b_dn_e = wt->b_dn_e;
+    a.lu_u = wt->lora_up_u; a.lu_v = wt->lora_up_v; a.ld_u = wt->lora_dn_u; a.ld_v = wt->lora_dn_v;
+    a.z1 = reinterpret_cast<uint16_t*>(base + L.z1);
+    a.zl = reinterpret_cast<uint16_t*>(base + L.zl);
+    a.hs = reinterpret_cast<float*>(base + L.hs);
+    a.act = reinterpret_cast<uint16_t*>(base + L.act);
+    a.z2 = reinterpret_cast<uint16_t*>(base + L.z2);
+    a.zl2 = reinterpret_cast<uint16_t*>(base + L.zl2);
+    a.o = reinterpret_cast<float*>(base + L.o);
+    a.xq = reinterpret_cast<uint8_t*>(base + M.xq);
+    a.xs = reinterpret_cast<uint8_t*>(base + M.xs);
+    a.aq = reinterpret_cast<uint8_t*>(base + M.aq);
+    a.as = reinterpret_cast<uint8_t*>(base + M.as);
+    a.y = y;
+    a.db = dispatch_bufs(L, base);
+    const int64_t R = L.R, G = L.G, E = d.n_experts;
+    a.max_etiles = (int)((R + a.mt - 1) / a.mt + (E < R ? E : R));
+    a.max_gtiles_u = (int)((L.Umax + a.mt - 1) / a.mt + G);
+    a.max_gtiles_r = (int)((R + a.mt - 1) / a.mt + G);
+    a.umax = L.Umax;
+    a.rmax = R;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err = em::launch_dispatch(topk_idx, a.db, d.T, d.top_k, d.n_experts, d.experts_per_group, a.mt, s);
+    if (err == hipSuccess) err = em::launch_mx_layer(a, s);
+    if (err != hipSuccess) return EDGE_MOE_EHIP;
+    if (trace) {
+        err = copy_perm_trace(trace, a.db, d, s);
+        if (err == hipSuccess && trace->act)
+            err = em::launch_gather_rows(a.act, a.db.slot_row, trace->act, R, (int64_t)d.h * 2, s);
+        if (err == hipSuccess && trace->expert_out)
+            err = em::launch_gather_rows(a.o, a.db.slot_row, trace->expert_out, R, (int64_t)d.d * 4, s);
+        if (err != hipSuccess) return EDGE_MOE_EHIP;
+    }
+    return EDGE_MOE_OK;
+}
+
 int edge_moe_forward(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                      const float* topk_w, const edge_moe_weights* weights, float* y, void* ws,
                      size_t ws_bytes, void* stream) {

@@ -474,9 +474,7 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
     } else {
         launch_gemm<M_Z1>(a, a.max_etiles, a.r, s, "gemm_z1");
     }
-    prof_begin(s);
-    lora_in<0><<<a.max_gtiles_u, 256, 0, s>>>(a);
-    prof_end(s, "lora_in_up");
+    launch_lora_in(a, 0, s);
     // a4 + a6: shared up + LoRA up, once per (token, group)
     if (a.pf) {
         hipError_t e = launch_gather_x(a, a.umax, s);
@@ -499,9 +497,7 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
     } else {
         launch_gemm<M_Z2>(a, a.max_etiles, a.r, s, "gemm_z2");
     }
-    prof_begin(s);
-    lora_in<1><<<a.max_gtiles_r, 256, 0, s>>>(a);
-    prof_end(s, "lora_in_down");
+    launch_lora_in(a, 1, s);
     // a8 - a10: shared down + delta down + LoRA down
     if (a.pf) {
         const hipError_t e = launch_prefill_gemm(a, PF_OUT, a.rmax, s);
@@ -509,7 +505,21 @@ hipError_t launch_expert_layer(const LayerArgs& a, hipStream_t s) {
     } else {
         launch_gemm<M_OUT>(a, a.max_gtiles_r, a.d, s, "gemm_down");
     }
-    // a11
+    return launch_combine(a, s);   // a11
+}
+
+void launch_lora_in(const LayerArgs& a, int down, hipStream_t s) {
+    prof_begin(s);
+    if (down) {
+        lora_in<1><<<a.max_gtiles_r, 256, 0, s>>>(a);
+        prof_end(s, "lora_in_down");
+    } else {
+        lora_in<0><<<a.max_gtiles_u, 256, 0, s>>>(a);
+        prof_end(s, "lora_in_up");
+    }
+}
+
+hipError_t launch_combine(const LayerArgs& a, hipStream_t s) {
     const int64_t n4 = (int64_t)a.T * (a.d / 4);
     prof_begin(s);
     combine<<<(int)((n4 + 255) / 256), 256, 0, s>>>(a.o, a.topk_w, a.db.slot_row, a.y, a.T, a.d, a.k);

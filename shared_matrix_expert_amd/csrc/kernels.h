@@ -58,6 +58,13 @@ struct LayerArgs {
     int max_etiles, max_gtiles_u, max_gtiles_r;   // grid bounds
     int pf;                     // shared up / down on the LDS-tiled prefill GEMMs (prefill_gemm_ok)
     int64_t umax, rmax;         // bounds on distinct (token, group) pairs and rows
+    // microscaling variant: E8M0 block scales of the six MXFP4 matrices (the
+    // codes are in s_up .. b_dn) and the MXFP8 copies of the product inputs
+    const uint8_t* s_up_e; const uint8_t* s_dn_e;
+    const uint8_t* a_up_e; const uint8_t* b_up_e;
+    const uint8_t* a_dn_e; const uint8_t* b_dn_e;
+    uint8_t* xq;  uint8_t* xs;  // [T][d] E4M3, [T][d/32] E8M0
+    uint8_t* aq;  uint8_t* as;  // [R][h], [R][h/32]
 };
 
 // Small-batch expert layer (T <= 64, T*k <= 1024): three launches, every
@@ -149,6 +156,10 @@ hipError_t launch_prefill_gemm(const LayerArgs& a, int mode, int64_t max_rows, h
 hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);
 hipError_t launch_act(const LayerArgs& a, hipStream_t s);     // needs r == 128, h % 256 == 0
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+void launch_lora_in(const LayerArgs& a, int down, hipStream_t s);
+hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
+bool mx_layer_ok(int d, int h, int r, int rL);
+hipError_t launch_mx_layer(const LayerArgs& a, hipStream_t s);
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t stream);
 hipError_t launch_tile_shared(const uint8_t* src_q, uint8_t* dst_q, int G, int N, int K, hipStream_t stream);
 hipError_t launch_colblock(const uint8_t* src_q, uint8_t* dst_q, int M, int N, int K, hipStream_t stream);

@@ -6,6 +6,7 @@ misaligned pointers, workspace size) is exercised with fake addresses that the
 library never dereferences.
 """
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert em.edge_moe_abi_version() == 3
+    assert em.edge_moe_abi_version() == 4
     for st in (0, -1, -2, -3, -4):
         assert em.status_string(st)
     assert em.status_string(7) == "unknown status"
@@ -184,3 +185,27 @@ def test_tile_shared_validation_before_device():
                                     ctypes.c_void_p(base + big), None) == em.EDGE_MOE_EUNSUPPORTED
     assert lib.edge_moe_tile_shared(ctypes.byref(em.cdims(D8)), 3, ctypes.c_void_p(base),
                                     ctypes.c_void_p(base + big), None) == em.EDGE_MOE_EUNSUPPORTED
+
+
+def test_mx_shapes_and_validation_before_any_device_call():
+    """The MX variant takes rank 128, d and h multiples of 256, lora rank 8..32
+    (multiple of 8); other shapes get no workspace size and EUNSUPPORTED."""
+    D = synth.config(5).dims
+    assert em.edge_moe_workspace_bytes_mx(D) > em.edge_moe_workspace_bytes(D) > 0
+    for bad in (dict(delta_rank=64), dict(d=384), dict(h=640), dict(lora_rank=4), dict(lora_rank=40)):
+        Db = dataclasses.replace(D, **bad)
+        assert em.edge_moe_workspace_bytes_mx(Db) == 0, bad
+    lib = em.load()
+    base = 1 << 40
+    W = em.CWeightsMX(*([base] * 16))
+    dims = em.cdims(dataclasses.replace(D, delta_rank=64))
+    st = lib.edge_moe_forward_mx(ctypes.byref(dims), base, base, base, ctypes.byref(W), base, base,
+                                 1 << 40, None, None)
+    assert st == em.EDGE_MOE_EUNSUPPORTED
+    W2 = em.CWeightsMX(*([base] * 15 + [base + 8]))       # misaligned LoRA factor
+    st = lib.edge_moe_forward_mx(ctypes.byref(em.cdims(D)), base, base, base, ctypes.byref(W2), base, base,
+                                 1 << 40, None, None)
+    assert st == em.EDGE_MOE_EINVAL
+    st = lib.edge_moe_forward_mx(ctypes.byref(em.cdims(D)), base, base, base, ctypes.byref(W), base, base,
+                                 16, None, None)
+    assert st == em.EDGE_MOE_EWORKSPACE
