@@ -18,8 +18,11 @@ specification v1.0, whose definitions this module follows:
 Readings (each listed in the design notes, "MX variant"):
 
 * Weights (S_up, S_dn, A_up, B_up, A_dn, B_dn) are stored as MXFP4 along K
-  (two codes per byte, element 2i in the low nibble of byte i; E8M0 scales
-  [N][K/32]).  LoRA factors stay bf16.
+  (two codes per byte, element 2i in the low nibble of byte i); the E8M0
+  scales of an N x K matrix are stored K-step-major, [K/128][N][4]: for each
+  128-element step of K, the four block scales of every row in turn (the
+  layout the library's tiled products load one step at a time).  LoRA
+  factors stay bf16.
 * The inputs of the large MXFP4 products are quantised to MXFP8 (E4M3) along
   K first: the token rows x (for S_up and A_up) and the activation rows a (for
   S_dn and A_dn), where the matrix cores multiply FP4 by FP8.  The rank-r
@@ -129,13 +132,21 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def scales_by_row(scales: np.ndarray) -> np.ndarray:
+    """E8M0 scales stored [K/128][N][4] -> [N][K/32] (row n's block scales in K order)."""
+    s = np.asarray(scales)
+    steps, N, four = s.shape
+    assert four == 4
+    return np.transpose(s, (1, 0, 2)).reshape(N, 4 * steps)
+
+
 def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
-    """MXFP4 matrix [N][K/2] codes + [N][K/32] E8M0 -> float64 [N][K], exactly
-    (every E2M1 value times a power of two is a float64)."""
+    """MXFP4 matrix [N][K/2] codes + E8M0 scales [K/128][N][4] -> float64
+    [N][K], exactly (every E2M1 value times a power of two is a float64)."""
     c = unpack_fp4(packed)
-    assert c.shape[-1] == K and K % MX_BLOCK == 0
+    assert c.shape[-1] == K and K % 128 == 0
     vals = e2m1_to_f64(c)
-    sc = e8m0_to_f64(scales)
+    sc = e8m0_to_f64(scales_by_row(scales))
     return vals * np.repeat(sc, MX_BLOCK, axis=-1)
 
 

@@ -109,11 +109,13 @@ EM_DEV uint32_t amax16(const uint4& a, const uint4& b) {
 
 // ------------------------------------------------------------------ quantiser --
 // One thread per block of 32 (64 bytes in, 32 + 1 out).  src rows are
-// contiguous with K a multiple of 32, so block b starts at element 32 b.
+// contiguous with K a multiple of 128, so block b (row b / nkb, block b % nkb)
+// starts at element 32 b; its scale goes to the K-step-major array
+// [K/128][rows][4].
 __global__ void __launch_bounds__(256)
-mx_quant(const uint16_t* __restrict__ src, int64_t nblk, uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+mx_quant(const uint16_t* __restrict__ src, int64_t rows, int nkb, uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
     const int64_t b = blockIdx.x * 256ll + threadIdx.x;
-    if (b >= nblk) return;
+    if (b >= rows * nkb) return;
     const uint4* p = reinterpret_cast<const uint4*>(src + b * 32);
     const uint4 v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
     const int X = block_exp(max(amax16(v0, v1), amax16(v2, v3)));
@@ -121,20 +123,25 @@ mx_quant(const uint16_t* __restrict__ src, int64_t nblk, uint8_t* __restrict__ q
     uint4* o = reinterpret_cast<uint4*>(q + b * 32);
     o[0] = make_uint4(e4m3x4(v0.x, v0.y, inv), e4m3x4(v0.z, v0.w, inv), e4m3x4(v1.x, v1.y, inv), e4m3x4(v1.z, v1.w, inv));
     o[1] = make_uint4(e4m3x4(v2.x, v2.y, inv), e4m3x4(v2.z, v2.w, inv), e4m3x4(v3.x, v3.y, inv), e4m3x4(v3.z, v3.w, inv));
-    sc[b] = (uint8_t)X;
+    const int64_t row = b / nkb;
+    const int kb = (int)(b % nkb);
+    sc[((int64_t)(kb >> 2) * rows + row) * 4 + (kb & 3)] = (uint8_t)X;
 }
 
 // ------------------------------------------------------------------ the GEMM ---
 namespace {
 
 enum MxMode { MX_HS = 0, MX_OUT = 1, MX_Z1 = 2, MX_Z2 = 3 };
-constexpr int MBM = 128, MBK = 128, MX_TH = 512, MX_STAGES = 4;
+constexpr int MBM = 128, MBK = 128, MX_TH = 512;
 
-// Waves are 2 (rows) x 4 (columns); each takes 64 rows x BN / 4 columns.
+// Waves are 2 (rows) x 4 (columns); each takes 64 rows x BN / 4 columns.  The
+// shared products tile 512 columns, so that each activation tile read from
+// the L2 feeds 512 columns, with three stages (loads two steps ahead); the
+// rank-128 inputs tile their 128 columns with four stages.
 template <int MODE>
 struct MxCfg {
     static constexpr bool Z = MODE == MX_Z1 || MODE == MX_Z2;
-    static constexpr int BN = Z ? 128 : 256;
+    static constexpr int BN = Z ? 128 : 512;
     static constexpr int WN = BN / 4;
     static constexpr int NJ = WN / 16;
     static constexpr int NI = 4;
@@ -142,7 +149,9 @@ struct MxCfg {
     static constexpr int B_B = BN * (MBK / 2);     // E2M1 tile
     static constexpr int AS_B = MBM * 4, BS_B = BN * 4;
     static constexpr int STAGE = A_B + B_B + AS_B + BS_B;
+    static constexpr int STAGES = Z ? 4 : 3;
     static constexpr int B_INSTR = BN / 16 / 8;    // 16-byte weight loads per wave per stage
+    static constexpr int BS_W0 = Z ? 2 : 0;        // first wave of the BN / 64 weight-scale loads
 };
 
 struct MxTile { int g, r0, r1, n0; };
@@ -191,18 +200,20 @@ EM_DEV bool mx_tile(const LayerArgs& a, int b, int ntn, MxTile& t) {
 //   B: round q of wave w covers columns 16 (B_INSTR w + q) .. + 15; lane l
 //      writes slot l % 4 of column 16 (..) + l / 4, fetching segment
 //      (l % 4) ^ ((col >> 2) & 3).
-//   Scales: waves 0, 1 fetch the A rows' four scale bytes (one word per row);
-//      waves 2 .. 2 + BN / 64 - 1 the B columns'.
+//   Scales (stored K-step-major, [K/128][rows][4], so one step's words of
+//      consecutive rows are consecutive): waves 0, 1 fetch the A rows' words;
+//      waves BS_W0 .. BS_W0 + BN / 64 - 1 the B columns'.
 template <int MODE>
 struct MxSrc {
     const uint8_t* a[2];     // A row (with segment) per round, at K = 0
     const uint8_t* b[MxCfg<MODE>::B_INSTR];
-    const uint8_t* s;        // this wave's scale word source at K = 0 (or null)
-    int s_is_a;
+    const uint8_t* as;       // A-scale word of this lane at K step 0 (waves 0, 1), else null
+    const uint8_t* bs;       // B-scale word of this lane at K step 0, or null
+    size_t as_step, bs_step; // bytes between K steps
 };
 
 template <int MODE>
-EM_DEV void mx_fetch(uint8_t* stage, const MxSrc<MODE>& src, int k0) {
+EM_DEV void mx_fetch(uint8_t* stage, const MxSrc<MODE>& src, int ks) {
     using C = MxCfg<MODE>;
     const int w = wave_id();
     uint8_t* As = stage;
@@ -211,15 +222,17 @@ EM_DEV void mx_fetch(uint8_t* stage, const MxSrc<MODE>& src, int k0) {
     uint8_t* BS = AS + C::AS_B;
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.a[q] + k0), (lds_ptr_t)(As + (8 * (2 * w + q)) * MBK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.a[q] + (size_t)ks * MBK),
+                                         (lds_ptr_t)(As + (8 * (2 * w + q)) * MBK), 16, 0, 0);
 #pragma unroll
     for (int q = 0; q < C::B_INSTR; ++q)
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[q] + (k0 >> 1)),
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[q] + (size_t)ks * (MBK / 2)),
                                          (lds_ptr_t)(Bs + 16 * (C::B_INSTR * w + q) * (MBK / 2)), 16, 0, 0);
-    if (src.s) {
-        uint8_t* dst = src.s_is_a ? AS + 64 * 4 * w : BS + 64 * 4 * (w - 2);
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + (k0 >> 5)), (lds_ptr_t)dst, 4, 0, 0);
-    }
+    if (src.as)
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.as + ks * src.as_step), (lds_ptr_t)(AS + 256 * w), 4, 0, 0);
+    if (src.bs)
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.bs + ks * src.bs_step),
+                                         (lds_ptr_t)(BS + 256 * (w - C::BS_W0)), 4, 0, 0);
 }
 
 template <int MODE>
@@ -263,6 +276,7 @@ EM_DEV void wait_vm_n(int n) {
         case 4: wait_vm<4>(); break;
         case 5: wait_vm<5>(); break;
         case 6: wait_vm<6>(); break;
+        case 7: wait_vm<7>(); break;
         case 8: wait_vm<8>(); break;
         case 10: wait_vm<10>(); break;
         default: wait_vm<0>(); break;
@@ -276,7 +290,8 @@ __global__ void __launch_bounds__(MX_TH)
 mx_gemm(LayerArgs a) {
     using C = MxCfg<MODE>;
     constexpr int BN = C::BN, WN = C::WN, NI = C::NI, NJ = C::NJ;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MX_STAGES * C::STAGE];
+    constexpr int STAGES = C::STAGES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * C::STAGE];
     const int ntn = C::Z ? 1 : (MODE == MX_HS ? a.h : a.d) / BN;
     // XCD-aware order: XCD x = blockIdx % 8 takes tiles [x * per, (x + 1) * per)
     const int per = gridDim.x >> 3;
@@ -312,15 +327,15 @@ mx_gemm(LayerArgs a) {
         const int col = 16 * (C::B_INSTR * wv + q) + (l >> 2);
         src.b[q] = Wt + (size_t)col * (K / 2) + 16 * ((l & 3) ^ ((col >> 2) & 3));
     }
-    src.s = nullptr;
-    src.s_is_a = 0;
-    if (wv < 2) {
-        src.s = AE + a_row(64 * wv + l) * (K / 32);
-        src.s_is_a = 1;
-    } else if (wv < 2 + BN / 64) {
-        src.s = WE + ((size_t)t.g * N + t.n0 + 64 * (wv - 2) + l) * (K / 32);
-    }
-    const int per_stage = 2 + C::B_INSTR + (src.s ? 1 : 0);     // this wave's loads per stage
+    // scale words: activations [K/128][rows][4] (rows of x for HS / Z1, of a
+    // for Z2 / OUT), weights [lead][K/128][N][4]
+    const int64_t a_rows = (MODE == MX_HS || MODE == MX_Z1) ? a.T : a.rmax;
+    src.as = wv < 2 ? AE + a_row(64 * wv + l) * 4 : nullptr;
+    src.as_step = (size_t)a_rows * 4;
+    const int bsw = wv - C::BS_W0;
+    src.bs = (bsw >= 0 && bsw < BN / 64) ? WE + ((size_t)t.g * (K / 128) * N + t.n0 + 64 * bsw + l) * 4 : nullptr;
+    src.bs_step = (size_t)N * 4;
+    const int per_stage = 2 + C::B_INSTR + (src.as ? 1 : 0) + (src.bs ? 1 : 0);   // this wave's loads per stage
 
     floatx4 acc[NI][NJ];
 #pragma unroll
@@ -328,17 +343,17 @@ mx_gemm(LayerArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
 
-    // ---- main loop: four stages, loads three K steps ahead of the math
+    // ---- main loop: loads STAGES - 1 K steps ahead of the math
     const int nk = K / MBK;
-    for (int s = 0; s < MX_STAGES - 1 && s < nk; ++s) mx_fetch<MODE>(lds + s * C::STAGE, src, s * MBK);
-    wait_vm_n(per_stage * (min(nk, MX_STAGES - 1) - 1));
+    for (int s = 0; s < STAGES - 1 && s < nk; ++s) mx_fetch<MODE>(lds + s * C::STAGE, src, s);
+    wait_vm_n(per_stage * (min(nk, STAGES - 1) - 1));
     __syncthreads();
     for (int ks = 0; ks < nk; ++ks) {
-        const int ahead = ks + MX_STAGES - 1;
-        if (ahead < nk) mx_fetch<MODE>(lds + (ahead % MX_STAGES) * C::STAGE, src, ahead * MBK);
-        mx_compute<MODE>(acc, lds + (ks % MX_STAGES) * C::STAGE);
+        const int ahead = ks + STAGES - 1;
+        if (ahead < nk) mx_fetch<MODE>(lds + (ahead % STAGES) * C::STAGE, src, ahead);
+        mx_compute<MODE>(acc, lds + (ks % STAGES) * C::STAGE);
         // the next step's loads must have landed: the later ones may stay in flight
-        const int later = min(nk - 1, ks + MX_STAGES - 1) - (ks + 1);
+        const int later = min(nk - 1, ks + STAGES - 1) - (ks + 1);
         wait_vm_n(per_stage * max(later, 0));
         __syncthreads();
     }
@@ -392,12 +407,6 @@ mx_gemm(LayerArgs a) {
             const int p = max(a.db.eoff[e], t.r0) - t.r0;          // tile rows [p, q) are expert e's
             const int q = min(a.db.eoff[e + 1], t.r1) - t.r0;
             if (p >= q) continue;
-            uint4 bq[NJ][4];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const size_t n = (size_t)e * a.d + t.n0 + WN * wn + 16 * j + m;
-                fp4_block_bf16(ld16(a.b_dn + n * (KC / 2) + 16 * g), a.b_dn_e[n * (KC / 32) + g], bq[j]);
-            }
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int rl = 64 * wm + 16 * i;                    // subtile rows [rl, rl + 16)
@@ -409,9 +418,14 @@ mx_gemm(LayerArgs a) {
 #pragma unroll
                 for (int st = 0; st < 4; ++st) af[st] = mine ? ld16(zr + 8 * st) : zero_u4();
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
+                for (int j = 0; j < NJ; ++j) {                      // one column subtile's operands at a time
+                    uint4 bq[4];
+                    const size_t n = (size_t)e * a.d + t.n0 + WN * wn + 16 * j + m;
+                    fp4_block_bf16(ld16(a.b_dn + n * (KC / 2) + 16 * g), a.b_dn_e[n * (KC / 32) + g], bq);
 #pragma unroll
-                    for (int st = 0; st < 4; ++st) acc[i][j] = mfma_bf16(af[st], bq[j][st], acc[i][j]);
+                    for (int st = 0; st < 4; ++st) acc[i][j] = mfma_bf16(af[st], bq[st], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     }
@@ -512,7 +526,7 @@ mx_act(LayerArgs a) {
             *reinterpret_cast<uint4*>(a.aq + row * a.h + col) =
                 make_uint4(e4m3x4(w0.x, w0.y, inv), e4m3x4(w0.z, w0.w, inv), e4m3x4(w1.x, w1.y, inv),
                            e4m3x4(w1.z, w1.w, inv));
-            if ((tq & 1) == 0) a.as[row * (a.h / 32) + col / 32] = (uint8_t)X;
+            if ((tq & 1) == 0) a.as[((size_t)(col >> 7) * a.rmax + row) * 4 + ((col >> 5) & 3)] = (uint8_t)X;
         }
         __syncthreads();
     }
@@ -521,15 +535,15 @@ mx_act(LayerArgs a) {
 // ------------------------------------------------------------------ host side ---
 
 bool mx_layer_ok(int d, int h, int r, int rL) {
-    return r == KC && d % 256 == 0 && h % 256 == 0 && d >= 256 && h >= 256 && rL % 8 == 0 && rL >= 8 && rL <= 32;
+    return r == KC && d % 512 == 0 && h % 512 == 0 && rL % 8 == 0 && rL >= 8 && rL <= 32;
 }
 
-static hipError_t launch_quant(const uint16_t* src, int64_t n_elems, uint8_t* q, uint8_t* sc, hipStream_t s,
+static hipError_t launch_quant(const uint16_t* src, int64_t rows, int K, uint8_t* q, uint8_t* sc, hipStream_t s,
                                const char* name) {
-    const int64_t nblk = n_elems / 32;
+    const int64_t nblk = rows * (K / 32);
     if (nblk == 0) return hipSuccess;
     prof_begin(s);
-    mx_quant<<<(unsigned)((nblk + 255) / 256), 256, 0, s>>>(src, nblk, q, sc);
+    mx_quant<<<(unsigned)((nblk + 255) / 256), 256, 0, s>>>(src, rows, K / 32, q, sc);
     prof_end(s, name);
     return hipGetLastError();
 }
@@ -552,7 +566,7 @@ static hipError_t launch_gemm_mx(const LayerArgs& a, int64_t max_rows, hipStream
 
 // The layer after the dispatch kernels: every stage of the MX variant.
 hipError_t launch_mx_layer(const LayerArgs& a, hipStream_t s) {
-    hipError_t e = launch_quant(a.x, (int64_t)a.T * a.d, a.xq, a.xs, s, "mx_quant_x");
+    hipError_t e = launch_quant(a.x, a.T, a.d, a.xq, a.xs, s, "mx_quant_x");
     if (e == hipSuccess) e = launch_gemm_mx<MX_Z1>(a, a.rmax, s, "mx_z1");
     if (e != hipSuccess) return e;
     launch_lora_in(a, 0, s);

@@ -293,12 +293,19 @@ def quantize_mxfp4_torch(w):
     return packed.contiguous(), X.to(torch.uint8).contiguous()
 
 
+def mx_scales_by_step(X):
+    """E8M0 bytes [..., N, K/32] -> the stored K-step-major layout [..., K/128, N, 4]."""
+    lead, N, nb = X.shape[:-2], X.shape[-2], X.shape[-1]
+    assert nb % 4 == 0
+    return X.reshape(*lead, N, nb // 4, 4).transpose(-3, -2).contiguous()
+
+
 def _mxfp4_tensor(name, shape, cfg_id, layer, seed, device, zero=False):
     import torch
     if zero:
         K = shape[-1]
         return (torch.zeros(*shape[:-1], K // 2, dtype=torch.uint8, device=device),
-                torch.zeros(*shape[:-1], K // MX_BLOCK, dtype=torch.uint8, device=device))
+                torch.zeros(shape[0], K // 128, shape[1], 4, dtype=torch.uint8, device=device))
     g = torch.Generator(device=device)
     g.manual_seed(_torch_seed(cfg_id, layer, name, seed))
     qs, ss = [], []
@@ -306,7 +313,7 @@ def _mxfp4_tensor(name, shape, cfg_id, layer, seed, device, zero=False):
         w = torch.randn(*shape[1:], generator=g, device=device, dtype=torch.float32) * WEIGHT_STD
         q, s = quantize_mxfp4_torch(w)
         qs.append(q)
-        ss.append(s)
+        ss.append(mx_scales_by_step(s))
     return torch.stack(qs).contiguous(), torch.stack(ss).contiguous()
 
 
@@ -314,8 +321,9 @@ def make_weights_mx(cfg_id: int, seed: int, layer: int = 0, device="cpu",
                     zero_delta: bool = False, zero_lora: bool = False) -> dict:
     """The MXFP4 variant of make_weights: the same draws (same streams, same
     N(0, 0.02^2)), rounded to MXFP4 instead of int4.  Layouts: codes as the
-    int4 ones ([N][K/2], two per byte), E8M0 scales uint8 [N][K/32] under the
-    same "_scale" names; LoRA factors bf16 as in make_weights."""
+    int4 ones ([N][K/2], two per byte), E8M0 scales uint8 stored K-step-major
+    [K/128][N][4] under the same "_scale" names; LoRA factors bf16 as in
+    make_weights."""
     D = CONFIGS[cfg_id].dims
     G, E, d, h, r, rL = D.n_groups, D.n_experts, D.d, D.h, D.delta_rank, D.lora_rank
     out = {}

@@ -84,12 +84,28 @@ def test_unpack_fp4_nibble_order():
 
 
 def test_dequant_mxfp4_every_code_and_scale():
-    codes = np.arange(32) % 16                             # two rows of all 16 codes per block
+    codes = np.arange(128) % 16                            # all 16 codes in every block
     packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    table = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6] * 8)
     for X in (0, 100, 127, 130, 254):
-        got = mx.dequant_mxfp4(packed, np.array([[X]]), 32)[0]
-        want = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6] * 2) * 2.0 ** (X - 127)
-        assert np.array_equal(got, want)
+        got = mx.dequant_mxfp4(packed, np.full((1, 1, 4), X), 128)[0]
+        assert np.array_equal(got, table * 2.0 ** (X - 127))
+
+
+def test_scale_layout_k_step_major():
+    """Stored [K/128][N][4]: row n's block b scale sits at [b // 4][n][b % 4]."""
+    N, K = 3, 256
+    sc = np.zeros((K // 128, N, 4), dtype=np.int64)
+    for n in range(N):
+        for b in range(K // 32):
+            sc[b // 4, n, b % 4] = 100 + 10 * n + b
+    rows = mx.scales_by_row(sc)
+    assert rows.tolist() == [[100 + 10 * n + b for b in range(K // 32)] for n in range(N)]
+    packed = np.full((N, K // 2), 0x22, dtype=np.uint8)          # every element 1.0
+    w = mx.dequant_mxfp4(packed, sc, K)
+    for n in range(N):
+        for b in range(K // 32):
+            assert np.all(w[n, 32 * b:32 * b + 32] == 2.0 ** (100 + 10 * n + b - 127))
 
 
 def test_block_scale_range():
@@ -202,7 +218,7 @@ def _mx_diag_weights(n, diag):
         if name in diag:
             codes[np.arange(n), np.arange(n)] = diag[name]
         W[name] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)[None]
-        W[name + "_scale"] = np.full((1, n, n // 32), 127, dtype=np.int64)
+        W[name + "_scale"] = np.full((1, n // 128, n, 4), 127, dtype=np.int64)
     for name in ("lora_up_u", "lora_up_v", "lora_dn_u", "lora_dn_v"):
         W[name] = np.zeros((1, n, 8) if name.endswith("_v") else (1, 8, n), dtype=np.uint16)
     return W
@@ -211,7 +227,7 @@ def _mx_diag_weights(n, diag):
 def test_mx_quantiser_points_shared_path():
     """S_up = S_dn = I, no delta, no LoRA: h = Q(x), o = Q(R3(SiLU(Q(x))))."""
     rng = np.random.default_rng(17)
-    n, T = 64, 3
+    n, T = 128, 3
     W = _mx_diag_weights(n, {"s_up": 2, "s_dn": 2})
     x = bf16_from(rng.standard_normal((T, n)) * 3)
     idx = np.zeros((T, 1), dtype=np.int64)
@@ -227,7 +243,7 @@ def test_mx_quantiser_points_delta_path():
     = 1.5 Q(x) exactly, h = z1 (z1 meets B_up unquantised, although Q(z1) != z1),
     a = R3(SiLU(h)), z2 = R4(1.5 Q(a)) = 1.5 Q(a), o = z2."""
     rng = np.random.default_rng(19)
-    n, T = 64, 3
+    n, T = 128, 3
     W = _mx_diag_weights(n, {"a_up": 3, "b_up": 2, "a_dn": 3, "b_dn": 2})
     x = bf16_from(rng.standard_normal((T, n)) * 3)
     idx = np.zeros((T, 1), dtype=np.int64)
@@ -250,7 +266,7 @@ def test_mx_lora_takes_unquantised_inputs():
     coordinates (bf16 identity blocks): zl = x[:8], h[:8] = x[:8],
     zl2 = a[:8], o[:8] = a[:8]: the LoRA branch sees x and a, not Q(x), Q(a)."""
     rng = np.random.default_rng(23)
-    n, T, rL = 64, 3, 8
+    n, T, rL = 128, 3, 8
     W = _mx_diag_weights(n, {})
     eye_u = np.zeros((1, rL, n), dtype=np.float32)
     eye_u[0, np.arange(rL), np.arange(rL)] = 1.0
@@ -280,7 +296,7 @@ def test_synth_mxfp4_rounding_is_nearest():
     w[1, 6] = 0.012                                          # block max: X = floor(log2 .012) - 2 + 127 = 118
     w[1, 5] = 2.5 * 2.0 ** -9                                # then w / 2^-9 = 2.5, a tie between 2 and 3
     q, X = synth.quantize_mxfp4_torch(w)
-    vals = mx.dequant_mxfp4(q.numpy(), X.numpy(), 256)
+    vals = mx.dequant_mxfp4(q.numpy(), synth.mx_scales_by_step(X).numpy(), 256)
     wn = w.double().numpy()
     grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
     for n in range(4):
