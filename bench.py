@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8
 METRIC = "MoE-layer tokens/s at T=8 verify & 16K prefill; % peak HBM GB/s / % MFMA"
 
 
@@ -129,7 +130,7 @@ def step_bytes(D, idx):
 def step_flops(D, idx):
     """Algorithmic MFMA flops of one layer step: every stage once (the pf_* and
     gemm_* names of kernel_flops are two implementations of the same stages)."""
-    return sum(v for k, v in kernel_flops(D, idx).items() if not k.startswith("pf_"))
+    return sum(v for k, v in kernel_flops(D, idx).items() if not k.startswith(("pf_", "mx_")))
 
 
 def kernel_flops(D, idx):
@@ -152,13 +153,18 @@ def kernel_flops(D, idx):
         "pf_shared_up": 2 * U * h * d + 2 * U * h * rL,
         "pf_delta_up_act": 2 * R * h * r,
         "pf_down": 2 * R * d * h + 2 * R * d * r + 2 * R * d * rL,
+        # the MX variant's kernels (same products)
+        "mx_z1": 2 * R * r * d,
+        "mx_shared_up": 2 * U * h * d + 2 * U * h * rL,
+        "mx_z2": 2 * R * r * h,
+        "mx_down": 2 * R * d * h + 2 * R * d * r + 2 * R * d * rL,
     }
 
 
 # ---------------------------------------------------------------- device workload ----
 
 class Workload:
-    def __init__(self, cfg_id, layers, seed=0, host_init=False):
+    def __init__(self, cfg_id, layers, seed=0, host_init=False, mx=False):
         import torch
         import shared_matrix_expert_amd as em
         import synth
@@ -166,6 +172,7 @@ class Workload:
         c = synth.config(cfg_id)
         self.D = c.dims
         self.cfg_id = cfg_id
+        self.mx = mx
         self.layers = []
         x = synth.make_activations(cfg_id, seed)
         self.x_host = x
@@ -176,10 +183,14 @@ class Workload:
                 "wr_host": wr, "bias_host": bias,
                 "wr": torch.from_numpy(wr.view(np.int16)).cuda(),
                 "bias": None if bias is None else torch.from_numpy(bias).cuda(),
-                "W": self._weights(synth, cfg_id, seed, layer, host_init, em, self.D),
+                "W": (self._weights_mx(synth, cfg_id, seed, layer, host_init) if mx else
+                      self._weights(synth, cfg_id, seed, layer, host_init, em, self.D)),
             })
         D = self.D
-        self.ws = torch.empty(em.edge_moe_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+        ws_bytes = em.edge_moe_workspace_bytes(D)
+        if mx:
+            ws_bytes = max(ws_bytes, em.edge_moe_workspace_bytes_mx(D))
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         self.idx = torch.empty(D.T, D.top_k, dtype=torch.int32, device="cuda")
         self.w = torch.empty(D.T, D.top_k, dtype=torch.float32, device="cuda")
         self.y = torch.empty(D.T, D.d, dtype=torch.float32, device="cuda")
@@ -199,13 +210,21 @@ class Workload:
             W = em.tile_weights(D, W)          # kinds 0-3: the decode kernels and the persistent launch
         return W
 
+    @staticmethod
+    def _weights_mx(synth, cfg_id, seed, layer, host_init):
+        if not host_init:
+            return synth.make_weights_mx(cfg_id, seed, layer, device="cuda")
+        return {k: v.cuda() for k, v in synth.make_weights_mx(cfg_id, seed, layer, device="cpu").items()}
+
     persistent = False   # the layer through edge_moe_forward_persistent (one persistent launch)
 
     def step(self, i):
         L = self.layers[i % len(self.layers)]
         em, D = self.em, self.D
         em.edge_moe_route(D, self.x, L["wr"], L["bias"], self.idx, self.w, None, self.ws, self.stream)
-        if self.persistent:
+        if self.mx:
+            em.edge_moe_forward_mx(D, self.x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
+        elif self.persistent:
             em.edge_moe_forward_persistent(D, self.x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
         else:
             em.edge_moe_forward(D, self.x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
@@ -272,7 +291,7 @@ def stored_traffic(kernel: str, workload_tag: str):
 
 # Library kernel names (the per-kernel event table) and their names in a
 # rocprofv3 kernel trace, for the kernels that can be a roofline's dominant one.
-TRACE_NAMES = {"dec_down_wst": "dec_down_ws<true>", "dec_down_ws": "dec_down_ws<false>", "dec_act": "dec_act<1>",
+TRACE_NAMES = {"mx_down": "mx_gemm<1>", "mx_shared_up": "mx_gemm<0>", "dec_down_wst": "dec_down_ws<true>", "dec_down_ws": "dec_down_ws<false>", "dec_act": "dec_act<1>",
                "dec_up_ws": "dec_up_ws", "dec_layer": "dec_layer<16>", "router_topk": "router_topk_split",
                "router_logits_split": "router_logits_split", "pf_down": "pf_gemm<1>",
                "pf_shared_up": "pf_gemm<0>", "pf_z1": "pf_gemm<2>", "pf_z2": "pf_gemm<3>",
@@ -317,14 +336,14 @@ def kernel_table(D, idxs, ktimes):
     return out
 
 
-def roofline_mfma(D, idxs, ktimes):
+def roofline_mfma(D, idxs, ktimes, peak=MFMA_BF16_PEAK_TFLOPS):
     fl = {k: np.mean([kernel_flops(D, ix).get(k, 0) for ix in idxs]) for k in ktimes}
     cand = {k: v for k, v in ktimes.items() if fl.get(k, 0) > 0}
     name = max(cand, key=lambda k: cand[k][0] * cand[k][1])
     avg_ms = ktimes[name][1]
     tf = fl[name] / (avg_ms * 1e-3) / 1e12
-    return name, {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                  "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+    return name, {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
+                  "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
                   "kernel": name, "avg_ms": round(avg_ms, 4), "flops_per_launch": int(fl[name])}
 
 
@@ -522,6 +541,36 @@ def calibrate(em, torch):
             "published": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS}}
 
 
+def mx_prefill_line(args):
+    """The same 16K prefill through the MX variant (MXFP4 shared and delta
+    matrices, MXFP8 activations on the scaled FP4 x FP8 matrix cores): tokens/s
+    and the dominant kernel against the dense FP8 peak (its large products run
+    at the FP8 rate)."""
+    import torch
+    log("building MX prefill workload ...")
+    wp = Workload(3, 1, host_init=args.host_init, mx=True)
+    pidx = wp.routed_indices()
+    psec = wp.time_steps(args.prefill_steps, 2)
+    pk = wp.kernel_times(args.prefill_steps)
+    for k, (n, ms) in sorted(pk.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        log(f"  MX prefill kernel {k:20s} launches {n:5d} avg {ms:9.3f} ms")
+    name, roof = roofline_mfma(wp.D, pidx, pk, peak=MFMA_FP8_PEAK_TFLOPS)
+    roof["dtype"] = "fp8 x fp4 (E4M3 activations, E2M1 weights, E8M0 block scales)"
+    add_rocprof(roof, "prefill_16k_mx")
+    total_fl = float(np.mean([step_flops(wp.D, ix) for ix in pidx]))
+    out = {"value": round(wp.D.T / psec, 1), "unit": "tokens/s", "steps": args.prefill_steps,
+           "ms_per_step": round(psec * 1e3, 3),
+           "workload": "prefill T=16384, one layer, MXFP4 weights (same draws as the int4 layer), "
+                       "router logits ~ N(0,1)",
+           "roofline": roof,
+           "step_mfma": {"flops_per_step": int(total_fl),
+                         "achieved_TFLOPs": round(total_fl / psec / 1e12, 2),
+                         "frac_of_fp8_peak": round(total_fl / psec / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4)}}
+    del wp
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,6 +584,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="skip the verify T=8 workload (profiling runs)")
     ap.add_argument("--no-calibrate", action="store_true")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MX-variant prefill line")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (counter calibration)")
@@ -673,6 +723,10 @@ def main():
         }
         if not args.no_cpu_baseline:
             line["prefill_16k"]["cpu_baseline"] = cpu_baseline_prefill(wp)
+        del wp
+        torch.cuda.empty_cache()
+        if not args.no_mx:
+            line["prefill_16k_mx"] = mx_prefill_line(args)
     if not args.no_calibrate:
         line["calibration"] = calibrate(em, torch)
         log(f"  calibration: {line['calibration']}")
