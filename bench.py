@@ -375,11 +375,40 @@ class Stack:
         self.xb = torch.empty_like(self.x0)
         self.stream = torch.cuda.current_stream()
         self.idxs = []
+        self.pf_stream = None
+        self.pf_ws = None
 
-    def step(self, record=False):
-        em, D = self.em, self.D
+    def predictions(self, hit_rate, seed=0):
+        """A synthetic stand-in for the prerouter head: for each layer, the groups
+        its recorded routing touched, each kept with probability hit_rate and
+        otherwise replaced by a group it did not touch (device int32 lists)."""
+        rng = np.random.default_rng(seed)
+        G = self.D.n_experts // self.D.experts_per_group
+        out = []
+        for ix in self.idxs:
+            true = sorted(set((ix // self.D.experts_per_group).ravel().tolist()))
+            other = [g for g in range(G) if g not in true]
+            pred = []
+            for g in true:
+                if rng.random() < hit_rate or not other:
+                    pred.append(g)
+                else:
+                    pred.append(other.pop(int(rng.integers(len(other)))))
+            out.append(self.torch.tensor(pred, dtype=self.torch.int32, device="cuda"))
+        return out
+
+    def step(self, record=False, prefetch=None, parts=1):
+        """One pass.  With prefetch (a device group list per layer), layer l+1's
+        predicted groups are read on a second stream, starting with layer l."""
+        em, D, torch = self.em, self.D, self.torch
         x = self.x0
         for li, L in enumerate(self.layers):
+            if prefetch is not None and li + 1 < self.n_layers:
+                ev = torch.cuda.Event()
+                ev.record(self.stream)
+                self.pf_stream.wait_event(ev)
+                em.edge_moe_prefetch(D, self.layers[li + 1]["W"], prefetch[li + 1], parts, self.pf_ws,
+                                     self.pf_stream)
             em.edge_moe_route(D, x, L["wr"], None, self.idx, self.w, None, self.ws, self.stream)
             em.edge_moe_forward(D, x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
             if record:
@@ -400,6 +429,30 @@ class Stack:
             self.step()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
+
+    def final_x(self):
+        return self.xa if (self.n_layers - 1) % 2 == 0 else self.xb
+
+    def time_prefetch(self, steps, hit_rate, parts=1):
+        """Passes with the next layer's predicted shared matrices read ahead on
+        a second stream (default priority); returns (seconds per pass, whether
+        the output equals the plain pass bitwise)."""
+        torch = self.torch
+        if self.pf_stream is None:
+            self.pf_stream = torch.cuda.Stream()
+            self.pf_ws = torch.empty(self.em.edge_moe_prefetch_ws_bytes(), dtype=torch.uint8, device="cuda")
+        pred = self.predictions(hit_rate)
+        self.step()
+        torch.cuda.synchronize()
+        ref = self.final_x().clone()
+        self.step(prefetch=pred, parts=parts)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(ref, self.final_x()))
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(prefetch=pred, parts=parts)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps, same
 
     def time_graph(self, steps):
         """The same pass captured once as a HIP graph (48 x (route, layer,
@@ -697,6 +750,15 @@ def main():
                                      "ms_per_step": round(gsec * 1e3, 4), "equals_eager": gsame,
                                      "what": "the same pass captured once as a HIP graph and replayed"}
         log(f"  stack, HIP graph: {gsec * 1e3:.3f} ms per replay, equal to eager: {gsame}")
+        pf = {}
+        for hit, parts in ((1.0, 1), (0.5, 1), (1.0, 3)):
+            psec, psame = st.time_prefetch(args.stack_steps, hit, parts)
+            key = f"hit{hit:.1f}_{'s_up' if parts == 1 else 's_up+s_dn'}"
+            pf[key] = {"value": round(st.D.T / psec, 1), "ms_per_step": round(psec * 1e3, 4), "equals_plain": psame}
+            log(f"  stack, prefetch {key}: {psec * 1e3:.3f} ms per pass, equal to plain: {psame}")
+        line["stack_48"]["prefetch"] = dict(pf, what="layer l+1's predicted groups' shared matrices read on a "
+                                                    "second stream while layer l runs (synthetic predictor with "
+                                                    "the stated hit rate)")
         del st
         torch.cuda.empty_cache()
 

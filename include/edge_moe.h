@@ -208,6 +208,26 @@ int edge_moe_forward_traced(const edge_moe_dims* dims, const uint16_t* x,
 int edge_moe_forward_noalloc(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                              const float* topk_w, const edge_moe_weights* weights, float* y, void* stream);
 
+/* Next-layer prefetch (the prerouter idea: a light predictor names the next
+ * layer's experts one step ahead so that their weights can be fetched while
+ * the current layer computes; byteiota "Edge0-145B: Run a 145B Open-Source
+ * Model on Your Laptop", The Three Pillars, Prerouter paragraph).  Reads the
+ * shared matrices of the listed groups of one layer once, computing nothing,
+ * so that a later layer call can find them in the GPU's memory-side cache.
+ * Results of every other call are unchanged by it.
+ *   groups   device int32[n_groups], the predicted groups (entries outside
+ *            0..G-1 are skipped; duplicates are read twice)
+ *   parts    bit 0: S_up (codes, or its decode-tiled copy when weights has
+ *            one, and scales); bit 1: S_dn likewise
+ *   ws       device scratch of at least edge_moe_prefetch_ws_bytes() bytes,
+ *            written (no meaning) by the call
+ * Meant to run on a second stream of default priority beside the layer;
+ * asynchronous.  EDGE_MOE_EINVAL for bad pointers, n_groups < 0 or
+ * n_groups > 4 G, parts outside 1..3. */
+size_t edge_moe_prefetch_ws_bytes(void);
+int edge_moe_prefetch(const edge_moe_dims* dims, const edge_moe_weights* weights, const int32_t* groups,
+                      int32_t n_groups, int32_t parts, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- MX variant --
  * The expert layer with its six large matrices in MXFP4 instead of int4: the
  * microscaling format of the Open Compute Project's MX specification v1.0,

@@ -30,7 +30,8 @@ EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_abi_version", "edge_moe_copy", "edge_moe_tile_shared",
             "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset",
             "edge_moe_forward_noalloc", "edge_moe_forward_persistent", "edge_moe_mfma_peak",
-            "edge_moe_workspace_bytes_mx", "edge_moe_forward_mx")
+            "edge_moe_workspace_bytes_mx", "edge_moe_forward_mx", "edge_moe_prefetch_ws_bytes",
+            "edge_moe_prefetch")
 
 
 class CDims(ctypes.Structure):
@@ -107,6 +108,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_moe_forward_persistent.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights),
                                                 vp, vp, sz, vp, ctypes.POINTER(CTrace)]
     lib.edge_moe_forward_persistent.restype = i32
+    lib.edge_moe_prefetch_ws_bytes.argtypes = []
+    lib.edge_moe_prefetch_ws_bytes.restype = sz
+    lib.edge_moe_prefetch.argtypes = [ctypes.POINTER(CDims), ctypes.POINTER(CWeights), vp, i32, i32, vp, sz, vp]
+    lib.edge_moe_prefetch.restype = i32
     lib.edge_moe_workspace_bytes_mx.argtypes = [ctypes.POINTER(CDims)]
     lib.edge_moe_workspace_bytes_mx.restype = sz
     lib.edge_moe_forward_mx.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeightsMX),
@@ -165,6 +170,21 @@ def cweights_mx(weights: dict) -> CWeightsMX:
     """Struct of an MX weight dict (keys as the int4 ones: codes under the
     matrix name, E8M0 bytes under "<name>_scale")."""
     return CWeightsMX(*(_ptr(weights[k]) for k in _WEIGHT_KEYS[:16]))
+
+
+def edge_moe_prefetch_ws_bytes() -> int:
+    return int(load().edge_moe_prefetch_ws_bytes())
+
+
+def edge_moe_prefetch(dims, weights, groups, parts, ws, stream=None) -> None:
+    """Read the listed groups' shared matrices (parts: 1 S_up, 2 S_dn, 3 both)
+    so that a later layer call finds them in the memory-side cache."""
+    n = 0 if groups is None else int(groups.numel())
+    st = load().edge_moe_prefetch(ctypes.byref(cdims(dims)), ctypes.byref(cweights(weights)),
+                                  _ptr(groups) if n else None, n, int(parts), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    if st != EDGE_MOE_OK:
+        raise EdgeMoeError("edge_moe_prefetch", st)
 
 
 def edge_moe_workspace_bytes_mx(dims) -> int:

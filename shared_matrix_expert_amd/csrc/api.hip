@@ -496,6 +496,45 @@ static int forward_impl(const edge_moe_dims* dims, const uint16_t* x, const int3
     return EDGE_MOE_OK;
 }
 
+// ---------------------------------------------------------------- prefetch ----
+size_t edge_moe_prefetch_ws_bytes(void) { return (size_t)em::kPrefetchBlocks * 256 * 4; }
+
+int edge_moe_prefetch(const edge_moe_dims* dims, const edge_moe_weights* wt, const int32_t* groups,
+                      int32_t n_groups, int32_t parts, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_dims(dims);
+    if (st != EDGE_MOE_OK) return st;
+    const edge_moe_dims& d = *dims;
+    const int G = d.n_experts / d.experts_per_group;
+    if (!wt || parts < 1 || parts > 3 || n_groups < 0 || n_groups > 4 * G) return EDGE_MOE_EINVAL;
+    if (n_groups > 0 && !aligned(groups, 4)) return EDGE_MOE_EINVAL;
+    if (!aligned(ws, 16)) return ws ? EDGE_MOE_EINVAL : EDGE_MOE_EWORKSPACE;
+    if (ws_bytes < edge_moe_prefetch_ws_bytes()) return EDGE_MOE_EWORKSPACE;
+    const uint8_t* up_q = wt->s_up_t ? wt->s_up_t : wt->s_up_q;
+    const uint8_t* dn_q = wt->s_dn_t ? wt->s_dn_t : wt->s_dn_q;
+    if (((parts & 1) && (!aligned(up_q, 16) || !aligned(wt->s_up_scale, 16))) ||
+        ((parts & 2) && (!aligned(dn_q, 16) || !aligned(wt->s_dn_scale, 16))))
+        return EDGE_MOE_EINVAL;
+    if (n_groups == 0) return EDGE_MOE_OK;
+    st = check_device();
+    if (st != EDGE_MOE_OK) return st;
+    const int gq_d = d.quant_group < d.d ? d.quant_group : d.d;
+    const int gq_h = d.quant_group < d.h ? d.quant_group : d.h;
+    const uint8_t* bases[4];
+    size_t bytes[4];
+    int n = 0;
+    if (parts & 1) {
+        bases[n] = up_q; bytes[n++] = (size_t)d.h * d.d / 2;
+        bases[n] = reinterpret_cast<const uint8_t*>(wt->s_up_scale); bytes[n++] = (size_t)d.h * (d.d / gq_d) * 2;
+    }
+    if (parts & 2) {
+        bases[n] = dn_q; bytes[n++] = (size_t)d.d * d.h / 2;
+        bases[n] = reinterpret_cast<const uint8_t*>(wt->s_dn_scale); bytes[n++] = (size_t)d.d * (d.h / gq_h) * 2;
+    }
+    const hipError_t e = em::launch_prefetch(bases, bytes, n, groups, n_groups, G, static_cast<uint32_t*>(ws),
+                                             em::kPrefetchBlocks, (hipStream_t)stream);
+    return e == hipSuccess ? EDGE_MOE_OK : EDGE_MOE_EHIP;
+}
+
 // ---------------------------------------------------------------- MX variant --
 // The general layout followed by the MXFP8 copies of the product inputs.
 struct MxLayout {

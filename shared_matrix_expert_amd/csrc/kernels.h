@@ -157,6 +157,9 @@ hipError_t launch_gather_x(const LayerArgs& a, int64_t umax, hipStream_t s);
 hipError_t launch_act(const LayerArgs& a, hipStream_t s);     // needs r == 128, h % 256 == 0
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 void launch_lora_in(const LayerArgs& a, int down, hipStream_t s);
+constexpr int kPrefetchBlocks = 128;      // workgroups of the prefetch launch (sink: 256 words each)
+hipError_t launch_prefetch(const uint8_t* const* bases, const size_t* group_bytes, int n_regions,
+                           const int32_t* groups, int n_groups, int G, uint32_t* sink, int blocks, hipStream_t s);
 hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
 bool mx_layer_ok(int d, int h, int r, int rL);
 hipError_t launch_mx_layer(const LayerArgs& a, hipStream_t s);

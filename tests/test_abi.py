@@ -209,3 +209,23 @@ def test_mx_shapes_and_validation_before_any_device_call():
     st = lib.edge_moe_forward_mx(ctypes.byref(em.cdims(D)), base, base, base, ctypes.byref(W), base, base,
                                  16, None, None)
     assert st == em.EDGE_MOE_EWORKSPACE
+
+
+def test_prefetch_validation_before_any_device_call():
+    D = synth.config(2).dims
+    lib = em.load()
+    base = 1 << 40
+    W = em.CWeights(*([base] * 16 + [None] * 4))
+    ws_n = em.edge_moe_prefetch_ws_bytes()
+    assert ws_n >= 64 * 1024
+    dims = ctypes.byref(em.cdims(D))
+    call = lambda groups, n, parts, ws, nbytes: lib.edge_moe_prefetch(dims, ctypes.byref(W), groups, n, parts,  # noqa: E731
+                                                                      ws, nbytes, None)
+    assert call(base, 4, 0, base, ws_n) == em.EDGE_MOE_EINVAL          # no part
+    assert call(base, 4, 4, base, ws_n) == em.EDGE_MOE_EINVAL          # unknown part
+    assert call(base, -1, 1, base, ws_n) == em.EDGE_MOE_EINVAL         # negative count
+    assert call(base, 33, 1, base, ws_n) == em.EDGE_MOE_EINVAL         # more than 4 G entries
+    assert call(base + 2, 4, 1, base, ws_n) == em.EDGE_MOE_EINVAL      # misaligned list
+    assert call(base, 4, 1, base, ws_n - 4) == em.EDGE_MOE_EWORKSPACE  # scratch too small
+    assert call(base, 4, 1, None, ws_n) == em.EDGE_MOE_EWORKSPACE
+    assert call(None, 0, 1, base, ws_n) == em.EDGE_MOE_OK              # nothing to read: no device call
