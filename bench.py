@@ -609,6 +609,7 @@ def mx_prefill_line(args):
         log(f"  MX prefill kernel {k:20s} launches {n:5d} avg {ms:9.3f} ms")
     name, roof = roofline_mfma(wp.D, pidx, pk, peak=MFMA_FP8_PEAK_TFLOPS)
     roof["dtype"] = "fp8 x fp4 (E4M3 activations, E2M1 weights, E8M0 block scales)"
+    roof["traffic"] = stored_traffic(name, "prefill_16k_mx")
     add_rocprof(roof, "prefill_16k_mx")
     total_fl = float(np.mean([step_flops(wp.D, ix) for ix in pidx]))
     out = {"value": round(wp.D.T / psec, 1), "unit": "tokens/s", "steps": args.prefill_steps,

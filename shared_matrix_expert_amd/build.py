@@ -32,16 +32,20 @@ KERNEL_SOURCES = (("dec_layer", "layer.hip"), ("pl_", "layer.hip"), ("dec_", "de
 
 
 def sources_digest(kernel: str = "") -> str:
-    """sha256 over the headers and either every source (no kernel given) or the
-    source file of `kernel`: identifies the code a stored profile was taken from."""
+    """sha256 over the library's internal headers and either every source and
+    the public header (no kernel given) or the source file of `kernel`:
+    identifies the code a stored profile was taken from.  Kernel sources do not
+    include the public header, so its text is left out of a kernel's digest."""
     import hashlib
     h = hashlib.sha256()
     headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    public = ["../../include/edge_moe.h"]
     if kernel:
         hit = [f for pre, f in KERNEL_SOURCES if kernel.startswith(pre)]
-        srcs = hit[:1] if hit else srcs
-    for f in headers + srcs + ["../../include/edge_moe.h"]:
+        if hit:
+            srcs, public = hit[:1], []
+    for f in headers + srcs + public:
         with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()

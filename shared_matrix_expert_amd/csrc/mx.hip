@@ -253,17 +253,25 @@ EM_DEV void mx_compute(floatx4 (&acc)[MxCfg<MODE>::NI][MxCfg<MODE>::NJ], const u
         bf[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         sb[j] = (int)__builtin_amdgcn_ubfe(BS[col], 8 * g, 8);
     }
-#pragma unroll
-    for (int i = 0; i < C::NI; ++i) {
+    auto frag = [&](int i, v8i& af, int& sa) {
         const int row = 64 * wm + 16 * i + m;
         const int sw = (row >> 1) & 7;
         const uint4 lo = *reinterpret_cast<const uint4*>(As + row * MBK + 16 * (g ^ sw));
         const uint4 hi = *reinterpret_cast<const uint4*>(As + row * MBK + 16 * ((4 + g) ^ sw));
-        const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const int sa = (int)__builtin_amdgcn_ubfe(AS[row], 8 * g, 8);
+        af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sa = (int)__builtin_amdgcn_ubfe(AS[row], 8 * g, 8);
+    };
+    v8i afc, afn;
+    int sac, san;
+    frag(0, afc, sac);
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+        if (i + 1 < C::NI) frag(i + 1, afn, san);
 #pragma unroll
         for (int j = 0; j < C::NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afc, bf[j], acc[i][j], 0, 4, 0, sac, 0, sb[j]);
+        afc = afn;
+        sac = san;
     }
 }
 

@@ -167,8 +167,10 @@ def counters(out_dir: str, kernels: list, cmd: str, title: str) -> str:
         m = {c: sum(acc[(d, c)] for d in dids) / len(dids) for c in ctrs}
         lines.append(f"| {k} | {len(dids)} | " + " | ".join(f"{m[c]:.4g}" for c in ctrs) + " |")
         row = []
-        if m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
-            row.append(("bf16 flops (MOPS x 512)", f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}"))
+        mops = {c[len("SQ_INSTS_VALU_MFMA_MOPS_"):]: v for c, v in m.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")}
+        if any(mops.values()):
+            parts = ", ".join(f"{t.lower()} {v * 512:.4g}" for t, v in mops.items() if v)
+            row.append(("matrix-core flops (MOPS x 512)", f"{sum(mops.values()) * 512:.4g} ({parts})"))
         if m.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in m:
             row.append(("SQ_INSTS_VALU / SQ_INSTS_MFMA",
                         f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.3f}"))
