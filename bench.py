@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8
+PCIE_PEAK_GBS = 64.0            # host link, PCIe 5.0 x16, one direction
 METRIC = "MoE-layer tokens/s at T=8 verify & 16K prefill; % peak HBM GB/s / % MFMA"
 
 
@@ -486,6 +487,227 @@ class Stack:
         return sec, same
 
 
+class StreamStack:
+    """Decode (T=1) through a stack of full-size layers whose per-expert tensors
+    live in pinned host memory and reach HBM through an LRU of S slots per group
+    and layer (edge_moe_cache_*); the shared matrices (with their decode-tiled
+    copies), the LoRA factors and the routers stay resident.  One step decodes a
+    new synthetic token through every layer: route, read the routed experts back
+    to the host, rename them to slots (the misses' copies go on the compute
+    stream), run the slot layer, add the residual.
+
+    With predict=True, layer l+1's experts are guessed while layer l runs, by
+    routing layer l's input through layer l+1's router (the next layer's own
+    router standing in for the pages' light prerouter head), and the guesses'
+    copies go on a second stream (default priority) so that they overlap layer
+    l's kernels; layer l+1 waits for them before its kernels start."""
+
+    def __init__(self, n_layers, slots_per_group, seed=0, n_tokens=512, host_init=False):
+        import torch
+        import shared_matrix_expert_amd as em
+        import synth
+        self.torch, self.em = torch, em
+        self.D = D = synth.config(1).dims
+        self.S = slots_per_group
+        self.n_layers = n_layers
+        self.xs = torch.from_numpy(synth.make_activations(1, seed + 7, T=n_tokens).view(np.int16)).cuda()
+        G = D.n_experts // D.experts_per_group
+        self.SD = em.slot_dims(D, self.S)
+        self.layers = []
+        keys = em.EXPERT_TENSOR_KEYS[:8]
+        for layer in range(n_layers):
+            wr, bias = synth.make_router(1, seed, layer)
+            W = Workload._weights(synth, 1, seed, layer, host_init, em, D)
+            W.pop("a_up_t", None)
+            W.pop("a_dn_t", None)
+            host = {k: W[k].cpu().pin_memory() for k in keys}
+            slots = {k: torch.empty((G * self.S,) + tuple(W[k].shape[1:]), dtype=W[k].dtype, device="cuda")
+                     for k in keys}
+            resident = W
+            self.layers.append({"wr": torch.from_numpy(wr.view(np.int16)).cuda(),
+                                "bias": None if bias is None else torch.from_numpy(bias).cuda(),
+                                "W": resident, "SW": em.slot_weights(W, slots),
+                                "cache": em.ExpertCache(D, self.S, host, slots), "slots": slots,
+                                "ready": torch.cuda.Event()})
+        self.expert_bytes_resident = sum(W[k].numel() * W[k].element_size() for k in keys)
+        self.slot_bytes = sum(v.numel() * v.element_size() for v in self.layers[0]["slots"].values())
+        self.ws = torch.empty(max(em.edge_moe_workspace_bytes(D), em.edge_moe_workspace_bytes(self.SD)),
+                              dtype=torch.uint8, device="cuda")
+        self.idx = torch.empty(1, D.top_k, dtype=torch.int32, device="cuda")
+        self.pidx = torch.empty(1, D.top_k, dtype=torch.int32, device="cuda")
+        self.w = torch.empty(1, D.top_k, dtype=torch.float32, device="cuda")
+        self.pw = torch.empty_like(self.w)
+        self.sidx = torch.empty_like(self.idx)
+        self.idx_h = torch.empty(2, D.top_k, dtype=torch.int32).pin_memory()
+        self.slot_h = torch.empty(1, D.top_k, dtype=torch.int32).pin_memory()
+        self.y = torch.empty(1, D.d, dtype=torch.float32, device="cuda")
+        self.xa = torch.empty(1, D.d, dtype=torch.int16, device="cuda")
+        self.xb = torch.empty_like(self.xa)
+        self.stream = torch.cuda.current_stream()
+        self.copy_stream = torch.cuda.Stream()
+        self.tok = 0
+
+    def drop_resident_experts(self):
+        """Free the resident copies of the expert tensors (kept until the
+        streamed pass has been checked against them)."""
+        for L in self.layers:
+            for k in self.em.EXPERT_TENSOR_KEYS[:8]:
+                L["W"].pop(k, None)
+        self.torch.cuda.empty_cache()
+
+    def step(self, predict=False, resident=False, stats=None):
+        em, D, torch = self.em, self.D, self.torch
+        x = self.xs[self.tok % self.xs.shape[0]:self.tok % self.xs.shape[0] + 1]
+        self.tok += 1
+        for li, L in enumerate(self.layers):
+            em.edge_moe_route(D, x, L["wr"], L["bias"], self.idx, self.w, None, self.ws, self.stream)
+            out = self.xa if li % 2 == 0 else self.xb
+            if resident:
+                em.edge_moe_forward(D, x, self.idx, self.w, L["W"], self.y, self.ws, self.stream)
+                em.edge_moe_residual(x, self.y, out, self.stream)
+                x = out
+                continue
+            nxt = self.layers[li + 1] if predict and li + 1 < self.n_layers else None
+            if nxt is not None:
+                em.edge_moe_route(D, x, nxt["wr"], nxt["bias"], self.pidx, self.pw, None, self.ws, self.stream)
+                self.idx_h[1].copy_(self.pidx[0], non_blocking=True)
+            self.idx_h[0].copy_(self.idx[0])                     # waits for the stream: routing is on the host now
+            # this layer's predicted copies land before any copy of the batch's
+            # misses (which may reuse a slot a prediction is still filling) and
+            # before its kernels
+            self.stream.wait_event(L["ready"])
+            st = L["cache"].map(self.idx_h[:1], self.slot_h, self.stream)
+            if stats is not None:
+                for k in st:
+                    stats[k] = stats.get(k, 0) + st[k]
+            self.sidx.copy_(self.slot_h, non_blocking=True)
+            em.edge_moe_forward(self.SD, x, self.sidx, self.w, L["SW"], self.y, self.ws, self.stream)
+            if nxt is not None:
+                # layer l+1's slots: the last kernels reading them (its previous
+                # token) precede everything enqueued since on this stream
+                ev = torch.cuda.Event()
+                ev.record(self.stream)
+                self.copy_stream.wait_event(ev)
+                guess = torch.unique(self.idx_h[1]).to(torch.int32)
+                pst = nxt["cache"].prefetch(guess, self.copy_stream)
+                nxt["ready"].record(self.copy_stream)
+                if stats is not None:
+                    stats["prefetched"] = stats.get("prefetched", 0) + pst["misses"]
+                    stats["prefetch_bytes"] = stats.get("prefetch_bytes", 0) + pst["bytes_copied"]
+            em.edge_moe_residual(x, self.y, out, self.stream)
+            x = out
+        return x
+
+    def check(self, n_tokens=2):
+        """The streamed pass against the resident one, bitwise, on a few tokens."""
+        torch = self.torch
+        ok = True
+        for predict in (False, True):
+            for i in range(n_tokens):
+                t = self.tok
+                ref = self.step(resident=True).clone()
+                self.tok = t
+                got = self.step(predict=predict)
+                torch.cuda.synchronize()
+                ok = ok and bool(torch.equal(ref, got))
+        return ok
+
+    def time_steps(self, steps, warmup, predict=False, resident=False):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(predict=predict, resident=resident)
+        torch.cuda.synchronize()
+        stats = {}
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(predict=predict, resident=resident, stats=stats)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps, stats
+
+
+def h2d_rate(torch, mib=256, reps=5):
+    """Measured host -> HBM copy rate from pinned memory (GB/s)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+
+def stream_line(args):
+    """Decode with the experts streamed from host memory (edge_moe_cache_*):
+    tokens/s through a stack of full-size layers, for a few slot counts, with
+    and without next-layer prediction; the all-resident pass through the same
+    loop beside it."""
+    import torch
+    log("building the host-streamed decode stack ...")
+    rate = h2d_rate(torch)
+    out = {"unit": "tokens/s", "h2d_pinned_GBs": round(rate, 1), "layers": args.stream_layers,
+           "workload": "decode T=1, a new synthetic token every step through %d full-size layers; per-expert "
+                       "int4 tensors (A_up, B_up, A_dn, B_dn with scales, %.2f MB per expert) in pinned host "
+                       "memory, S slots per group and layer in HBM" % (args.stream_layers, 0.0)}
+    first = True
+    for S in args.stream_slots:
+        ss = StreamStack(args.stream_layers, S, host_init=args.host_init)
+        per_expert = ss.expert_bytes_resident / ss.D.n_experts
+        if first:
+            out["workload"] = out["workload"].replace("0.00 MB", "%.2f MB" % (per_expert / 1e6))
+            rsec, _ = ss.time_steps(args.stream_steps, 3, resident=True)
+            out["resident"] = {"value": round(1 / rsec, 1), "ms_per_step": round(rsec * 1e3, 4),
+                               "what": "the same loop with every expert resident (no host round trip)"}
+            log(f"  resident: {rsec * 1e3:.3f} ms per token")
+            first = False
+        same = ss.check()
+        ss.drop_resident_experts()
+        for predict in (False, True):
+            sec, st = ss.time_steps(args.stream_steps, 3, predict=predict)
+            em = ss.em
+            em.edge_moe_prof_reset()
+            em.edge_moe_prof_enable(True)
+            _, pst = ss.time_steps(max(10, args.stream_steps // 4), 0, predict=predict)
+            torch.cuda.synchronize()
+            em.edge_moe_prof_enable(False)
+            tab = em.edge_moe_prof_read()
+            em.edge_moe_prof_reset()
+            g_n, g_ms = tab.get("cache_gather", (0, 0.0))
+            g_bytes = pst.get("bytes_copied", 0) + pst.get("prefetch_bytes", 0)
+            n = args.stream_steps * args.stream_layers
+            hits, misses = st.get("hits", 0), st.get("misses", 0)
+            copied = st.get("bytes_copied", 0) + st.get("prefetch_bytes", 0)
+            key = f"S{S}" + ("_predict" if predict else "")
+            out[key] = {
+                "value": round(1 / sec, 1), "ms_per_step": round(sec * 1e3, 4), "slots_per_group": S,
+                "hbm_expert_bytes_per_layer": ss.slot_bytes,
+                "host_expert_bytes_per_layer": ss.expert_bytes_resident,
+                "hit_rate": round(hits / max(hits + misses, 1), 4),
+                "experts_copied_per_layer": round((misses + st.get("prefetched", 0)) / n, 2),
+                "h2d_bytes_per_token": int(copied / args.stream_steps),
+                "h2d_GBs": round(copied / args.stream_steps / sec / 1e9, 2),
+                "link_busy_frac": round(copied / args.stream_steps / (rate * 1e9) / sec, 4),
+                "equals_resident": same}
+            if g_n:
+                # the gather kernel against the host link: bytes it moved over its
+                # launches' summed time (HIP events around each launch)
+                ach = g_bytes / (g_ms * 1e-3) / 1e9
+                out[key]["roofline"] = {"bound": "host link", "kernel": "cache_gather", "launches": g_n,
+                                        "avg_ms": round(g_ms / g_n, 5),
+                                        "bytes_per_launch": int(g_bytes / g_n),
+                                        "achieved": round(ach, 1), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                                        "frac": round(ach / PCIE_PEAK_GBS, 4),
+                                        "frac_of_measured_dma": round(ach / rate, 4)}
+            log(f"  stream {key}: {sec * 1e3:.3f} ms per token, hit rate {out[key]['hit_rate']}, "
+                f"{out[key]['h2d_GBs']} GB/s host->HBM, equal to resident: {same}")
+        del ss
+        torch.cuda.empty_cache()
+    return out
+
+
 # ---------------------------------------------------------------- CPU baseline -------
 
 def cpu_baseline(wl: Workload, budget_s: float = 30.0):
@@ -640,6 +862,10 @@ def main():
     ap.add_argument("--no-calibrate", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MX-variant prefill line")
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--no-stream", action="store_true", help="skip the host-streamed decode line (also skipped by --no-decode)")
+    ap.add_argument("--stream-layers", type=int, default=4)
+    ap.add_argument("--stream-steps", type=int, default=100)
+    ap.add_argument("--stream-slots", type=int, nargs="+", default=[16, 32])
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--host-init", action="store_true",
@@ -731,6 +957,9 @@ def main():
         line["decode_t1"]["persistent"] = persistent_line(wd, args.steps, args.warmup, "decode_t1")
         del wd
         torch.cuda.empty_cache()
+
+    if not args.no_decode and not args.no_stream:
+        line["decode_t1_streamed"] = stream_line(args)
 
     if not args.no_stack:
         log("building the 48-layer stack ...")

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define EDGE_MOE_ABI_VERSION 4
+#define EDGE_MOE_ABI_VERSION 5
 
 /* Status codes. */
 #define EDGE_MOE_OK           0
@@ -256,7 +256,7 @@ int edge_moe_prefetch(const edge_moe_dims* dims, const edge_moe_weights* weights
  * B_up and B_dn scale bytes must not exceed 252 (their weights are formed in
  * bf16).
  *
- * Shapes: delta_rank 128, d and h multiples of 256 (at least 256), lora_rank a
+ * Shapes: delta_rank 128, d and h multiples of 512 (at least 512), lora_rank a
  * multiple of 8 from 8 to 32; any T.  quant_group is not used.  Other shapes:
  * EDGE_MOE_EUNSUPPORTED.  Every batch size runs the tiled large-batch kernels. */
 typedef struct edge_moe_weights_mx {
@@ -279,6 +279,92 @@ size_t edge_moe_workspace_bytes_mx(const edge_moe_dims* dims);
 int edge_moe_forward_mx(const edge_moe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                         const float* topk_w, const edge_moe_weights_mx* weights, float* y, void* ws,
                         size_t ws_bytes, void* stream, const edge_moe_trace* trace);
+
+/* ------------------------------------------------ expert streaming from host --
+ * The pages keep the expert library in host memory and bring the experts a
+ * batch routes to into a small GPU memory, evicting the least recently used,
+ * through fixed slots filled while other work runs (launch post "Edge0-145B:
+ * Frontier AI Capabilities on Your Own Computer", Under the Hood, Loading
+ * paragraph; byteiota "Edge0-145B: Run a 145B Open-Source Model on Your
+ * Laptop", The Three Pillars, SSD expert streaming paragraph).  Here one
+ * layer's per-expert tensors live in host memory (pinned, for the copies to
+ * overlap) and HBM holds S slots per group: slot arrays shaped like the
+ * layer's expert arrays with G * S experts in place of E.
+ *
+ * A batch runs unchanged kernels on a "slot layer": dims with
+ * n_experts = G * S and experts_per_group = S, weights whose shared matrices
+ * and LoRA factors are the resident layer's and whose expert tensors are the
+ * slot arrays, and topk_idx renamed by edge_moe_cache_map (topk_w unchanged).
+ * Slot g * S + s belongs to group g, so every (token, slot) pair computes what
+ * it computes with all E experts resident: bitwise through edge_moe_forward;
+ * through edge_moe_forward_persistent up to the order of fp32 additions (its
+ * down tasks split a pass's distinct experts over two K halves by their rank,
+ * so the numbering decides which partial sum a row's delta term joins).
+ *
+ * A cache is a host object: it keeps the pointers given to
+ * edge_moe_cache_create until edge_moe_cache_destroy, the one exception to
+ * the no-retained-pointer convention above.  One cache serves one layer and
+ * is not thread-safe. */
+typedef struct edge_moe_expert_tensors {
+    /* per expert, in edge_moe_weights' layouts; the first eight required,
+     * the two decode copies (edge_moe_tile_shared which = 2, 3) optional */
+    void* a_up_q;  void* a_up_scale;   /* [E or G*S][r][d/2],  [..][r][d/Gq_eff] fp16  */
+    void* b_up_q;  void* b_up_scale;   /* [..][h][r/2],        [..][h][r/Gq_eff]       */
+    void* a_dn_q;  void* a_dn_scale;   /* [..][r][h/2],        [..][r][h/Gq_eff]       */
+    void* b_dn_q;  void* b_dn_scale;   /* [..][d][r/2],        [..][d][r/Gq_eff]       */
+    void* a_up_t;  void* a_dn_t;       /* [..][r * d / 2], [..][r * h / 2] (optional) */
+} edge_moe_expert_tensors;
+
+typedef struct edge_moe_cache_stats {
+    int64_t hits;          /* distinct experts found resident            */
+    int64_t misses;        /* distinct experts copied into a slot        */
+    int64_t evictions;     /* misses that replaced a resident expert     */
+    int64_t bytes_copied;  /* host -> HBM bytes issued                   */
+} edge_moe_cache_stats;
+
+typedef struct edge_moe_cache edge_moe_cache;
+
+/* A cache of slots_per_group (1..P) slots per group.  host: the E experts'
+ * tensors (host memory); slots: the G * S slots' tensors (device memory, set
+ * exactly where host is set), or NULL for a cache that only plans (no copy is
+ * issued; the policy and the statistics behave the same).  The per-expert
+ * sizes follow from dims (T ignored).  NULL for invalid arguments or no
+ * memory.  Slots start empty. */
+edge_moe_cache* edge_moe_cache_create(const edge_moe_dims* dims, int32_t slots_per_group,
+                                      const edge_moe_expert_tensors* host, const edge_moe_expert_tensors* slots);
+void edge_moe_cache_destroy(edge_moe_cache* cache);
+
+/* Make a batch's experts resident and rename them to slots.  topk_idx: HOST
+ * int32[T][top_k] expert ids (as edge_moe_route wrote them); slot_idx: HOST
+ * int32[T][top_k], receives each entry's slot.  Resident experts of the batch
+ * are refreshed first; each missing one then takes a free slot of its group,
+ * else the group's least recently used slot that the batch does not use, and
+ * its tensors are copied there with hipMemcpyAsync on `stream`.  Work that
+ * still reads a slot (an earlier batch's kernels) or writes one (an earlier
+ * prefetch's copies on another stream) must be ordered before those copies
+ * (same stream, or an event), and the layer call after them.
+ * EDGE_MOE_EINVAL for a null cache or pointers or ids outside 0..E-1;
+ * EDGE_MOE_EUNSUPPORTED when some group needs more distinct experts than it
+ * has slots (nothing changes then); EDGE_MOE_EHIP when a copy could not be
+ * enqueued.  stats (may be NULL) receives this call's counts. */
+int edge_moe_cache_map(edge_moe_cache* cache, int32_t T, const int32_t* topk_idx, int32_t* slot_idx,
+                       void* stream, edge_moe_cache_stats* stats);
+
+/* Bring predicted experts in ahead of their batch (host int32[n] ids), e.g. on
+ * a copy stream while the previous layer computes, so that the slots are
+ * filled before edge_moe_cache_map needs them.  Same placement rule, except
+ * that any slot not filled by this call may be replaced; experts past a
+ * group's S in one call are skipped.  The same ordering duty and errors (ids
+ * outside 0..E-1: EDGE_MOE_EINVAL). */
+int edge_moe_cache_prefetch(edge_moe_cache* cache, int32_t n, const int32_t* experts, void* stream,
+                            edge_moe_cache_stats* stats);
+
+/* Counts summed over every map and prefetch call of the cache. */
+int edge_moe_cache_totals(const edge_moe_cache* cache, edge_moe_cache_stats* stats);
+
+/* The slot of a resident expert (0..G*S-1), -1 if not resident, -2 for a null
+ * cache or an id outside 0..E-1. */
+int edge_moe_cache_slot_of(const edge_moe_cache* cache, int32_t expert);
 
 /* Residual between stacked layers (a12): x_out[t][i] = bf16(x[t][i] + y[t][i]),
  * the exact sum rounded once to the nearest bf16 (ties to even).  The layers

@@ -31,7 +31,8 @@ EXPORTED = ("edge_moe_workspace_bytes", "edge_moe_route", "edge_moe_forward",
             "edge_moe_prof_enable", "edge_moe_prof_read", "edge_moe_prof_reset",
             "edge_moe_forward_noalloc", "edge_moe_forward_persistent", "edge_moe_mfma_peak",
             "edge_moe_workspace_bytes_mx", "edge_moe_forward_mx", "edge_moe_prefetch_ws_bytes",
-            "edge_moe_prefetch")
+            "edge_moe_prefetch", "edge_moe_cache_create", "edge_moe_cache_destroy", "edge_moe_cache_map",
+            "edge_moe_cache_prefetch", "edge_moe_cache_totals", "edge_moe_cache_slot_of")
 
 
 class CDims(ctypes.Structure):
@@ -65,6 +66,21 @@ _WEIGHT_FIELDS_MX = ("s_up_q", "s_up_e", "s_dn_q", "s_dn_e", "a_up_q", "a_up_e",
 
 class CWeightsMX(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS_MX]
+
+
+# per-expert tensors that an expert cache streams (weight-dict keys, struct order)
+EXPERT_TENSOR_KEYS = ("a_up", "a_up_scale", "b_up", "b_up_scale", "a_dn", "a_dn_scale",
+                      "b_dn", "b_dn_scale", "a_up_t", "a_dn_t")
+
+
+class CExpertTensors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("a_up_q", "a_up_scale", "b_up_q", "b_up_scale", "a_dn_q", "a_dn_scale",
+                 "b_dn_q", "b_dn_scale", "a_up_t", "a_dn_t")]
+
+
+class CCacheStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("hits", "misses", "evictions", "bytes_copied")]
 
 
 class CTrace(ctypes.Structure):
@@ -121,6 +137,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_moe_mfma_peak.restype = i32
     lib.edge_moe_forward_noalloc.argtypes = [ctypes.POINTER(CDims), vp, vp, vp, ctypes.POINTER(CWeights), vp, vp]
     lib.edge_moe_forward_noalloc.restype = i32
+    lib.edge_moe_cache_create.argtypes = [ctypes.POINTER(CDims), i32, ctypes.POINTER(CExpertTensors),
+                                          ctypes.POINTER(CExpertTensors)]
+    lib.edge_moe_cache_create.restype = vp
+    lib.edge_moe_cache_destroy.argtypes = [vp]
+    lib.edge_moe_cache_destroy.restype = None
+    lib.edge_moe_cache_map.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(CCacheStats)]
+    lib.edge_moe_cache_map.restype = i32
+    lib.edge_moe_cache_prefetch.argtypes = [vp, i32, vp, vp, ctypes.POINTER(CCacheStats)]
+    lib.edge_moe_cache_prefetch.restype = i32
+    lib.edge_moe_cache_totals.argtypes = [vp, ctypes.POINTER(CCacheStats)]
+    lib.edge_moe_cache_totals.restype = i32
+    lib.edge_moe_cache_slot_of.argtypes = [vp, i32]
+    lib.edge_moe_cache_slot_of.restype = i32
     lib.edge_moe_residual.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     lib.edge_moe_residual.restype = i32
     lib.edge_moe_copy.argtypes = [vp, vp, sz, vp]
@@ -305,6 +334,127 @@ def edge_moe_residual(x, y, x_out, stream=None) -> None:
     st = load().edge_moe_residual(int(T), int(d), _ptr(x), _ptr(y), _ptr(x_out), _stream(stream))
     if st != EDGE_MOE_OK:
         raise EdgeMoeError("edge_moe_residual", st)
+
+
+def _host_ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if t.is_cuda:
+        raise ValueError("this argument must be in host memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stats(c: CCacheStats) -> dict:
+    return {n: int(getattr(c, n)) for n, _ in CCacheStats._fields_}
+
+
+class ExpertCache:
+    """edge_moe_cache_*: an LRU of `slots_per_group` HBM slots per group for one
+    layer's expert tensors, filled from host memory.
+
+    host:  dict with EXPERT_TENSOR_KEYS (the last two optional) of host tensors
+           holding the layer's E experts (pin them for the copies to overlap);
+    slots: dict of device tensors with G * S experts each, the same keys set,
+           or None for a cache that only plans.
+    map() renames a batch's expert ids to slots and issues the copies of the
+    misses; the layer then runs on slot_dims() with the slot tensors in place
+    of the expert tensors (slot_weights())."""
+
+    def __init__(self, dims, slots_per_group: int, host: dict, slots: Optional[dict] = None):
+        self._lib = load()
+        self.S = int(slots_per_group)
+        self._keep = (host, slots)
+        # the library trusts the buffers to hold E experts (host) and G * S
+        # slots (device) of the per-expert sizes its dims imply: check them here
+        per = expert_tensor_bytes(dims)
+        G = dims.n_experts // dims.experts_per_group
+        for k in EXPERT_TENSOR_KEYS:
+            for side, tensors, count in (("host", host, dims.n_experts), ("slot", slots, G * self.S)):
+                t = None if tensors is None else tensors.get(k)
+                if t is not None and t.numel() * t.element_size() != count * per[k]:
+                    raise ValueError(f"{side} tensor {k}: {t.numel() * t.element_size()} bytes, "
+                                     f"expected {count} x {per[k]}")
+        ch = CExpertTensors(*(_host_ptr(host.get(k)) for k in EXPERT_TENSOR_KEYS))
+        cs = None if slots is None else CExpertTensors(*(_ptr(slots.get(k)) for k in EXPERT_TENSOR_KEYS))
+        self._h = self._lib.edge_moe_cache_create(ctypes.byref(cdims(dims)), self.S, ctypes.byref(ch),
+                                                  None if cs is None else ctypes.byref(cs))
+        if not self._h:
+            raise ValueError("edge_moe_cache_create rejected its arguments")
+
+    def map(self, topk_idx, slot_idx, stream=None) -> dict:
+        """topk_idx, slot_idx: host int32 [T][k] tensors; returns this call's counts."""
+        T = topk_idx.shape[0] if topk_idx.dim() else 0
+        st = CCacheStats()
+        r = self._lib.edge_moe_cache_map(self._h, int(T), _host_ptr(topk_idx), _host_ptr(slot_idx),
+                                         _stream(stream) if self._keep[1] is not None else None, ctypes.byref(st))
+        if r != EDGE_MOE_OK:
+            raise EdgeMoeError("edge_moe_cache_map", r)
+        return _stats(st)
+
+    def prefetch(self, experts, stream=None) -> dict:
+        st = CCacheStats()
+        r = self._lib.edge_moe_cache_prefetch(self._h, int(experts.numel()), _host_ptr(experts),
+                                              _stream(stream) if self._keep[1] is not None else None,
+                                              ctypes.byref(st))
+        if r != EDGE_MOE_OK:
+            raise EdgeMoeError("edge_moe_cache_prefetch", r)
+        return _stats(st)
+
+    def totals(self) -> dict:
+        st = CCacheStats()
+        r = self._lib.edge_moe_cache_totals(self._h, ctypes.byref(st))
+        if r != EDGE_MOE_OK:
+            raise EdgeMoeError("edge_moe_cache_totals", r)
+        return _stats(st)
+
+    def slot_of(self, expert: int) -> int:
+        return int(self._lib.edge_moe_cache_slot_of(self._h, int(expert)))
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.edge_moe_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def expert_tensor_bytes(dims) -> dict:
+    """Bytes of one expert's tensor of each EXPERT_TENSOR_KEYS key (packed int4
+    codes, fp16 scales per min(quant_group, K) elements; the decode copies are
+    the size of the codes they copy)."""
+    r, d, h, q = dims.delta_rank, dims.d, dims.h, dims.quant_group
+    sc = lambda n, k: n * (k // min(q, k)) * 2  # noqa: E731
+    out = {"a_up": r * d // 2, "a_up_scale": sc(r, d), "b_up": h * r // 2, "b_up_scale": sc(h, r),
+           "a_dn": r * h // 2, "a_dn_scale": sc(r, h), "b_dn": d * r // 2, "b_dn_scale": sc(d, r)}
+    out["a_up_t"], out["a_dn_t"] = out["a_up"], out["a_dn"]
+    return out
+
+
+class _SlotDims:
+    def __init__(self, dims, S: int):
+        for f, _ in CDims._fields_:
+            setattr(self, f, int(getattr(dims, f)))
+        self.n_experts = (self.n_experts // self.experts_per_group) * S
+        self.experts_per_group = S
+
+
+def slot_dims(dims, slots_per_group: int):
+    """The dims of the slot layer: G groups of S experts."""
+    return _SlotDims(dims, slots_per_group)
+
+
+def slot_weights(weights: dict, slots: dict) -> dict:
+    """The resident layer's weights with the slot tensors in place of the
+    per-expert tensors (missing optional slot tensors drop the key)."""
+    out = {k: v for k, v in weights.items() if k not in EXPERT_TENSOR_KEYS}
+    out.update({k: v for k, v in slots.items() if v is not None})
+    return out
 
 
 def edge_moe_prof_enable(on: bool) -> bool:

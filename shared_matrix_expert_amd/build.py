@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libedge_moe.so")
 SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "decode.hip", "layer.hip",
-           "prefill.hip", "calib.hip", "mx.hip", "prefetch.hip"]
+           "prefill.hip", "calib.hip", "mx.hip", "prefetch.hip", "cache.hip"]
 ARCH = "gfx950"
 
 
@@ -28,7 +28,8 @@ ARCH = "gfx950"
 # profile of a kernel stays valid while that file and the headers are unchanged.
 KERNEL_SOURCES = (("dec_layer", "layer.hip"), ("pl_", "layer.hip"), ("dec_", "decode.hip"),
                   ("router_", "router.hip"), ("perm_", "dispatch.hip"), ("pf_", "prefill.hip"),
-                  ("mfma_peak", "calib.hip"), ("mx_", "mx.hip"), ("prefetch_", "prefetch.hip"), ("copy_bytes", "gemm.hip"))
+                  ("mfma_peak", "calib.hip"), ("mx_", "mx.hip"), ("prefetch_", "prefetch.hip"), ("cache_", "cache.hip"),
+                  ("copy_bytes", "gemm.hip"))
 
 
 def sources_digest(kernel: str = "") -> str:

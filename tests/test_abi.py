@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert em.edge_moe_abi_version() == 4
+    assert em.edge_moe_abi_version() == 5
     for st in (0, -1, -2, -3, -4):
         assert em.status_string(st)
     assert em.status_string(7) == "unknown status"
