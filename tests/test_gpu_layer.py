@@ -449,6 +449,30 @@ def test_zero_delta_zero_lora():
     _run_parity(D, x, wr, bias, W)
 
 
+@pytest.mark.parametrize("pattern", ["2", "3", "4", "6", "8", "5+3"])
+def test_repeated_token_batches(pattern):
+    """Batches made of repeated tokens, so that selected experts carry several
+    rows: "n" is one token n times (every selected expert has n rows), "5+3"
+    one token five times beside three distinct ones.  The sampled verify
+    routings give one or two rows per expert; these cases fill the decode
+    kernels' 16-row tiles further and put up to 8 rows into one expert's
+    range.  Traced: permutation, activations and expert outputs too."""
+    say(f"case: repeated-token batch {pattern}")
+    if "+" in pattern:
+        n, m = (int(p) for p in pattern.split("+"))
+        base = synth.make_activations(1, 9, T=1 + m)
+        x = np.concatenate([np.repeat(base[:1], n, axis=0), base[1:]])
+    else:
+        n = int(pattern)
+        x = np.repeat(synth.make_activations(1, 9, T=1), n, axis=0)
+    D = synth.config(1).dims.with_T(x.shape[0])
+    wr, _ = synth.make_router(1, 9)
+    lay, idx, w, y, tr, fw = _run_parity(D, x, wr, None, synth.make_weights(1, 9, device="cuda"), keep=True)
+    _check_trace(D, idx, tr, fw)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=D.n_experts)
+    assert counts.max() == n
+
+
 def test_top1_routing():
     say("case: top-1")
     D = synth.Dims(**{**synth.config(2).dims.__dict__, "top_k": 1})
