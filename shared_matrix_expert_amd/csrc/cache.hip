@@ -34,9 +34,9 @@
 #include "edge_moe.h"
 #include "kernels.h"
 
-namespace {
+namespace em {
 
-constexpr int kTensors = 10;   // a_up, a_up_s, b_up, b_up_s, a_dn, a_dn_s, b_dn, b_dn_s, a_up_t, a_dn_t
+constexpr int kCacheTensors = 10;   // a_up, a_up_s, b_up, b_up_s, a_dn, a_dn_s, b_dn, b_dn_s, a_up_t, a_dn_t
 constexpr int kMaxPairs = 256; // (expert, slot) pairs per gather launch
 constexpr int GC_THREADS = 256;
 constexpr int GC_UNROLL = 4;
@@ -46,10 +46,10 @@ constexpr int GC_MAX_BLOCKS = 2048;
 // Everything a gather launch needs travels in its kernel arguments (about 1.3
 // KB), so a call needs no descriptor memory.
 struct GatherArgs {
-    const uint8_t* src[kTensors];     // device addresses of the host tensors
-    uint8_t* dst[kTensors];           // slot tensors
-    uint32_t bytes[kTensors];         // per expert, multiples of 16 (0: tensor absent)
-    uint32_t chunk_pre[kTensors + 1]; // first chunk of each tensor within a pair
+    const uint8_t* src[kCacheTensors];     // device addresses of the host tensors
+    uint8_t* dst[kCacheTensors];           // slot tensors
+    uint32_t bytes[kCacheTensors];         // per expert, multiples of 16 (0: tensor absent)
+    uint32_t chunk_pre[kCacheTensors + 1]; // first chunk of each tensor within a pair
     int32_t n;                        // pairs
     uint16_t e[kMaxPairs];            // source expert of each pair
     uint16_t slot[kMaxPairs];         // destination slot of each pair
@@ -60,13 +60,13 @@ struct GatherArgs {
 // flight before the first store.
 __global__ void __launch_bounds__(GC_THREADS)
 cache_gather(GatherArgs a) {
-    const uint32_t per_pair = a.chunk_pre[kTensors];
+    const uint32_t per_pair = a.chunk_pre[kCacheTensors];
     const uint32_t total = (uint32_t)a.n * per_pair;
     for (uint32_t item = blockIdx.x; item < total; item += gridDim.x) {
         const uint32_t p = item / per_pair;
         uint32_t c = item % per_pair;
         int t = 0;
-        while (t < kTensors - 1 && c >= a.chunk_pre[t + 1]) ++t;
+        while (t < kCacheTensors - 1 && c >= a.chunk_pre[t + 1]) ++t;
         c -= a.chunk_pre[t];
         const uint32_t nb = a.bytes[t];
         const uint8_t* src = a.src[t] + (size_t)a.e[p] * nb;
@@ -85,6 +85,17 @@ cache_gather(GatherArgs a) {
     }
 }
 
+}  // namespace em
+
+namespace {
+
+using em::GatherArgs;
+using em::GC_CHUNK;
+using em::GC_MAX_BLOCKS;
+using em::GC_THREADS;
+using em::kMaxPairs;
+
+constexpr int kTensors = em::kCacheTensors;   // a_up, a_up_s, b_up, b_up_s, a_dn, a_dn_s, b_dn, b_dn_s, a_up_t, a_dn_t
 struct Cache {
     edge_moe_dims dims;
     int G = 0, P = 0, S = 0;
@@ -182,7 +193,7 @@ hipError_t flush(Cache& c, hipStream_t s) {
         }
         const int blocks = (int)std::min<uint32_t>((uint32_t)n * pre, GC_MAX_BLOCKS);
         em::prof_begin(s);
-        cache_gather<<<blocks, GC_THREADS, 0, s>>>(a);
+        em::cache_gather<<<blocks, GC_THREADS, 0, s>>>(a);
         em::prof_end(s, "cache_gather");
         err = hipGetLastError();
     }
