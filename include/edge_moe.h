@@ -327,9 +327,13 @@ typedef struct edge_moe_cache edge_moe_cache;
 /* A cache of slots_per_group (1..P) slots per group.  host: the E experts'
  * tensors (host memory); slots: the G * S slots' tensors (device memory, set
  * exactly where host is set), or NULL for a cache that only plans (no copy is
- * issued; the policy and the statistics behave the same).  The per-expert
- * sizes follow from dims (T ignored).  NULL for invalid arguments or no
- * memory.  Slots start empty. */
+ * issued; the policy and the statistics behave the same).  dims must pass
+ * the layer's checks (T is not used otherwise); the per-expert sizes follow
+ * from it, and the buffers must hold E (host) and G * S (slots) experts of
+ * those sizes.  NULL for invalid arguments or no memory.  Slots start empty.
+ * Copies go out as one gather kernel per call that reads the host memory
+ * directly when every host tensor is device-addressable pinned memory
+ * (hipHostMalloc) and 16-byte aligned, else as hipMemcpyAsync per tensor. */
 edge_moe_cache* edge_moe_cache_create(const edge_moe_dims* dims, int32_t slots_per_group,
                                       const edge_moe_expert_tensors* host, const edge_moe_expert_tensors* slots);
 void edge_moe_cache_destroy(edge_moe_cache* cache);

@@ -36,12 +36,14 @@
 
 namespace em {
 
+int layer_dims_status(const edge_moe_dims* d);     // api.hip: the layer's shape checks
+
 constexpr int kCacheTensors = 10;   // a_up, a_up_s, b_up, b_up_s, a_dn, a_dn_s, b_dn, b_dn_s, a_up_t, a_dn_t
 constexpr int kMaxPairs = 256; // (expert, slot) pairs per gather launch
 constexpr int GC_THREADS = 256;
 constexpr int GC_UNROLL = 4;
 constexpr uint32_t GC_CHUNK = GC_THREADS * 16 * GC_UNROLL;   // bytes per workgroup turn
-constexpr int GC_MAX_BLOCKS = 2048;
+constexpr int GC_MAX_BLOCKS = 64;   // enough reads in flight for the host link, few CUs taken
 
 // Everything a gather launch needs travels in its kernel arguments (about 1.3
 // KB), so a call needs no descriptor memory.
@@ -212,11 +214,10 @@ extern "C" {
 
 edge_moe_cache* edge_moe_cache_create(const edge_moe_dims* dims, int32_t slots_per_group,
                                       const edge_moe_expert_tensors* host, const edge_moe_expert_tensors* slots) {
-    if (!dims || !host || dims->d <= 0 || dims->h <= 0 || dims->n_experts <= 0 || dims->experts_per_group <= 0 ||
-        dims->n_experts % dims->experts_per_group != 0 || dims->top_k <= 0 || dims->delta_rank <= 0 ||
-        dims->quant_group <= 0)
-        return nullptr;
-    if (slots_per_group < 1 || slots_per_group > dims->experts_per_group || dims->n_experts > 65535) return nullptr;
+    // the layer's own shape rules, so that the per-expert sizes are those its
+    // kernels address
+    if (!host || em::layer_dims_status(dims) != EDGE_MOE_OK) return nullptr;
+    if (slots_per_group < 1 || slots_per_group > dims->experts_per_group) return nullptr;
     Cache* c = new (std::nothrow) Cache();
     if (!c) return nullptr;
     c->dims = *dims;

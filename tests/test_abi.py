@@ -229,3 +229,24 @@ def test_prefetch_validation_before_any_device_call():
     assert call(base, 4, 1, base, ws_n - 4) == em.EDGE_MOE_EWORKSPACE  # scratch too small
     assert call(base, 4, 1, None, ws_n) == em.EDGE_MOE_EWORKSPACE
     assert call(None, 0, 1, base, ws_n) == em.EDGE_MOE_OK              # nothing to read: no device call
+
+
+def test_cache_validation_before_any_device_call():
+    lib = em.load()
+    st = em.CCacheStats()
+    assert lib.edge_moe_cache_map(None, 1, None, None, None, ctypes.byref(st)) == em.EDGE_MOE_EINVAL
+    assert lib.edge_moe_cache_prefetch(None, 1, None, None, None) == em.EDGE_MOE_EINVAL
+    assert lib.edge_moe_cache_totals(None, ctypes.byref(st)) == em.EDGE_MOE_EINVAL
+    assert lib.edge_moe_cache_slot_of(None, 0) == -2
+    lib.edge_moe_cache_destroy(None)
+    D = synth.config(1).dims
+    fake = em.CExpertTensors(*([0x1000] * 8 + [None, None]))
+    c = lib.edge_moe_cache_create(ctypes.byref(em.cdims(D)), 8, ctypes.byref(fake), None)   # plans only
+    assert c
+    lib.edge_moe_cache_destroy(c)
+    assert not lib.edge_moe_cache_create(ctypes.byref(em.cdims(D)), 8, ctypes.byref(em.CExpertTensors()), None)
+    assert not lib.edge_moe_cache_create(ctypes.byref(em.cdims(D)), 0, ctypes.byref(fake), None)
+    assert not lib.edge_moe_cache_create(ctypes.byref(em.cdims(D)), 65, ctypes.byref(fake), None)
+    for bad in (dict(d=100), dict(quant_group=48), dict(delta_rank=12), dict(n_experts=500)):
+        Db = dataclasses.replace(D, **bad)
+        assert not lib.edge_moe_cache_create(ctypes.byref(em.cdims(Db)), 8, ctypes.byref(fake), None), bad
