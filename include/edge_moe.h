@@ -350,7 +350,8 @@ void edge_moe_cache_destroy(edge_moe_cache* cache);
  * EDGE_MOE_EINVAL for a null cache or pointers or ids outside 0..E-1;
  * EDGE_MOE_EUNSUPPORTED when some group needs more distinct experts than it
  * has slots (nothing changes then); EDGE_MOE_EHIP when a copy could not be
- * enqueued.  stats (may be NULL) receives this call's counts. */
+ * enqueued (the placement was recorded, so the slots no longer match it:
+ * destroy the cache).  stats (may be NULL) receives this call's counts. */
 int edge_moe_cache_map(edge_moe_cache* cache, int32_t T, const int32_t* topk_idx, int32_t* slot_idx,
                        void* stream, edge_moe_cache_stats* stats);
 
