@@ -350,6 +350,67 @@ mx_gemm(LayerArgs a) {
     for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
+    // The LoRA and per-expert delta products go into the accumulators before
+    // the main loop: every load they make is consumed before the first
+    // stage's, and the main loop's operand state is not yet live, so the
+    // epilogue is left with the stores alone.
+    if constexpr (!C::Z) {
+        const int wm = wv >> 2, wn = wv & 3;
+        // ---- LoRA branch: V[g] (bf16 [N][rL]) x the rounded LoRA input rows (bf16 [rows][rLp])
+        const int rLp = (a.rL + 7) & ~7;
+        {
+            const uint16_t* V = (MODE == MX_HS ? a.lu_v : a.ld_v) + (size_t)t.g * N * a.rL;
+            const uint16_t* Zl = MODE == MX_HS ? a.zl : a.zl2;
+            for (int kb = 0; kb < a.rL; kb += 32) {
+                const bool kv = kb + 8 * g < a.rL;
+                uint4 bv[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int n = t.n0 + WN * wn + 16 * j + m;
+                    bv[j] = kv ? ld16(V + (size_t)n * a.rL + kb + 8 * g) : zero_u4();
+                }
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int row = t.r0 + min(64 * wm + 16 * i + m, nrow - 1);
+                    const uint4 av = kv ? ld16(Zl + (size_t)row * rLp + kb + 8 * g) : zero_u4();
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_bf16(av, bv[j], acc[i][j]);
+                }
+            }
+        }
+
+        // ---- per-expert delta down: B_dn[e] (MXFP4 [d][r], exact in bf16) x z2 rows of expert e.
+        // Lane group g takes K block g (32 elements): its 16 code bytes and scale
+        // convert to the four bf16 operands of steps s = 0..3 (elements 8 s ..).
+        if constexpr (MODE == MX_OUT) {
+            const int e_first = a.db.row_exp[t.r0], e_last = a.db.row_exp[t.r1 - 1];
+            for (int e = e_first; e <= e_last; ++e) {
+                const int p = max(a.db.eoff[e], t.r0) - t.r0;          // tile rows [p, q) are expert e's
+                const int q = min(a.db.eoff[e + 1], t.r1) - t.r0;
+                if (p >= q) continue;
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int rl = 64 * wm + 16 * i;                    // subtile rows [rl, rl + 16)
+                    if (rl + 16 <= p || rl >= q) continue;              // wave-uniform
+                    const int row = rl + m;
+                    const bool mine = row >= p && row < q;
+                    const uint16_t* zr = a.z2 + (size_t)(t.r0 + (mine ? row : p)) * KC + 32 * g;
+                    uint4 af[4];
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) af[st] = mine ? ld16(zr + 8 * st) : zero_u4();
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {                      // one column subtile's operands at a time
+                        uint4 bq[4];
+                        const size_t n = (size_t)e * a.d + t.n0 + WN * wn + 16 * j + m;
+                        fp4_block_bf16(ld16(a.b_dn + n * (KC / 2) + 16 * g), a.b_dn_e[n * (KC / 32) + g], bq);
+#pragma unroll
+                        for (int st = 0; st < 4; ++st) acc[i][j] = mfma_bf16(af[st], bq[st], acc[i][j]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        }
+    }
 
     // ---- main loop: loads STAGES - 1 K steps ahead of the math
     const int nk = K / MBK;
@@ -381,61 +442,6 @@ mx_gemm(LayerArgs a) {
                     out[(size_t)(t.r0 + tr) * a.r + WN * wn + 16 * j + m] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
             }
         return;
-    }
-
-    // ---- LoRA branch: V[g] (bf16 [N][rL]) x the rounded LoRA input rows (bf16 [rows][rLp])
-    const int rLp = (a.rL + 7) & ~7;
-    {
-        const uint16_t* V = (MODE == MX_HS ? a.lu_v : a.ld_v) + (size_t)t.g * N * a.rL;
-        const uint16_t* Zl = MODE == MX_HS ? a.zl : a.zl2;
-        for (int kb = 0; kb < a.rL; kb += 32) {
-            const bool kv = kb + 8 * g < a.rL;
-            uint4 bv[NJ];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int n = t.n0 + WN * wn + 16 * j + m;
-                bv[j] = kv ? ld16(V + (size_t)n * a.rL + kb + 8 * g) : zero_u4();
-            }
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int row = t.r0 + min(64 * wm + 16 * i + m, nrow - 1);
-                const uint4 av = kv ? ld16(Zl + (size_t)row * rLp + kb + 8 * g) : zero_u4();
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_bf16(av, bv[j], acc[i][j]);
-            }
-        }
-    }
-
-    // ---- per-expert delta down: B_dn[e] (MXFP4 [d][r], exact in bf16) x z2 rows of expert e.
-    // Lane group g takes K block g (32 elements): its 16 code bytes and scale
-    // convert to the four bf16 operands of steps s = 0..3 (elements 8 s ..).
-    if constexpr (MODE == MX_OUT) {
-        const int e_first = a.db.row_exp[t.r0], e_last = a.db.row_exp[t.r1 - 1];
-        for (int e = e_first; e <= e_last; ++e) {
-            const int p = max(a.db.eoff[e], t.r0) - t.r0;          // tile rows [p, q) are expert e's
-            const int q = min(a.db.eoff[e + 1], t.r1) - t.r0;
-            if (p >= q) continue;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int rl = 64 * wm + 16 * i;                    // subtile rows [rl, rl + 16)
-                if (rl + 16 <= p || rl >= q) continue;              // wave-uniform
-                const int row = rl + m;
-                const bool mine = row >= p && row < q;
-                const uint16_t* zr = a.z2 + (size_t)(t.r0 + (mine ? row : p)) * KC + 32 * g;
-                uint4 af[4];
-#pragma unroll
-                for (int st = 0; st < 4; ++st) af[st] = mine ? ld16(zr + 8 * st) : zero_u4();
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {                      // one column subtile's operands at a time
-                    uint4 bq[4];
-                    const size_t n = (size_t)e * a.d + t.n0 + WN * wn + 16 * j + m;
-                    fp4_block_bf16(ld16(a.b_dn + n * (KC / 2) + 16 * g), a.b_dn_e[n * (KC / 32) + g], bq);
-#pragma unroll
-                    for (int st = 0; st < 4; ++st) acc[i][j] = mfma_bf16(af[st], bq[st], acc[i][j]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
     }
 
     // ---- store: lane holds rows 16 i + 4 g + v of its wave's 64, column 16 j + m of its wave's block
