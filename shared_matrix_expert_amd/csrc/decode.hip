@@ -394,7 +394,12 @@ EM_DEV void upw_run(const DecodeArgs& a, RouteView& v, UpwLds& L) {
     const int n_z1 = L.nx * (a.r / 16) * 2;             // A_up tile halves
     const int n_items = n_hs + n_z1;
     const int nw = (int)gridDim.x * UPW_WAVES;
-    const int gw = (int)blockIdx.x * UPW_WAVES + wv;
+    // Items go to the waves in turn.  Numbered workgroup by workgroup, a
+    // workgroup's eight waves stream one contiguous tile group; but when most
+    // waves hold one or two items, the last round then lands on the first
+    // CUs only (at one token: twice the bytes on 148 of 256 CUs), so below two
+    // items per wave the waves are numbered across the CUs first.
+    const int gw = n_items < 2 * nw ? wv * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x * UPW_WAVES + wv;
     const int nk_hs = gw < n_hs ? (n_hs - 1 - gw) / nw + 1 : 0;
     const int nk = gw < n_items ? (n_items - 1 - gw) / nw + 1 : 0;
     const int nhalf = 2 * nk_hs + (nk - nk_hs);         // K halves to stream
