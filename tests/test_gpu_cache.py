@@ -132,3 +132,17 @@ def test_cache_large_batch_full_size(T):
     # batches above the decode kernels' range: the permutation and tiled GEMM path
     tot = _run(1, T, batches=4, tiled=False)
     assert tot["misses"] > 0
+
+
+def test_streamed_stack_equals_resident():
+    # the benchmark's streamed decode stack (two full-size layers with the
+    # residual between them, 8 slots per group, a new token per step): every
+    # token's output, with and without next-layer prediction, bitwise equal to
+    # the same stack with every expert resident
+    import bench
+    say("case: streamed two-layer decode stack against the resident stack")
+    ss = bench.StreamStack(2, 8, n_tokens=16)
+    assert ss.check(n_tokens=6)
+    tot = [L["cache"].totals() for L in ss.layers]
+    assert all(t["misses"] > 0 for t in tot)
+    assert sum(t["evictions"] for t in tot) > 0
