@@ -982,33 +982,92 @@ dec_act(DecodeArgs a) {
             // for later loads would otherwise count these as possibly absent
             act_fetch_up(ru_, a, e, min(cb + 1, j1 - 1));
 
-            // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h))
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int lrow = wv * 64 + nt * 16 + li;
-                const int ncol = cb * CB_L + lrow;
-                floatx4 acc[NS];
-#pragma unroll
-                for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+            // ---- h = shared + B_up[e] z1 + V_up[g] zl; a = R3(SiLU(h)).  With
+            // one subtile the wave's four column tiles take each K step
+            // together, so that their conversions and MFMA chains interleave
+            // (the four-subtile instance lacks the registers and keeps one tile
+            // at a time).
+            if constexpr (NS == 1) {
                 uint4 af[NS][4];
 #pragma unroll
                 for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
                         af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
-                mac_fast<NS>(acc, af, wb[lrow * 5 + c], bsc[lrow]);
+                uint4 raw[4];
+                float sc[4];
 #pragma unroll
-                for (int ms = 0; ms < NS; ++ms)
-                    acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt], acc[ms]);
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int lrow = wv * 64 + nt * 16 + li;
+                    raw[nt] = wb[lrow * 5 + c];
+                    sc[nt] = 16.0f * fp16_bits_to_f32(bsc[lrow]);
+                }
+                floatx4 acc[4][NS];
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const uint32_t w = s == 0 ? raw[nt].x : s == 1 ? raw[nt].y : s == 2 ? raw[nt].z : raw[nt].w;
+                        uint32_t q[4];
+                        dequant8(w, q);
+                        const uint4 b = make_uint4(q[0], q[1], q[2], q[3]);
+#pragma unroll
+                        for (int ms = 0; ms < NS; ++ms) acc[nt][ms] = mfma_bf16(af[ms][s], b, s == 0 ? zero4() : acc[nt][ms]);
+                    }
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms) {
+                        acc[nt][ms] = fma4(sc[nt], acc[nt][ms], zero4());
+                        acc[nt][ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt],
+                                                acc[nt][ms]);
+                    }
+                // SiLU only for the rows some lane holds (a wave-uniform test);
+                // rows past the expert's count store zeros
 #pragma unroll
                 for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int i = ms * 16 + 4 * c + q;
-                        uint16_t ab = 0;
-                        if (i < nrows) ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
-                        as_[i][lrow] = ab;
+                        if (ms * 16 + q < nrows) {
+#pragma unroll
+                            for (int nt = 0; nt < 4; ++nt) {
+                                const uint16_t ab = (uint16_t)f32_to_bf16_rne(silu(acc[nt][ms][q] + hv[nt][ms][q]));
+                                as_[i][wv * 64 + nt * 16 + li] = i < nrows ? ab : (uint16_t)0;
+                            }
+                        } else {
+#pragma unroll
+                            for (int nt = 0; nt < 4; ++nt) as_[i][wv * 64 + nt * 16 + li] = 0;
+                        }
                     }
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int lrow = wv * 64 + nt * 16 + li;
+                    const int ncol = cb * CB_L + lrow;
+                    floatx4 acc[NS];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms) acc[ms] = zero4();
+                    uint4 af[NS][4];
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
+                    mac_fast<NS>(acc, af, wb[lrow * 5 + c], bsc[lrow]);
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+                        acc[ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&zls[ms * 16 + li][8 * c]), vb[nt], acc[ms]);
+#pragma unroll
+                    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int i = ms * 16 + 4 * c + q;
+                            uint16_t ab = 0;
+                            if (i < nrows) ab = (uint16_t)f32_to_bf16_rne(silu(acc[ms][q] + hv[nt][ms][q]));
+                            as_[i][lrow] = ab;
+                        }
+                }
             }
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) fetch_hv(min(cb + 1, j1 - 1), nt);
@@ -1036,33 +1095,84 @@ dec_act(DecodeArgs a) {
             __syncthreads();
             act_fetch_dn(rd_, a, e, g, min(cb + 1, j1 - 1));
 
-            // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows
+            // ---- R4, R5 inputs over these 256 columns: 8 tiles of A_dn rows, 1-2 of U_dn rows.
+            // With one subtile the wave's two A_dn tiles (wv and wv + 4) take
+            // each K step together.
+            if constexpr (NS == 1) {
 #pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                const int nt2 = wv + 4 * t;
-                if (nt2 >= N2 / 16) break;
-                const int n2 = nt2 * 16 + li;
-                if (nt2 * 16 < KC) {
+                for (int u = 0; u < 2; ++u) {
+                    uint4 af[NS][4];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        uint4 af[NS][4];
+                    for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
-                        for (int ms = 0; ms < NS; ++ms)
+                        for (int s = 0; s < 4; ++s)
+                            af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
+                    uint4 raw[2];
+                    float sc[2];
 #pragma unroll
-                            for (int s = 0; s < 4; ++s)
-                                af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
-                        mac_fast<NS>(z2acc[t], af, wb[n2 * 9 + u * 4 + c], asc[n2][u]);
+                    for (int t = 0; t < 2; ++t) {
+                        const int n2 = (wv + 4 * t) * 16 + li;
+                        raw[t] = wb[n2 * 9 + u * 4 + c];
+                        sc[t] = 16.0f * fp16_bits_to_f32(asc[n2][u]);
                     }
-                } else {
-                    const int cl = n2 - KC;
+                    floatx4 tp[2][NS];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const uint32_t w = s == 0 ? raw[t].x : s == 1 ? raw[t].y : s == 2 ? raw[t].z : raw[t].w;
+                            uint32_t q[4];
+                            dequant8(w, q);
+                            const uint4 b = make_uint4(q[0], q[1], q[2], q[3]);
+#pragma unroll
+                            for (int ms = 0; ms < NS; ++ms) tp[t][ms] = mfma_bf16(af[ms][s], b, s == 0 ? zero4() : tp[t][ms]);
+                        }
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int ms = 0; ms < NS; ++ms) z2acc[t][ms] = fma4(sc[t], tp[t][ms], z2acc[t][ms]);
+                }
+                // the U_dn tile (tile wv + 8, past the eight A_dn tiles)
+                if (wv + 8 < N2 / 16) {
+                    const int cl = (wv + 8) * 16 + li - KC;
                     const bool nvalid = cl < a.rL;
 #pragma unroll
                     for (int st = 0; st < CB_L / 32; ++st) {
                         const uint4 bv = nvalid ? ub[cl * 33 + st * 4 + c] : zero_u4();
 #pragma unroll
                         for (int ms = 0; ms < NS; ++ms)
-                            z2acc[t][ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]),
-                                                     bv, z2acc[t][ms]);
+                            z2acc[2][ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]),
+                                                     bv, z2acc[2][ms]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    const int nt2 = wv + 4 * t;
+                    if (nt2 >= N2 / 16) break;
+                    const int n2 = nt2 * 16 + li;
+                    if (nt2 * 16 < KC) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            uint4 af[NS][4];
+#pragma unroll
+                            for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+                                for (int s = 0; s < 4; ++s)
+                                    af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
+                            mac_fast<NS>(z2acc[t], af, wb[n2 * 9 + u * 4 + c], asc[n2][u]);
+                        }
+                    } else {
+                        const int cl = n2 - KC;
+                        const bool nvalid = cl < a.rL;
+#pragma unroll
+                        for (int st = 0; st < CB_L / 32; ++st) {
+                            const uint4 bv = nvalid ? ub[cl * 33 + st * 4 + c] : zero_u4();
+#pragma unroll
+                            for (int ms = 0; ms < NS; ++ms)
+                                z2acc[t][ms] = mfma_bf16(*reinterpret_cast<const uint4*>(&as_[ms * 16 + li][st * 32 + 8 * c]),
+                                                         bv, z2acc[t][ms]);
+                        }
                     }
                 }
             }
