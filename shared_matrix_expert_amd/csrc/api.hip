@@ -240,9 +240,7 @@ void* scratch_ptr() {
 namespace em {
 // The layer's shape checks, for the host-side expert cache (cache.hip).
 int layer_dims_status(const edge_moe_dims* d) { return check_dims(d); }
-}  // namespace em
 
-namespace em {
 void prof_begin(hipStream_t s) {
     ProfState& p = prof();
     if (!p.on.load(std::memory_order_relaxed)) return;
