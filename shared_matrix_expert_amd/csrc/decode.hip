@@ -951,7 +951,10 @@ dec_act(DecodeArgs a) {
             const int i = tid + 256 * u, row = i / KC, col = i % KC;
             float sum = 0.f + zp[u][0];
             if (a.S1 > 1) sum += zp[u][1];
-            zs[row][col] = row < nrows ? (uint16_t)f32_to_bf16_rne(sum) : (uint16_t)0;
+            // one subtile: each 8-element group in the K order (0,4,1,5,2,6,3,7)
+            // of dq_offset, so that B_up's codes need no reordering
+            const int pcol = NS == 1 ? (col & ~7) | ((col & 3) << 1) | ((col >> 2) & 1) : col;
+            zs[row][pcol] = row < nrows ? (uint16_t)f32_to_bf16_rne(sum) : (uint16_t)0;
         }
 #pragma unroll
         for (int u = 0; u < ZLI; ++u) {
@@ -968,7 +971,6 @@ dec_act(DecodeArgs a) {
         for (int t = 0; t < 3; ++t)
 #pragma unroll
             for (int ms = 0; ms < NS; ++ms) z2acc[t][ms] = zero4();
-
         for (int cb = j0; cb < j1; ++cb) {
             // this block's B_up into LDS; the next block's B_up loads go out at once
 #pragma unroll
@@ -994,13 +996,23 @@ dec_act(DecodeArgs a) {
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
                         af[ms][s] = *reinterpret_cast<const uint4*>(&zs[ms * 16 + li][32 * c + 8 * s]);
+                // B_up's codes enter the products as 136 + q (dq_offset, with
+                // z1 staged in its K order), so each product starts from -136
+                // times its z1 row's sum: K = r = 128 is a single quant group,
+                // so one such product per row serves every column
+                floatx4 zcorr = zero4();
+                {
+                    const uint4 neg136 = make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) zcorr = mfma_bf16(af[0][s], neg136, zcorr);
+                }
                 uint4 raw[4];
                 float sc[4];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     const int lrow = wv * 64 + nt * 16 + li;
                     raw[nt] = wb[lrow * 5 + c];
-                    sc[nt] = 16.0f * fp16_bits_to_f32(bsc[lrow]);
+                    sc[nt] = fp16_bits_to_f32(bsc[lrow]);
                 }
                 floatx4 acc[4][NS];
 #pragma unroll
@@ -1008,11 +1020,9 @@ dec_act(DecodeArgs a) {
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) {
                         const uint32_t w = s == 0 ? raw[nt].x : s == 1 ? raw[nt].y : s == 2 ? raw[nt].z : raw[nt].w;
-                        uint32_t q[4];
-                        dequant8(w, q);
-                        const uint4 b = make_uint4(q[0], q[1], q[2], q[3]);
+                        const uint4 b = dq_offset(w);
 #pragma unroll
-                        for (int ms = 0; ms < NS; ++ms) acc[nt][ms] = mfma_bf16(af[ms][s], b, s == 0 ? zero4() : acc[nt][ms]);
+                        for (int ms = 0; ms < NS; ++ms) acc[nt][ms] = mfma_bf16(af[ms][s], b, s == 0 ? zcorr : acc[nt][ms]);
                     }
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
@@ -1107,13 +1117,22 @@ dec_act(DecodeArgs a) {
 #pragma unroll
                         for (int s = 0; s < 4; ++s)
                             af[ms][s] = *reinterpret_cast<const uint4*>(&as_[ms * 16 + li][u * KC + 32 * c + 8 * s]);
+                    // A_dn's codes enter as 136 + q in natural K order
+                    // (dq_offset_nat); each chunk's products start from -136
+                    // times the chunk's activation row sums
+                    floatx4 acorr = zero4();
+                    {
+                        const uint4 neg136 = make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) acorr = mfma_bf16(af[0][s], neg136, acorr);
+                    }
                     uint4 raw[2];
                     float sc[2];
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const int n2 = (wv + 4 * t) * 16 + li;
                         raw[t] = wb[n2 * 9 + u * 4 + c];
-                        sc[t] = 16.0f * fp16_bits_to_f32(asc[n2][u]);
+                        sc[t] = fp16_bits_to_f32(asc[n2][u]);
                     }
                     floatx4 tp[2][NS];
 #pragma unroll
@@ -1121,11 +1140,9 @@ dec_act(DecodeArgs a) {
 #pragma unroll
                         for (int t = 0; t < 2; ++t) {
                             const uint32_t w = s == 0 ? raw[t].x : s == 1 ? raw[t].y : s == 2 ? raw[t].z : raw[t].w;
-                            uint32_t q[4];
-                            dequant8(w, q);
-                            const uint4 b = make_uint4(q[0], q[1], q[2], q[3]);
+                            const uint4 b = dq_offset_nat(w);
 #pragma unroll
-                            for (int ms = 0; ms < NS; ++ms) tp[t][ms] = mfma_bf16(af[ms][s], b, s == 0 ? zero4() : tp[t][ms]);
+                            for (int ms = 0; ms < NS; ++ms) tp[t][ms] = mfma_bf16(af[ms][s], b, s == 0 ? acorr : tp[t][ms]);
                         }
 #pragma unroll
                     for (int t = 0; t < 2; ++t)

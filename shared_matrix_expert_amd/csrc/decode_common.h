@@ -234,10 +234,29 @@ EM_DEV uint4 k_interleave(uint4 v) {
 // holding 136 + q exactly: flipping each nibble's sign bit gives q + 8 in
 // 0..15, which becomes the low mantissa bits below the exponent of 128.  The
 // pairs come out in the K order (0,4,1,5,2,6,3,7).
+// Each pair is one three-input bit operation: (v & M) ^ K with K = C ^ 0x00080008
+// (M and C share no bits, so the OR with C and the sign flip are one XOR).
+// The truth table of f(src0, src1, src2) is f evaluated on the bytes 0xF0,
+// 0xCC, 0xAA: (0xF0 & 0xCC) ^ 0xAA = 0x6A.
 EM_DEV uint4 dq_offset(uint32_t w) {
-    constexpr uint32_t M = 0x000F000Fu, C = 0x43004300u;
-    w ^= 0x88888888u;
-    return make_uint4((w & M) | C, ((w >> 4) & M) | C, ((w >> 8) & M) | C, ((w >> 12) & M) | C);
+    constexpr uint32_t M = 0x000F000Fu, K = 0x43084308u;
+    constexpr unsigned char AND_XOR = 0x6A;
+    return make_uint4(__builtin_amdgcn_bitop3_b32(w, M, K, AND_XOR), __builtin_amdgcn_bitop3_b32(w >> 4, M, K, AND_XOR),
+                      __builtin_amdgcn_bitop3_b32(w >> 8, M, K, AND_XOR), __builtin_amdgcn_bitop3_b32(w >> 12, M, K, AND_XOR));
+}
+
+// dq_offset with the pairs in natural K order: out[i] = (136 + q[2i]) |
+// (136 + q[2i + 1]) << 16.  A byte permute puts byte i of w (low nibble
+// q[2i]) at byte 0 and byte i of w >> 4 (low nibble q[2i + 1]) at byte 2; the
+// same three-input operation as above then masks, flips and offsets both.
+EM_DEV uint4 dq_offset_nat(uint32_t w) {
+    constexpr uint32_t M = 0x000F000Fu, K = 0x43084308u;
+    constexpr unsigned char AND_XOR = 0x6A;
+    const uint32_t u = w >> 4;
+    return make_uint4(__builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(u, w, 0x0C040C00u), M, K, AND_XOR),
+                      __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(u, w, 0x0C050C01u), M, K, AND_XOR),
+                      __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(u, w, 0x0C060C02u), M, K, AND_XOR),
+                      __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(u, w, 0x0C070C03u), M, K, AND_XOR));
 }
 
 // Delta down for the rows of one pass (sorted by expert): acc[ms] (output rows
