@@ -25,30 +25,60 @@ ARCH = "gfx950"
 
 
 # The source file of each kernel family (by kernel-name prefix); a stored
-# profile of a kernel stays valid while that file and the headers are unchanged.
+# profile of a kernel stays valid while that file and the headers it includes are
+# unchanged.
 KERNEL_SOURCES = (("dec_layer", "layer.hip"), ("pl_", "layer.hip"), ("dec_", "decode.hip"),
                   ("router_", "router.hip"), ("perm_", "dispatch.hip"), ("pf_", "prefill.hip"),
                   ("mfma_peak", "calib.hip"), ("mx_", "mx.hip"), ("prefetch_", "prefetch.hip"), ("cache_", "cache.hip"),
                   ("copy_bytes", "gemm.hip"))
 
 
-def sources_digest(kernel: str = "") -> str:
-    """sha256 over the library's internal headers and either every source and
-    the public header (no kernel given) or the source file of `kernel`:
-    identifies the code a stored profile was taken from.  Kernel sources do not
-    include the public header, so its text is left out of a kernel's digest."""
+def include_closure(src: str, root_csrc: str = CSRC, root_inc: str = os.path.join(ROOT, "include"),
+                    read=None) -> list:
+    """Files `src` (under csrc/) compiles from: itself and every header it
+    includes with #include "..." (internal headers and the public header),
+    transitively; sorted by path, the source last.  `read(path)` returns a file's text
+    (default: the working tree)."""
+    read = read or (lambda path: open(path, encoding="utf-8").read())
+    seen, todo = set(), [os.path.join(root_csrc, src)]
+    while todo:
+        path = todo.pop()
+        if path in seen:
+            continue
+        seen.add(path)
+        for line in read(path).splitlines():
+            t = line.strip()
+            if t.startswith("#include") and '"' in t:
+                name = t.split('"')[1]
+                for base in (root_csrc, root_inc):
+                    cand = os.path.join(base, name)
+                    try:
+                        read(cand)
+                    except (OSError, KeyError):
+                        continue
+                    todo.append(cand)
+                    break
+    src_path = os.path.join(root_csrc, src)
+    return sorted(p for p in seen if p != src_path) + [src_path]
+
+
+def sources_digest(kernel: str = "", read=None) -> str:
+    """sha256 identifying the code a stored profile was taken from: with a
+    kernel, the kernel's source file and the headers it includes (so that an
+    edit elsewhere leaves its profiles valid); without one, every source and
+    header and the public header."""
     import hashlib
+    read_b = (lambda path: open(path, "rb").read()) if read is None else (lambda path: read(path).encode())
     h = hashlib.sha256()
-    headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
-    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    public = ["../../include/edge_moe.h"]
-    if kernel:
-        hit = [f for pre, f in KERNEL_SOURCES if kernel.startswith(pre)]
-        if hit:
-            srcs, public = hit[:1], []
-    for f in headers + srcs + public:
-        with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+    hit = [f for pre, f in KERNEL_SOURCES if kernel.startswith(pre)] if kernel else []
+    if hit:
+        files = include_closure(hit[0], read=read)
+    else:
+        headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
+        srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+        files = [os.path.join(CSRC, f) for f in headers + srcs] + [os.path.join(ROOT, "include", "edge_moe.h")]
+    for path in files:
+        h.update(os.path.basename(path).encode() + b"\0" + read_b(path))
     return h.hexdigest()
 
 
