@@ -84,3 +84,32 @@ def expected_permutation(idx: np.ndarray, E: int):
     order = np.lexsort((t, e))
     offs = np.concatenate([[0], np.cumsum(np.bincount(e, minlength=E))])
     return offs.astype(np.int32), t[order].astype(np.int32), j[order].astype(np.int32)
+
+
+def tile_cover_sample(offs, row_tok, P, G, T, target, seed=0, tile=128):
+    """Tokens chosen so that every 128-row tile of the prefill GEMMs holds at
+    least one of them: the shared-up rows (distinct tokens of each group, by
+    token), the shared-down rows (each group's rows, by expert then token) and
+    the rank-128 input rows (each expert's rows, by token).  Greedy over the
+    tiles in order, then random tokens up to `target`."""
+    rng = np.random.default_rng(seed)
+    tiles = []                                   # arrays of the tokens in each tile
+    for g in range(G):
+        rows = row_tok[offs[g * P]:offs[(g + 1) * P]]
+        for t0 in range(0, rows.size, tile):
+            tiles.append(rows[t0:t0 + tile])
+        u = np.unique(rows)
+        for t0 in range(0, u.size, tile):
+            tiles.append(u[t0:t0 + tile])
+    for e in range(G * P):
+        rows = row_tok[offs[e]:offs[e + 1]]
+        for t0 in range(0, rows.size, tile):
+            tiles.append(rows[t0:t0 + tile])
+    chosen = set()
+    for tl in tiles:
+        if not chosen.intersection(tl.tolist()):
+            chosen.add(int(rng.choice(tl)))
+    n_cover = len(chosen)
+    while len(chosen) < max(target, n_cover):
+        chosen.add(int(rng.integers(T)))
+    return np.array(sorted(chosen)), n_cover, len(tiles)

@@ -11,7 +11,7 @@ import torch
 import shared_matrix_expert_amd as em
 import synth
 from oracle.layer import moe_forward, residual, route
-from gpu_helpers import (DEV, Layer, bits_to_dev, expected_permutation, f32_to_dev, say,
+from gpu_helpers import (DEV, Layer, bits_to_dev, expected_permutation, f32_to_dev, say, tile_cover_sample,
                          y_within_tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -213,35 +213,6 @@ def test_tile_shared_layout():
         assert np.array_equal(dq.cpu().numpy().reshape(-1), _tiled_reference(q))
 
 
-def _tile_cover_sample(offs, row_tok, P, G, T, target, seed=0, tile=128):
-    """Tokens chosen so that every 128-row tile of the prefill GEMMs holds at
-    least one of them: the shared-up rows (distinct tokens of each group, by
-    token), the shared-down rows (each group's rows, by expert then token) and
-    the rank-128 input rows (each expert's rows, by token).  Greedy over the
-    tiles in order, then random tokens up to `target`."""
-    rng = np.random.default_rng(seed)
-    tiles = []                                   # arrays of the tokens in each tile
-    for g in range(G):
-        rows = row_tok[offs[g * P]:offs[(g + 1) * P]]
-        for t0 in range(0, rows.size, tile):
-            tiles.append(rows[t0:t0 + tile])
-        u = np.unique(rows)
-        for t0 in range(0, u.size, tile):
-            tiles.append(u[t0:t0 + tile])
-    for e in range(G * P):
-        rows = row_tok[offs[e]:offs[e + 1]]
-        for t0 in range(0, rows.size, tile):
-            tiles.append(rows[t0:t0 + tile])
-    chosen = set()
-    for tl in tiles:
-        if not chosen.intersection(tl.tolist()):
-            chosen.add(int(rng.choice(tl)))
-    n_cover = len(chosen)
-    while len(chosen) < max(target, n_cover):
-        chosen.add(int(rng.integers(T)))
-    return np.array(sorted(chosen)), n_cover, len(tiles)
-
-
 def test_colblock_layout():
     """The column-blocked A_dn copy (edge_moe_tile_shared kind 3) against its
     definition, byte for byte, on random codes: for expert e and block cb of
@@ -284,7 +255,7 @@ def test_prefill_layer_tile_cover():
     assert np.array_equal(tr["expert_offsets"].cpu().numpy(), offs), "expert offsets differ"
     assert np.array_equal(tr["row_token"].cpu().numpy(), rt), "row tokens differ"
     assert np.array_equal(tr["row_slot"].cpu().numpy(), rs), "row slots differ"
-    sample, n_cover, n_tiles = _tile_cover_sample(offs, rt, D.experts_per_group, D.n_groups, D.T, 1024)
+    sample, n_cover, n_tiles = tile_cover_sample(offs, rt, D.experts_per_group, D.n_groups, D.T, 1024)
     say(f"  {n_cover} tokens cover {n_tiles} row tiles; {sample.size} tokens checked")
     ref = route(x[sample], wr, bias, D.top_k)
     assert np.array_equal(lg.cpu().numpy()[sample].astype(np.float64), ref["logits"]), "logits differ"
