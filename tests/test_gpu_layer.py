@@ -328,6 +328,36 @@ def test_verify_delta_handoff():
     _check_trace(D, idx_d, tr3, fw)
 
 
+@pytest.mark.parametrize("spread", ["one_group", "random"])
+def test_decode_traced(spread):
+    """One decode token, traced (permutation, activations, per-slot outputs):
+    the routed case, and a hand-routed one with all ten experts in one group
+    (the shared down's 10-row pass takes the 16-row staged instance, and the
+    other seven groups' workgroups have no rows)."""
+    say(f"case: decode T=1 traced, {spread}")
+    D = synth.config(1).dims
+    Wdev = synth.make_weights(1, 4, device="cuda")
+    x, wr, bias = _inputs(1, 4)
+    if spread == "random":
+        _run_parity(D, x, wr, bias, Wdev, keep=True)
+        return
+    idx = np.array([[3, 17, 22, 41, 5, 63, 0, 58, 30, 9]], dtype=np.int32)   # group 0 only
+    w = np.random.default_rng(8).uniform(0.1, 1.0, size=(1, D.top_k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    lay = Layer(D, Wdev)
+    idx_d = torch.from_numpy(idx).to("cuda")
+    w_d = torch.from_numpy(w).to("cuda")
+    y, tr = lay.forward(bits_to_dev(x), idx_d, w_d, trace=True)
+    torch.cuda.synchronize()
+    fw = moe_forward(x, idx, w.astype(np.float64), synth.weights_to_numpy(Wdev), D.experts_per_group, keep=True)
+    ok, ratio = y_within_tolerance(y.cpu().numpy(), fw["y"])
+    say(f"  worst |dy| / bound = {ratio:.3g}")
+    assert ok, f"y outside tolerance (worst ratio {ratio:.3g})"
+    _check_trace(D, idx_d, tr, fw)
+    y2, _ = lay.forward(bits_to_dev(x), idx_d, w_d)
+    assert torch.equal(y, y2)
+
+
 def test_graph_replay_two_layers():
     """Two full-size layers (route, forward, residual each) captured as one HIP
     graph: every replay, with eager work on the same workspaces and a
