@@ -276,7 +276,8 @@ dec_up(DecodeArgs a) {
 
 // ---- shared up and the R1 / R2 inputs from one work list --------------------------
 // Batches of at most 16 tokens with the decode-tiled S_up and A_up.  Every
-// token's x row is staged in LDS once per workgroup (8 or 16 rows of d), so any
+// token's x row is staged in LDS once per workgroup (1, 4, 8 or 16 rows of d,
+// the fewest that hold the batch; the MFMA rows past them repeat the last), so any
 // wave can take any weight tile.  The work is a list of items: the 16-row tiles
 // of S_up of each group with slots (whole K, 32 KB at d = 4096; outputs for
 // every token, the next kernel reads only the group's tokens), then the K
@@ -561,10 +562,14 @@ dec_up_ws(DecodeArgs a) {
         for (int i = threadIdx.x; i < a.d / 64; i += blockDim.x) a.cnt_c[i] = 0u;
     }
     if (a.d == 4096) {
-        if (a.T <= 8) upw_run<8, 8>(a, v, L);
+        if (a.T == 1) upw_run<1, 8>(a, v, L);
+        else if (a.T <= 4) upw_run<4, 8>(a, v, L);
+        else if (a.T <= 8) upw_run<8, 8>(a, v, L);
         else upw_run<16, 8>(a, v, L);
     } else {
-        if (a.T <= 8) upw_run<8, 4>(a, v, L);
+        if (a.T == 1) upw_run<1, 4>(a, v, L);
+        else if (a.T <= 4) upw_run<4, 4>(a, v, L);
+        else if (a.T <= 8) upw_run<8, 4>(a, v, L);
         else upw_run<16, 4>(a, v, L);
     }
 }
@@ -1473,7 +1478,8 @@ dec_down(DecodeArgs a) {
 // columns); each wave streams the int4 S_dn rows of its 16 columns (full-line
 // loads, four blocks ahead) against the group's activation rows staged
 // through LDS in pieces of 1024 elements per row (8 or 16 rows, chosen by the
-// row count), then adds the LoRA down V_dn zl2 and the delta down of each
+// row count; a 4-row instance measured slower at verify), then adds the LoRA
+// down V_dn zl2 and the delta down of each
 // distinct expert.  The per-slot outputs go to the workspace, and the column
 // block's last arriving workgroup forms y.  With every group's rows in one
 // workgroup, each light group of a decode step fills 32 compute units with
