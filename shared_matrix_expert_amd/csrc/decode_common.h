@@ -234,10 +234,11 @@ EM_DEV uint4 k_interleave(uint4 v) {
 // holding 136 + q exactly: flipping each nibble's sign bit gives q + 8 in
 // 0..15, which becomes the low mantissa bits below the exponent of 128.  The
 // pairs come out in the K order (0,4,1,5,2,6,3,7).
-// Each pair is one three-input bit operation: (v & M) ^ K with K = C ^ 0x00080008
-// (M and C share no bits, so the OR with C and the sign flip are one XOR).
-// The truth table of f(src0, src1, src2) is f evaluated on the bytes 0xF0,
-// 0xCC, 0xAA: (0xF0 & 0xCC) ^ 0xAA = 0x6A.
+// Each pair is one three-input bit operation, (v & M) ^ K: M = 0x000F000F keeps
+// the two nibbles, and K = 0x43084308 is the exponent pattern 0x4300 of each
+// half (which shares no bits with M, so ORing it in is an XOR) together with
+// the sign-bit flip 0x0008.  The truth table of f(src0, src1, src2) is f
+// evaluated on the bytes 0xF0, 0xCC, 0xAA: (0xF0 & 0xCC) ^ 0xAA = 0x6A.
 EM_DEV uint4 dq_offset(uint32_t w) {
     constexpr uint32_t M = 0x000F000Fu, K = 0x43084308u;
     constexpr unsigned char AND_XOR = 0x6A;
